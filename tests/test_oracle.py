@@ -1,0 +1,351 @@
+"""Pins for the CPU oracle: each test holds it against something other than
+itself -- hand-written fixtures from the pages' bit layout, a textbook worked
+example, exhaustive search on tiny alphabets, closed forms, entropy bounds,
+and an independent string-matching decoder."""
+import hashlib
+import math
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import tiny
+from lossless_bf16_weight_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def _kraft24(lengths):
+    return sum(1 << (24 - int(l)) for l in lengths if l)
+
+
+# ---------------------------------------------------------------- fields --
+
+def test_bf16_fields_golden():
+    rows = list(_rows("bf16_fields.txt"))
+    vals = np.array([float(r[0]) for r in rows], np.float32)
+    words = np.array([int(r[1], 16) for r in rows], np.uint16)
+    # the generator's cast rounds to these words (ties to even included)
+    assert (W.bf16_rne(vals) == words).all()
+    raw = np.array([int(r[5], 16) for r in rows], np.uint8)
+    exps = sorted({int(r[3]) for r in rows})
+    c = oracle.encode(words)
+    h = oracle.header(c)
+    assert (c[h["off_raw"]:h["off_raw"] + words.size] == raw).all()
+    assert sorted(np.nonzero(h["code_len"])[0].tolist()) == exps
+    assert (oracle.decode(c, words.size) == words).all()
+
+
+def test_bf16_special_words_golden():
+    rows = list(_rows("bf16_special_words.txt"))
+    words = np.array([int(r[0], 16) for r in rows], np.uint16)
+    raw = np.array([int(r[4], 16) for r in rows], np.uint8)
+    c = oracle.encode(words)
+    h = oracle.header(c)
+    assert (c[h["off_raw"]:h["off_raw"] + words.size] == raw).all()
+    assert sorted(np.nonzero(h["code_len"])[0].tolist()) == sorted({int(r[2]) for r in rows})
+    assert (oracle.decode(c, words.size) == words).all()
+
+
+def test_exhaustive_all_65536_words():
+    """Every exponent 0..255 and every sign+fraction byte, including +-0,
+    subnormals, +-Inf and every NaN payload, round-trips bit for bit."""
+    w = W.exhaustive_words()
+    c = oracle.encode(w)
+    assert oracle.check(c) == oracle.OK
+    assert (oracle.decode(c, w.size) == w).all()
+    h = oracle.header(c)
+    raw = c[h["off_raw"]:h["off_raw"] + w.size]
+    s = (w >> 15).astype(np.uint8)
+    m = (w & 0x7F).astype(np.uint8)
+    assert (raw == ((s << 7) | m)).all()
+    # uniform histogram over 256 exponents -> every code is 8 bits
+    assert (h["code_len"] == 8).all()
+    assert h["total_bits"] == 8 * w.size
+    # independent decoder: code strings matched against the bit string
+    assert tiny.decode_with_strings(c.tobytes()) == w.tolist()
+
+
+# ---------------------------------------------------------- code lengths --
+
+def test_textbook_huffman_golden():
+    rows = list(_rows("textbook_huffman.txt"))
+    f = np.zeros(256, np.uint64)
+    want = {}
+    for s, fr, l in rows:
+        f[int(s)] = int(fr)
+        want[int(s)] = int(l)
+    ln = oracle.code_lengths(f)
+    assert {s: int(ln[s]) for s in want} == want
+    assert int((f * ln).sum()) == 224
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_lengths_optimal_under_cap_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    k = int(rng.integers(2, 8))
+    f = np.zeros(256, np.uint64)
+    syms = rng.choice(256, k, replace=False)
+    # skewed weights so that small caps bind
+    f[syms] = (rng.pareto(1.0, k) * 50 + 1).astype(np.uint64)
+    cap_min = max(1, math.ceil(math.log2(k)))
+    for cap in range(cap_min, 7):
+        ln = oracle.code_lengths(f, cap)
+        assert ln.max() <= cap
+        assert _kraft24(ln) == 1 << 24
+        assert int((f * ln).sum()) == tiny.brute_force_min_cost(f.tolist(), cap)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_lengths_match_textbook_huffman_cost_when_cap_not_binding(seed):
+    rng = np.random.default_rng(100 + seed)
+    k = int(rng.integers(2, 257))
+    f = np.zeros(256, np.uint64)
+    f[rng.choice(256, k, replace=False)] = rng.integers(1, 10**6, k).astype(np.uint64)
+    if tiny.heap_huffman_depth(f.tolist()) > 24:
+        pytest.skip("cap binds")
+    ln = oracle.code_lengths(f)
+    assert int((f * ln).sum()) == tiny.heap_huffman_cost(f.tolist())
+    assert _kraft24(ln) == 1 << 24
+
+
+def test_lengths_closed_forms():
+    # uniform over 2^k symbols -> every length is k
+    for k in range(1, 9):
+        f = np.zeros(256, np.uint64)
+        f[: 1 << k] = 7
+        assert (oracle.code_lengths(f)[: 1 << k] == k).all()
+    # dyadic probabilities -> l = -log2 p, cost = entropy
+    f = np.zeros(256, np.uint64)
+    f[[10, 20, 30, 40, 50]] = [64, 32, 16, 8, 8]
+    ln = oracle.code_lengths(f)
+    assert [int(ln[s]) for s in (10, 20, 30, 40, 50)] == [1, 2, 3, 4, 4]
+    # one symbol -> one bit per element; none -> no codes
+    f = np.zeros(256, np.uint64)
+    f[77] = 1000
+    ln = oracle.code_lengths(f)
+    assert ln[77] == 1 and ln.sum() == 1
+    assert oracle.code_lengths(np.zeros(256, np.uint64)).sum() == 0
+    f = np.zeros(256, np.uint64)
+    f[[3, 200]] = [1, 10**9]
+    assert oracle.code_lengths(f)[[3, 200]].tolist() == [1, 1]
+
+
+def test_fibonacci_weights_hit_the_cap():
+    """Fibonacci weights give the deepest Huffman tree: 40 symbols -> depth 39
+    uncapped; the capped code is exactly 24 deep and Kraft-complete."""
+    fib = [1, 1]
+    while len(fib) < 40:
+        fib.append(fib[-1] + fib[-2])
+    f = np.zeros(256, np.uint64)
+    f[:40] = fib
+    assert tiny.heap_huffman_depth(f.tolist()) == 39
+    ln = oracle.code_lengths(f, 24)
+    assert int(ln.max()) == 24
+    assert _kraft24(ln) == 1 << 24
+    # a looser cap never costs more
+    costs = [int((f * oracle.code_lengths(f, cap)).sum()) for cap in range(24, 33)]
+    assert costs == sorted(costs, reverse=True)
+    assert costs[-1] > tiny.heap_huffman_cost(f.tolist())   # 32 < 39 still binds
+    # 30 Fibonacci weights: depth 29, so a cap of 32 does not bind and the
+    # optimum is the textbook Huffman cost
+    g = np.zeros(256, np.uint64)
+    g[:30] = fib[:30]
+    assert tiny.heap_huffman_depth(g.tolist()) == 29
+    lg = oracle.code_lengths(g, 32)
+    assert int(lg.max()) == 29
+    assert int((g * lg).sum()) == tiny.heap_huffman_cost(g.tolist())
+
+
+# --------------------------------------------------------- canonical codes --
+
+@pytest.mark.parametrize("seed", range(10))
+def test_canonical_codes_prefix_free_and_ordered(seed):
+    rng = np.random.default_rng(200 + seed)
+    k = int(rng.integers(2, 60))
+    f = np.zeros(256, np.uint64)
+    f[rng.choice(256, k, replace=False)] = (rng.pareto(0.7, k) * 10 + 1).astype(np.uint64)
+    ln = oracle.code_lengths(f)
+    code = oracle.canonical_codes(ln)
+    strings = {s: format(int(code[s]), "0%db" % int(ln[s])) for s in range(256) if ln[s]}
+    # no code is a prefix of another
+    items = sorted(strings.values())
+    for a, b in zip(items, items[1:]):
+        assert not b.startswith(a)
+    # sorted by (length, symbol) the codes increase when left-aligned
+    order = sorted(strings, key=lambda s: (int(ln[s]), s))
+    la = [int(code[s]) << (24 - int(ln[s])) for s in order]
+    assert la == sorted(la) and len(set(la)) == len(la)
+    assert order[0] in strings and int(code[order[0]]) == 0
+    # the counting construction of RFC 1951 3.2.2 gives the same strings
+    assert tiny.canonical_code_strings([int(x) for x in ln]) == strings
+
+
+# ------------------------------------------------------------- workloads --
+
+def _entropy(f):
+    p = f[f > 0] / f.sum()
+    return float(-(p * np.log2(p)).sum()), float(p.max())
+
+
+def test_size_near_entropy_and_about_70_percent():
+    """Gaussian-like weights land near the exponent-entropy bound and at
+    roughly 70% of BF16 (mlx-dfloat page, introduction; df11pack page)."""
+    w = W.single_2048()[0].make()
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    e = (w.reshape(-1) >> 7) & 0xFF
+    f = np.bincount(e, minlength=256).astype(np.float64)
+    H, pmax = _entropy(f)
+    n = w.size
+    # no prefix code beats the entropy; Huffman is within p_max + 0.086
+    # (Gallager 1978) of it
+    assert n * H <= h["total_bits"] <= n * (H + pmax + 0.086)
+    ratio = c.size / (2 * n)
+    assert 0.60 <= ratio <= 0.75
+    # nf12 news page, "Confirmed": >99.7% of weights share the top four
+    # exponent bits 0111, i.e. exponent in [112, 127]
+    assert ((e >= 112) & (e <= 127)).mean() >= 0.997
+
+
+def test_heavy_tail_cap_binds():
+    """The heavy-tailed stress tensor needs the length cap (uncapped depth 25)."""
+    w = W.heavy_tail_8192()[0].make()
+    e = (w.reshape(-1) >> 7) & 0xFF
+    f = np.bincount(e, minlength=256).astype(np.uint64)
+    assert tiny.heap_huffman_depth(f.tolist()) > 24
+    ln = oracle.code_lengths(f)
+    assert int(ln.max()) == 24 and _kraft24(ln) == 1 << 24
+
+
+def test_workload_generators_are_pinned():
+    w = W.single_2048()[0].make()
+    assert hashlib.sha256(w.tobytes()).hexdigest() == SHA_SINGLE_2048
+    v = W.flux_dit_block()[-1].make()
+    assert hashlib.sha256(v.tobytes()).hexdigest() == SHA_FLUX_VEC15
+    # thread count does not change the result
+    w1 = W.normal_bf16((3 * W.BLOCK + 5,), 9, threads=1)
+    w4 = W.normal_bf16((3 * W.BLOCK + 5,), 9, threads=4)
+    assert (w1 == w4).all()
+
+
+SHA_SINGLE_2048 = "f2bef7fb86ef7a72fc617a4b449f984d1cd1393b6ab5f8a169be5507370bddd8"
+SHA_FLUX_VEC15 = "2b2473e3773fe5e667f7ad4200ca4c1759ab147ce158cc046af508385c05019d"
+
+
+# ------------------------------------------------------------ the index --
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 32767, 32768, 32769, 3 * 32768 + 1000])
+def test_chunk_and_lane_index_reproduce_the_source(n):
+    w = W.normal_bf16((n,), seed=n)
+    c = oracle.encode(w)
+    assert oracle.check(c) == oracle.OK
+    h = oracle.header(c)
+    n_chunks = h["n_chunks"]
+    assert n_chunks == (n + 32767) // 32768
+    ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 16 * (n_chunks + 1)].view(np.uint64)
+    for ch in range(n_chunks):
+        lo, hi = ch * 32768, min(n, (ch + 1) * 32768)
+        # a chunk decodes from its start bit alone (df11pack, sampled chunks)
+        assert (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all()
+        # the 64 lane windows decode exactly their cnt codes, back to back
+        parts, ends = [], []
+        b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
+        Wb = (b1 - b0 + 63) // 64
+        for lane in range(64):
+            words, end = oracle.decode_lane(c, ch, lane)
+            parts.append(words)
+            if len(words):
+                ends.append((lane, end))
+                # the window's last code starts inside it and may run past it
+                assert b0 + (lane + 1) * Wb <= end or end == b1
+                assert end - min(b1, b0 + (lane + 1) * Wb) < 24
+        assert (np.concatenate(parts) == w[lo:hi]).all()
+        assert ends[-1][1] == b1
+        gap = c[h["off_lane_gap"] + 64 * ch:h["off_lane_gap"] + 64 * ch + 64]
+        assert ((gap < 24) | (gap == 0xFF)).all()
+
+
+def test_degenerate_tensors():
+    # empty
+    c = oracle.encode(np.zeros((0,), np.uint16))
+    h = oracle.header(c)
+    assert h["n_chunks"] == 0 and h["total_bits"] == 0 and oracle.check(c) == 0
+    assert oracle.decode(c, 0).size == 0
+    # one element
+    w = np.array([0x3F80], np.uint16)
+    c = oracle.encode(w)
+    assert oracle.check(c) == 0 and (oracle.decode(c, 1) == w).all()
+    # a single exponent: one bit per element
+    w = (np.arange(70000) % 256).astype(np.uint16) | np.uint16(127 << 7)
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    assert h["total_bits"] == w.size and oracle.check(c) == 0
+    assert (oracle.decode(c, w.size) == w).all()
+    # two exponents
+    w = np.where(np.arange(50000) % 3 == 0, 0x3F80, 0x4000).astype(np.uint16)
+    c = oracle.encode(w)
+    assert oracle.header(c)["total_bits"] == w.size
+    assert (oracle.decode(c, w.size) == w).all()
+
+
+# ------------------------------------------------------- errors, determinism --
+
+def test_corruption_is_detected():
+    w = W.normal_bf16((40000,), seed=3)
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    # a flipped stream bit either breaks the structure or changes the words
+    # (a swap between two codes of one length keeps every code start)
+    for pos in (100, 2000, 7777):
+        bad = c.copy()
+        bad[h["off_stream"] + pos] ^= 0x10
+        st = oracle.check(bad)
+        if st == 0:
+            assert not (oracle.decode(bad, w.size) == w).all()
+    bad = c.copy()
+    bad[0] ^= 1                                      # magic
+    assert oracle.check(bad) == oracle.E_FORMAT
+    bad = c.copy()
+    bad[h["off_lane_gap"] + 5] ^= 1                  # a lane gap
+    assert oracle.check(bad) == oracle.E_FORMAT
+    bad = c.copy()
+    bad[h["off_lane_cnt"] + 10] ^= 1                 # a lane count
+    assert oracle.check(bad) == oracle.E_FORMAT
+    bad = c.copy()
+    bad[208 + 121] += 1                              # a code length: Kraft breaks
+    assert oracle.check(bad) != 0
+    assert oracle.check(c[:-1]) == oracle.E_FORMAT   # truncated container
+
+
+def test_encoding_is_deterministic_across_processes():
+    w = W.normal_bf16((100000,), seed=11)
+    a = oracle.encode(w)
+    assert (oracle.encode(w) == a).all()
+    code = ("import sys,hashlib; sys.path.insert(0, %r); import oracle;"
+            "from lossless_bf16_weight_amd import workloads as W;"
+            "print(hashlib.sha256(oracle.encode(W.normal_bf16((100000,), seed=11)).tobytes()).hexdigest())"
+            % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    out = subprocess.check_output([sys.executable, "-c", code]).decode().strip()
+    assert out == hashlib.sha256(a.tobytes()).hexdigest()
+
+
+def test_string_decoder_agrees_on_random_small_tensors():
+    rng = np.random.default_rng(5)
+    for n in (1, 2, 7, 100, 200):
+        w = rng.integers(0, 65536, n).astype(np.uint16)
+        c = oracle.encode(w)
+        assert oracle.check(c) == 0
+        assert tiny.decode_with_strings(c.tobytes()) == w.tolist()
+        assert (oracle.decode(c, n) == w).all()
