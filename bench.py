@@ -1,0 +1,207 @@
+"""Benchmark: decode throughput of one Llama-3-8B-shaped transformer block.
+
+One step = one df11_decode_batch over the block's seven compressed tensors
+(q, k, v, o, gate, up, down; 218,103,808 BF16 weights, each tensor its own
+code table), from containers resident in HBM to BF16 outputs in HBM.
+
+Prints one JSON line:
+  value          decoded BF16 GB/s over the timed steps (10^9 bytes of BF16
+                 output per second)
+  roofline       HBM roofline of the decode kernel: algorithmic bytes per
+                 launch (index + code stream + raw bytes read, BF16 written)
+                 over the kernel's average duration (HIP events on the launch
+                 stream), against the MI355X peak of 8 TB/s; `traffic` holds
+                 the HBM bytes per launch measured with rocprofv3 counters
+                 when they were taken on the current kernel source, else null
+  cpu_baseline   the CPU oracle's bit-serial decoder on the host cores, over a
+                 bounded sample of the same containers
+Inputs are synthetic: seeded N(0, 0.02) weights rounded to BF16.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "decoded BF16 GB/s and % of HBM roofline (Llama-8B block), bit-exact"
+WORKLOAD = "llama8b_block"
+KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_weight_amd", "csrc", "decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_block_counters.txt")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on this kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(containers, infos, budget_s: float = 12.0):
+    """Oracle decode of whole chunks of the same containers on host threads."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    jobs = []
+    for t, info in enumerate(infos):
+        for ch in range(info["n_chunks"]):
+            n_ch = min(32768, info["n_elems"] - ch * 32768)
+            jobs.append((t, ch, n_ch))
+    # interleave tensors so a prefix of the job list is a fair sample
+    jobs.sort(key=lambda j: (j[1], j[0]))
+
+    def run(job):
+        t, ch, n_ch = job
+        oracle.decode_chunk(containers[t], ch, n_ch)
+        return n_ch
+
+    done = 0
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        i = 0
+        while i < len(jobs) and time.perf_counter() - t0 < budget_s:
+            batch = jobs[i:i + 4 * threads]
+            done += sum(ex.map(run, batch))
+            i += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": round(2.0 * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{i} of {len(jobs)} chunks of the {WORKLOAD} containers "
+                      f"({done} elements), bit-serial oracle decode, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported; this decoder runs on one GPU "
+              "(each GPU decodes its own shard, no collective is involved)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+
+    specs = W.llama8b_block()
+    words = [s.make().reshape(-1) for s in specs]
+    conts = [df11.encode(w, shape=s.shape) for w, s in zip(words, specs)]
+    plan = df11.Plan(conts, device=0)
+    infos = plan.infos
+    n_total = sum(i["n_elems"] for i in infos)
+    bytes_read = sum(i["bytes_read_per_decode"] for i in infos)
+    bytes_written = 2 * n_total
+    algo_bytes = bytes_read + bytes_written
+    container_bytes = sum(i["container_bytes"] for i in infos)
+
+    dev = torch.device("cuda:0")
+    d_conts = [torch.from_numpy(c).to(dev) for c in conts]
+    outs = [torch.empty(i["n_elems"], dtype=torch.int16, device=dev) for i in infos]
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        df11.decode_batch(plan, d_conts, outs, stream=stream)
+    torch.cuda.synchronize()
+
+    # whole-job throughput: K back-to-back steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        df11.decode_batch(plan, d_conts, outs, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # kernel duration: HIP events around each launch on the launch stream
+    n_ev = min(args.steps, 100)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(n_ev):
+        starts[i].record(stream)
+        df11.decode_batch(plan, d_conts, outs, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_ms = sum(durs_ms) / len(durs_ms)
+
+    # bit-exact against the source words
+    df11.check(plan, stream=stream)
+    exact = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) for w, o in zip(words, outs))
+
+    achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(bytes_written * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD,
+            "tensors": [s.name.split(".")[-1] for s in specs],
+            "elements": n_total,
+            "bf16_bytes": bytes_written,
+            "container_bytes": container_bytes,
+            "compressed_ratio": round(container_bytes / bytes_written, 4),
+            "algorithmic_bytes_per_step": algo_bytes,
+            "launches_per_step": 1,
+            "bit_exact": bool(exact),
+            "gpu": torch.cuda.get_device_name(0),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "kernel": "df11::decode_kernel",
+            "kernel_ms_avg": round(avg_ms, 5),
+            "kernel_ms_min": round(durs_ms[0], 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(conts, infos)
+    print(json.dumps(result), flush=True)
+    if not exact:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

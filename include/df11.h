@@ -1,0 +1,175 @@
+/*
+ * df11 -- lossless BF16 weight decompression on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libdf11.so.  No C++ or torch types cross it: plain pointers
+ * (host or device, as each argument says), sizes, and a hipStream_t.
+ *
+ * The method (mlx-dfloat project page, introduction and its 16-bit weight
+ * diagram; df11pack project page, introduction): every BF16 weight keeps its
+ * sign and 7-bit fraction as one raw byte, and its 8-bit exponent is replaced
+ * by a variable-length prefix code; decoding gives back each weight bit for
+ * bit.  The weights stay compressed in GPU memory and are decoded on the GPU
+ * when they are needed (mlx-dfloat project page, introduction).
+ *
+ * Container version 1 (one tensor = one container = one code table; all
+ * integers little-endian; every section starts on a 256-byte boundary):
+ *
+ *   header (512 bytes)
+ *      0 char[8] magic "DF11HIPC"    8 u32 version = 1      12 u32 flags = 0
+ *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
+ *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 lanes = 64
+ *     98 u16 0                     100 u32 n_chunks       104 u64 total_bits
+ *    112 u64 off_chunk_index       120 u64 off_lane_gap   128 u64 off_lane_cnt
+ *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
+ *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
+ *    208 u8 code_len[256]          464 u8[48] 0
+ *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
+ *                entry is { total_bits, n_elems }
+ *   lane gap     n_chunks x 64 x u8
+ *   lane cnt     n_chunks x 64 x u16
+ *   stream       the exponent codes, concatenated, most significant bit first
+ *                (bit 7 of byte 0 is the first bit); ceil(total_bits/8) bytes
+ *                rounded up to 16, plus 16 zero bytes
+ *   raw          one byte per element: (sign << 7) | fraction; n_elems bytes
+ *                rounded up to 16
+ *   Bytes not named above are zero.
+ *
+ * Code: code_len[e] is the length of the code of exponent byte e (0 = absent),
+ * at most 24 bits.  Code values are canonical: symbols sorted by (length,
+ * symbol) get consecutive values, the first is 0 (the deflate construction).
+ *
+ * Chunks: element j of the tensor is in chunk j / 32768.  Chunk c owns the
+ * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]).  Its bits are cut in
+ * 64 lane windows of W = ceil((b1 - b0) / 64) bits: window i is
+ * [b0 + i*W, min(b0 + (i+1)*W, b1)).  cnt[c][i] counts the codes that START in
+ * window i; gap[c][i] is the offset of the first of them from the window
+ * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
+ * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
+ * the windows.
+ */
+#ifndef DF11_H
+#define DF11_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DF11_ABI_VERSION 1
+#define DF11_HEADER_BYTES 512
+#define DF11_CHUNK_ELEMS 32768
+#define DF11_LANES 64
+#define DF11_MAX_CODE_LEN 24
+/* Tensors decoded by one kernel launch; larger batches are split. */
+#define DF11_MAX_BATCH 64
+
+typedef enum {
+    DF11_OK = 0,
+    DF11_E_ARG = 1,          /* a NULL / misaligned / out-of-range argument */
+    DF11_E_FORMAT = 2,       /* the container fails structural validation */
+    DF11_E_UNSUPPORTED = 3,  /* a valid header this build does not decode */
+    DF11_E_HIP = 4,          /* a HIP runtime call failed */
+    DF11_E_CORRUPT = 5,      /* a decode found a stream inconsistent with its index */
+    DF11_E_NOMEM = 6         /* host allocation failed */
+} df11_status;
+
+typedef struct df11_plan_s *df11_plan_t;
+
+typedef struct {
+    uint64_t n_elems;
+    uint32_t ndim;
+    uint32_t n_chunks;
+    uint64_t dims[8];
+    uint64_t total_bits;
+    uint64_t container_bytes;     /* whole container */
+    uint64_t meta_bytes;          /* header + chunk index + lane index (what df11_plan needs) */
+    uint64_t bytes_read_per_decode;  /* index + stream + raw bytes a decode reads */
+    uint8_t code_len[256];
+} df11_tensor_info;
+
+/* ---------------------------------------------------------------- host-only */
+
+/* Validate a container prefix held in HOST memory and describe it.
+ * `host_meta` must hold at least the metadata prefix (header, chunk index,
+ * lane index: info->meta_bytes).  When `bytes` covers the whole container the
+ * stream padding is checked too.  Checks: magic, version, chunk size, lane
+ * count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
+ * symbol), section offsets and sizes, start bits monotone with out_elem =
+ * 32768*c, per chunk: sum of cnt = chunk size, gap < 24 when cnt > 0, gap =
+ * 0xFF when cnt = 0, and every window's codes fit the stream.
+ * `info` may be NULL.  Reads only; allocates nothing on the device.
+ * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
+df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info);
+
+/* Size bound of the container for n elements (any data). */
+uint64_t df11_container_bound(uint64_t n_elems);
+
+/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-1
+ * container in HOST memory `out` (capacity `out_cap`, at least
+ * df11_container_bound(n)).  dims[ndim] is the shape (ndim <= 8, product =
+ * n; ndim = 0 means a scalar, n = 1).  `threads` = 0 uses every hardware
+ * thread.  The result is deterministic (independent of `threads`).
+ * On success *out_bytes is the container size. */
+df11_status df11_encode(const uint16_t *host_words, uint64_t n_elems, int ndim,
+                        const uint64_t *dims, void *out, uint64_t out_cap,
+                        uint64_t *out_bytes, int threads);
+
+/* -------------------------------------------------------------------- plan */
+
+/* Build a decode plan for n_tensors containers.  host_meta[t] points to HOST
+ * memory holding (at least) the metadata prefix of container t, of
+ * host_meta_bytes[t] bytes.  Every prefix is validated (df11_validate).  The
+ * plan builds each tensor's decode tables (a 1024-entry first-level table
+ * that resolves up to three codes per look-up, and the canonical tables for
+ * codes longer than 10 bits) and uploads them, with the per-tensor
+ * descriptors and the chunk work list, to device `hip_device` in one
+ * allocation.  The caller may free host_meta once this returns.
+ * flags: reserved, pass 0. */
+df11_status df11_plan(const void *const *host_meta, const size_t *host_meta_bytes,
+                      int n_tensors, int hip_device, uint32_t flags, df11_plan_t *out);
+
+/* Release a plan.  The caller must first synchronize every stream that has
+ * a decode of this plan in flight. */
+void df11_plan_destroy(df11_plan_t plan);
+
+df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info);
+
+/* ------------------------------------------------------------------ decode */
+
+/* Decode tensor `tensor` of the plan.  d_container: DEVICE pointer to the
+ * whole container (16-byte aligned, at least container_bytes long, same
+ * bytes as the prefix given to df11_plan).  d_out: DEVICE pointer to
+ * n_elems * 2 bytes (16-byte aligned), not overlapping the container.
+ * Enqueues on `stream` and returns; never allocates and never synchronizes
+ * (safe under stream capture).  Memory safety does not depend on the
+ * device bytes: a container that differs from the planned one gives wrong
+ * words and sets the plan's corruption flag (see df11_check), never an
+ * out-of-bounds access. */
+df11_status df11_decode(df11_plan_t plan, int tensor, const void *d_container,
+                        void *d_out, hipStream_t stream);
+
+/* Decode every tensor of the plan in one launch (one launch per
+ * DF11_MAX_BATCH tensors): d_containers[t] / d_outs[t] are HOST arrays of
+ * DEVICE pointers, with the rules of df11_decode for each t. */
+df11_status df11_decode_batch(df11_plan_t plan, const void *const *d_containers,
+                              void *const *d_outs, hipStream_t stream);
+
+/* Synchronize `stream`, then read and clear the plan's corruption flag:
+ * DF11_OK, or DF11_E_CORRUPT if some decode since the last check found a
+ * lane whose codes did not end where the index says the next one starts. */
+df11_status df11_check(df11_plan_t plan, hipStream_t stream);
+
+/* ------------------------------------------------------------------- misc */
+
+/* Text of the last non-OK status on this thread (never NULL). */
+const char *df11_last_error(void);
+const char *df11_status_str(df11_status s);
+int df11_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DF11_H */

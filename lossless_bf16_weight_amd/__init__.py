@@ -1,0 +1,10 @@
+"""Lossless BF16 weight decompression (DFloat11-style) for AMD MI355X.
+
+The exponent byte of every BF16 weight is stored as a canonical,
+length-limited prefix code; sign and fraction are kept as a raw byte.  The
+HIP library `libdf11.so` decodes containers back into bit-identical BF16
+tensors in GPU memory.  See include/df11.h for the C ABI and the container
+layout.
+"""
+from ._lib import (DF11Error, Plan, check, container_bound, decode, decode_batch, encode,  # noqa: F401
+                   lib, validate, validate_status)

@@ -1,0 +1,211 @@
+"""ctypes binding of libdf11.so (C ABI in include/df11.h).
+
+Argument marshalling only: validation, table building, encoding and every
+decode step run inside the library (host C++ and the HIP kernel).  There is
+no fallback: if the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdf11.so")
+
+OK, E_ARG, E_FORMAT, E_UNSUPPORTED, E_HIP, E_CORRUPT, E_NOMEM = range(7)
+MAX_BATCH = 64
+
+
+class DF11Error(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class TensorInfo(ctypes.Structure):
+    _fields_ = [
+        ("n_elems", ctypes.c_uint64),
+        ("ndim", ctypes.c_uint32),
+        ("n_chunks", ctypes.c_uint32),
+        ("dims", ctypes.c_uint64 * 8),
+        ("total_bits", ctypes.c_uint64),
+        ("container_bytes", ctypes.c_uint64),
+        ("meta_bytes", ctypes.c_uint64),
+        ("bytes_read_per_decode", ctypes.c_uint64),
+        ("code_len", ctypes.c_uint8 * 256),
+    ]
+
+    def as_dict(self) -> dict:
+        return {
+            "n_elems": self.n_elems, "ndim": self.ndim, "n_chunks": self.n_chunks,
+            "dims": [self.dims[i] for i in range(self.ndim)], "total_bits": self.total_bits,
+            "container_bytes": self.container_bytes, "meta_bytes": self.meta_bytes,
+            "bytes_read_per_decode": self.bytes_read_per_decode,
+            "code_len": np.array(self.code_len[:], np.uint8),
+        }
+
+
+_lib = None
+
+EXPORTS = [
+    "df11_validate", "df11_container_bound", "df11_encode", "df11_plan", "df11_plan_destroy",
+    "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
+    "df11_status_str", "df11_abi_version",
+]
+
+
+def lib():
+    """Load libdf11.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+                          "or lossless_bf16_weight_amd._build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint64
+    L.df11_validate.argtypes = [vp, sz, ctypes.POINTER(TensorInfo)]
+    L.df11_validate.restype = ctypes.c_int
+    L.df11_container_bound.argtypes = [u64]
+    L.df11_container_bound.restype = u64
+    L.df11_encode.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), vp, u64,
+                              ctypes.POINTER(u64), ctypes.c_int]
+    L.df11_encode.restype = ctypes.c_int
+    L.df11_plan.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_int, ctypes.c_int,
+                            ctypes.c_uint32, ctypes.POINTER(vp)]
+    L.df11_plan.restype = ctypes.c_int
+    L.df11_plan_destroy.argtypes = [vp]
+    L.df11_plan_destroy.restype = None
+    L.df11_plan_info.argtypes = [vp, ctypes.c_int, ctypes.POINTER(TensorInfo)]
+    L.df11_plan_info.restype = ctypes.c_int
+    L.df11_decode.argtypes = [vp, ctypes.c_int, vp, vp, vp]
+    L.df11_decode.restype = ctypes.c_int
+    L.df11_decode_batch.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+    L.df11_decode_batch.restype = ctypes.c_int
+    L.df11_check.argtypes = [vp, vp]
+    L.df11_check.restype = ctypes.c_int
+    L.df11_last_error.argtypes = []
+    L.df11_last_error.restype = ctypes.c_char_p
+    L.df11_status_str.argtypes = [ctypes.c_int]
+    L.df11_status_str.restype = ctypes.c_char_p
+    L.df11_abi_version.argtypes = []
+    L.df11_abi_version.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _raise(st: int):
+    if st != OK:
+        raise DF11Error(st, lib().df11_last_error().decode())
+
+
+def _host_u8(buf) -> np.ndarray:
+    a = np.asarray(buf)
+    if a.dtype != np.uint8:
+        a = a.view(np.uint8)
+    return np.ascontiguousarray(a.reshape(-1))
+
+
+# ----------------------------------------------------------------- host --
+
+def container_bound(n: int) -> int:
+    return int(lib().df11_container_bound(n))
+
+
+def encode(words, shape=None, threads: int = 0) -> np.ndarray:
+    """Encode BF16 bit patterns (uint16/int16 numpy array, host) into a
+    version-1 container (uint8 numpy array)."""
+    w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
+    shape = tuple(np.asarray(words).shape) if shape is None else tuple(shape)
+    dims = (ctypes.c_uint64 * max(1, len(shape)))(*shape)
+    cap = container_bound(w.size)
+    out = np.empty(cap, np.uint8)
+    nbytes = ctypes.c_uint64(0)
+    st = lib().df11_encode(w.ctypes.data, w.size, len(shape), dims, out.ctypes.data, cap,
+                           ctypes.byref(nbytes), threads)
+    if st != OK:
+        raise DF11Error(st, f"df11_encode: status {st}")
+    return out[: nbytes.value]
+
+
+def validate(container) -> dict:
+    c = _host_u8(container)
+    info = TensorInfo()
+    _raise(lib().df11_validate(c.ctypes.data, c.size, ctypes.byref(info)))
+    return info.as_dict()
+
+
+def validate_status(container) -> int:
+    c = _host_u8(container)
+    return int(lib().df11_validate(c.ctypes.data, c.size, None))
+
+
+# ----------------------------------------------------------------- plan --
+
+def _stream_handle(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+class Plan:
+    """Decode plan for a list of containers (host copies of at least their
+    metadata prefix)."""
+
+    def __init__(self, host_containers: Sequence, device: int = 0):
+        metas = [_host_u8(c) for c in host_containers]
+        n = len(metas)
+        ptrs = (ctypes.c_void_p * n)(*[m.ctypes.data for m in metas])
+        sizes = (ctypes.c_size_t * n)(*[m.size for m in metas])
+        h = ctypes.c_void_p()
+        _raise(lib().df11_plan(ptrs, sizes, n, device, 0, ctypes.byref(h)))
+        self._h = h
+        self.n_tensors = n
+        self.device = device
+        self.infos = [self.info(t) for t in range(n)]
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self, t: int) -> dict:
+        info = TensorInfo()
+        _raise(lib().df11_plan_info(self._h, t, ctypes.byref(info)))
+        return info.as_dict()
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().df11_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def decode(plan: Plan, t: int, container, out, stream=None):
+    """Enqueue the decode of tensor t: container (uint8, device) -> out
+    (16-bit dtype, device, n_elems)."""
+    _raise(lib().df11_decode(plan.handle, t, container.data_ptr(), out.data_ptr(),
+                             _stream_handle(stream)))
+
+
+def decode_batch(plan: Plan, containers: List, outs: List, stream=None):
+    n = plan.n_tensors
+    if len(containers) != n or len(outs) != n:
+        raise ValueError("one container and one output per planned tensor")
+    cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in containers])
+    op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    _raise(lib().df11_decode_batch(plan.handle, cp, op, _stream_handle(stream)))
+
+
+def check(plan: Plan, stream=None):
+    """Synchronize the stream and raise DF11Error(E_CORRUPT) if a decode found
+    a stream inconsistent with its index."""
+    _raise(lib().df11_check(plan.handle, _stream_handle(stream)))

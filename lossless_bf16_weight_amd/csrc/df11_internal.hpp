@@ -1,0 +1,78 @@
+// Internal layout shared by the host library and the HIP kernels.
+#pragma once
+#include <stdint.h>
+
+#include "../../include/df11.h"
+
+namespace df11 {
+
+// Container version 1 constants (layout documented in include/df11.h).
+constexpr uint32_t kVersion = 1;
+constexpr uint32_t kHeader = DF11_HEADER_BYTES;
+constexpr uint32_t kChunk = DF11_CHUNK_ELEMS;
+constexpr int kLanes = DF11_LANES;
+constexpr int kMaxLen = DF11_MAX_CODE_LEN;
+
+// First-level decode table: indexed by the next kL1Bits bits of the stream.
+// Entry: bits 0..23 up to three exponent bytes (first code in the low byte),
+// bits 24..27 how many stream bits they use, bits 28..29 how many codes (1..3).
+// Entry 0: the next code is longer than kL1Bits (or no code matches: a
+// prefix no valid stream contains), resolved by the canonical tables.
+constexpr int kL1Bits = 10;
+constexpr int kL1Size = 1 << kL1Bits;
+constexpr int kMaxPerLookup = 3;
+
+// Per-tensor table record in device memory (and copied whole into LDS).
+struct alignas(16) LutRecord {
+    uint32_t l1[kL1Size];
+    // lim[l]: 24-bit left-aligned exclusive upper bound of the codes of
+    // length <= l (l = 1..24); a peeked 24-bit value v has a code of length l
+    // exactly when lim[l-1] <= v < lim[l].
+    uint32_t lim[32];
+    // base[l] = (index of the first length-l symbol in `sorted`) - (its code)
+    int32_t base[32];
+    // exponent bytes sorted by (code length, value)
+    uint8_t sorted[256];
+    // code length of every exponent byte (0 = absent)
+    uint8_t len[256];
+};
+static_assert(sizeof(LutRecord) == 4864, "LUT record size");
+
+// Per-tensor descriptor in device memory.
+struct alignas(16) TensorDesc {
+    uint64_t n_elems;
+    uint64_t off_ci;
+    uint64_t off_gap;
+    uint64_t off_cnt;
+    uint64_t off_stream;
+    uint64_t stream_bytes;
+    uint64_t off_raw;
+    uint64_t raw_bytes;
+    uint32_t n_chunks;
+    uint32_t lut_index;
+    uint32_t pad[2];
+};
+static_assert(sizeof(TensorDesc) == 80, "descriptor size");
+
+// Work item of a batched launch: (tensor index within the launch) << 24 | chunk.
+constexpr uint32_t kItemChunkBits = 24;
+constexpr uint32_t kItemChunkMask = (1u << kItemChunkBits) - 1;
+
+struct DecodeArgs {
+    const TensorDesc *desc;      // plan's descriptor table (indexed by global tensor)
+    const LutRecord *luts;       // plan's table records
+    const uint32_t *work;        // work items of this launch, or nullptr
+    uint32_t *status;            // plan's corruption flag
+    uint32_t n_items;
+    uint32_t tensor_base;        // global index of the launch's tensor 0
+    const uint8_t *containers[DF11_MAX_BATCH];
+    uint16_t *outs[DF11_MAX_BATCH];
+};
+
+// Launches the decode kernel (decode.hip).  grid = number of workgroups.
+hipError_t launch_decode(const DecodeArgs &args, int grid, hipStream_t stream);
+
+// Workgroups of the decode kernel that fit on one compute unit at once.
+int decode_wgs_per_cu();
+
+}  // namespace df11

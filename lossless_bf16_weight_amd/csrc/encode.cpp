@@ -1,0 +1,253 @@
+// libdf11 encoder: BF16 words -> version-1 container (layout in include/df11.h),
+// multi-threaded on the host.
+//
+// Method: mlx-dfloat project page, introduction and 16-bit weight diagram --
+// the exponent byte of every weight gets a variable-length prefix code and
+// the sign + 7-bit fraction are kept as one raw byte.  The code is the
+// optimal prefix code with lengths <= 24 (package-merge, Larmore and
+// Hirschberg 1990; leaves ordered by (frequency, symbol), a leaf before a
+// package of equal weight), with canonical code values (deflate counting
+// construction, RFC 1951 3.2.2).  df11pack's page (introduction, "Measured")
+// is the context for doing this fast on CPU cores.
+//
+// Parallel plan: histogram per thread slice; one chunk per task for the bit
+// counts, the packing and the lane index (chunks start at known bit offsets
+// once the per-chunk bit counts are summed); raw bytes per slice.  The output
+// does not depend on the thread count.
+#include <algorithm>
+#include <atomic>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "df11_internal.hpp"
+
+using namespace df11;
+
+namespace {
+
+template <class F>
+void parallel_for(uint64_t n_tasks, int threads, F &&fn) {
+    if (n_tasks == 0) return;
+    const int T = (int)std::min<uint64_t>((uint64_t)threads, n_tasks);
+    if (T <= 1) {
+        for (uint64_t i = 0; i < n_tasks; ++i) fn(i);
+        return;
+    }
+    std::atomic<uint64_t> next{0};
+    std::vector<std::thread> pool;
+    pool.reserve(T);
+    for (int t = 0; t < T; ++t)
+        pool.emplace_back([&] {
+            for (uint64_t i; (i = next.fetch_add(1)) < n_tasks;) fn(i);
+        });
+    for (auto &th : pool) th.join();
+}
+
+inline uint64_t up256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+inline uint64_t up16(uint64_t x) { return (x + 15) & ~uint64_t(15); }
+inline void wr16(uint8_t *p, uint16_t v) { memcpy(p, &v, 2); }
+inline void wr32(uint8_t *p, uint32_t v) { memcpy(p, &v, 4); }
+inline void wr64(uint8_t *p, uint64_t v) { memcpy(p, &v, 8); }
+
+// Package-merge over a node pool: a node is a leaf (symbol) or a package of
+// two nodes of the level below.  Each level's list is kept sorted by weight.
+void package_merge(const uint64_t *freq, int cap, uint8_t *len) {
+    memset(len, 0, 256);
+    int sym[256], n = 0;
+    for (int s = 0; s < 256; ++s)
+        if (freq[s]) sym[n++] = s;
+    if (n == 0) return;
+    if (n == 1) { len[sym[0]] = 1; return; }
+    std::stable_sort(sym, sym + n, [&](int a, int b) { return freq[a] < freq[b]; });
+
+    struct Node { uint64_t w; int sym; int a, b; };
+    std::vector<Node> pool;
+    pool.reserve((size_t)cap * 2 * n + n);
+    std::vector<int> leaves(n), level;
+    for (int i = 0; i < n; ++i) {
+        leaves[i] = (int)pool.size();
+        pool.push_back({freq[sym[i]], sym[i], -1, -1});
+    }
+    level = leaves;
+    for (int d = 1; d < cap; ++d) {
+        std::vector<int> next;
+        next.reserve(2 * n);
+        size_t il = 0, ip = 0, np = level.size() / 2;
+        while (il < leaves.size() || ip < np) {
+            bool take_leaf;
+            if (ip >= np) take_leaf = true;
+            else if (il >= leaves.size()) take_leaf = false;
+            else take_leaf = pool[leaves[il]].w <= pool[level[2 * ip]].w + pool[level[2 * ip + 1]].w;
+            if (take_leaf) {
+                next.push_back(leaves[il++]);
+            } else {
+                const int a = level[2 * ip], b = level[2 * ip + 1];
+                next.push_back((int)pool.size());
+                pool.push_back({pool[a].w + pool[b].w, -1, a, b});
+                ++ip;
+            }
+        }
+        level.swap(next);
+    }
+    // each leaf occurrence under the 2n-2 lightest top-level nodes adds one bit
+    unsigned depth[256] = {};
+    std::vector<int> stack;
+    for (int i = 0; i < 2 * n - 2; ++i) {
+        stack.push_back(level[i]);
+        while (!stack.empty()) {
+            const Node &x = pool[stack.back()];
+            stack.pop_back();
+            if (x.sym >= 0) depth[x.sym]++;
+            else { stack.push_back(x.a); stack.push_back(x.b); }
+        }
+    }
+    for (int s = 0; s < 256; ++s) len[s] = (uint8_t)depth[s];
+}
+
+void canonical_codes(const uint8_t *len, uint32_t *code) {
+    uint32_t bl_count[kMaxLen + 1] = {}, next_code[kMaxLen + 2] = {};
+    for (int s = 0; s < 256; ++s)
+        if (len[s]) bl_count[len[s]]++;
+    uint32_t c = 0;
+    for (int bits = 1; bits <= kMaxLen; ++bits) {
+        c = (c + bl_count[bits - 1]) << 1;
+        next_code[bits] = c;
+    }
+    for (int s = 0; s < 256; ++s) code[s] = len[s] ? next_code[len[s]]++ : 0;
+}
+
+}  // namespace
+
+extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, const uint64_t *dims,
+                                   void *out_v, uint64_t out_cap, uint64_t *out_bytes, int threads) {
+    uint8_t *out = (uint8_t *)out_v;
+    if ((!w && n) || !out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims)) return DF11_E_ARG;
+    uint64_t prod = 1;
+    for (int i = 0; i < ndim; ++i) prod *= dims[i];
+    if ((ndim && prod != n) || (!ndim && n != 1)) return DF11_E_ARG;
+    if (n > (uint64_t(1) << 46)) return DF11_E_UNSUPPORTED;
+    if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+
+    // 1. exponent histogram
+    const uint64_t n_slices = std::max<uint64_t>(1, std::min<uint64_t>((n + (1 << 20) - 1) >> 20, 4096));
+    std::vector<uint64_t> part(n_slices * 256, 0);
+    parallel_for(n_slices, threads, [&](uint64_t s) {
+        const uint64_t lo = n * s / n_slices, hi = n * (s + 1) / n_slices;
+        uint64_t *h = &part[s * 256];
+        for (uint64_t j = lo; j < hi; ++j) h[(w[j] >> 7) & 0xFF]++;
+    });
+    uint64_t freq[256] = {};
+    for (uint64_t s = 0; s < n_slices; ++s)
+        for (int e = 0; e < 256; ++e) freq[e] += part[s * 256 + e];
+
+    // 2. lengths, 3. canonical codes
+    uint8_t len[256];
+    uint32_t code[256];
+    package_merge(freq, kMaxLen, len);
+    canonical_codes(len, code);
+
+    // 4. per-chunk bit counts and start bits
+    const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
+    std::vector<uint64_t> start(n_chunks + 1, 0);
+    parallel_for(n_chunks, threads, [&](uint64_t c) {
+        const uint64_t lo = c * kChunk, hi = std::min<uint64_t>(n, lo + kChunk);
+        uint64_t bits = 0;
+        for (uint64_t j = lo; j < hi; ++j) bits += len[(w[j] >> 7) & 0xFF];
+        start[c + 1] = bits;
+    });
+    for (uint64_t c = 0; c < n_chunks; ++c) start[c + 1] += start[c];
+    const uint64_t total_bits = start[n_chunks];
+
+    // layout
+    const uint64_t off_ci = kHeader;
+    const uint64_t off_gap = up256(off_ci + (n_chunks + 1) * 16);
+    const uint64_t off_cnt = up256(off_gap + n_chunks * kLanes);
+    const uint64_t off_stream = up256(off_cnt + n_chunks * kLanes * 2);
+    const uint64_t stream_bytes = up16((total_bits + 7) / 8) + 16;
+    const uint64_t off_raw = up256(off_stream + stream_bytes);
+    const uint64_t raw_bytes = up16(n);
+    const uint64_t total = off_raw + raw_bytes;
+    if (out_cap < total) return DF11_E_ARG;
+
+    // zero everything (padding and reserved bytes stay zero)
+    const uint64_t zslices = std::max<uint64_t>(1, total >> 24);
+    parallel_for(zslices, threads, [&](uint64_t s) {
+        const uint64_t lo = total * s / zslices, hi = total * (s + 1) / zslices;
+        memset(out + lo, 0, hi - lo);
+    });
+
+    memcpy(out, "DF11HIPC", 8);
+    wr32(out + 8, kVersion);
+    wr64(out + 16, n);
+    wr32(out + 24, (uint32_t)ndim);
+    wr32(out + 28, kChunk);
+    for (int i = 0; i < ndim; ++i) wr64(out + 32 + 8 * i, dims[i]);
+    out[96] = kMaxLen;
+    out[97] = kLanes;
+    wr32(out + 100, (uint32_t)n_chunks);
+    wr64(out + 104, total_bits);
+    wr64(out + 112, off_ci);
+    wr64(out + 120, off_gap);
+    wr64(out + 128, off_cnt);
+    wr64(out + 136, off_stream);
+    wr64(out + 144, stream_bytes);
+    wr64(out + 152, off_raw);
+    wr64(out + 160, raw_bytes);
+    wr64(out + 168, total);
+    memcpy(out + 208, len, 256);
+    for (uint64_t c = 0; c <= n_chunks; ++c) {
+        wr64(out + off_ci + c * 16, start[c]);
+        wr64(out + off_ci + c * 16 + 8, std::min<uint64_t>(c * kChunk, n));
+    }
+
+    // 5. pack each chunk's codes and build its lane index
+    uint8_t *stream = out + off_stream;
+    parallel_for(n_chunks, threads, [&](uint64_t c) {
+        thread_local std::vector<uint8_t> buf;
+        const uint64_t lo = c * kChunk, hi = std::min<uint64_t>(n, lo + kChunk);
+        const uint64_t b0 = start[c], b1 = start[c + 1];
+        const uint64_t W = (b1 - b0 + kLanes - 1) / kLanes;
+        const unsigned head = (unsigned)(b0 & 7);
+        const uint64_t nbytes = (head + (b1 - b0) + 7) / 8;
+        buf.assign(nbytes + 8, 0);
+        unsigned cnt[kLanes] = {};
+        uint8_t gap[kLanes];
+        memset(gap, 0xFF, sizeof gap);
+        uint64_t acc = 0;   // pending bits, right-aligned
+        unsigned nacc = head;
+        uint64_t at = 0, pos = 0;   // output byte, chunk-relative bit position
+        for (uint64_t j = lo; j < hi; ++j) {
+            const unsigned e = (w[j] >> 7) & 0xFF;
+            const unsigned lane = (unsigned)(pos / W);
+            if (cnt[lane]++ == 0) gap[lane] = (uint8_t)(pos - lane * W);
+            acc = (acc << len[e]) | code[e];
+            nacc += len[e];
+            pos += len[e];
+            while (nacc >= 8) {
+                nacc -= 8;
+                buf[at++] = (uint8_t)(acc >> nacc);
+            }
+        }
+        if (nacc) buf[at++] = (uint8_t)(acc << (8 - nacc));
+        // bytes shared with the neighbouring chunks are merged with an OR
+        const uint64_t first = b0 / 8;
+        for (uint64_t i = 0; i < at; ++i) {
+            const bool shared = (i == 0 && head) || (i + 1 == at && ((head + (b1 - b0)) & 7));
+            if (shared) __atomic_fetch_or(&stream[first + i], buf[i], __ATOMIC_RELAXED);
+            else stream[first + i] = buf[i];
+        }
+        memcpy(out + off_gap + c * kLanes, gap, kLanes);
+        for (int i = 0; i < kLanes; ++i) wr16(out + off_cnt + c * kLanes * 2 + 2 * i, (uint16_t)cnt[i]);
+    });
+
+    // 6. raw bytes
+    parallel_for(n_slices, threads, [&](uint64_t s) {
+        const uint64_t lo = n * s / n_slices, hi = n * (s + 1) / n_slices;
+        uint8_t *r = out + off_raw;
+        for (uint64_t j = lo; j < hi; ++j) r[j] = (uint8_t)(((w[j] >> 8) & 0x80) | (w[j] & 0x7F));
+    });
+
+    *out_bytes = total;
+    return DF11_OK;
+}
