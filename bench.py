@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 512 MiB device-to-device copy (the reference "
+                         "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this decoder runs on one GPU "
@@ -109,6 +112,15 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        a = torch.ones(256 << 20, dtype=torch.int16, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 2, "copies": 3}))
+        return
 
     import lossless_bf16_weight_amd as df11
     from lossless_bf16_weight_amd import workloads as W

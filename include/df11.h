@@ -17,16 +17,16 @@
  *   header (512 bytes)
  *      0 char[8] magic "DF11HIPC"    8 u32 version = 1      12 u32 flags = 0
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
- *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 lanes = 64
+ *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 windows = 128
  *     98 u16 0                     100 u32 n_chunks       104 u64 total_bits
- *    112 u64 off_chunk_index       120 u64 off_lane_gap   128 u64 off_lane_cnt
+ *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_cnt
  *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
  *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
  *    208 u8 code_len[256]          464 u8[48] 0
  *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
  *                entry is { total_bits, n_elems }
- *   lane gap     n_chunks x 64 x u8
- *   lane cnt     n_chunks x 64 x u16
+ *   window gap   n_chunks x 128 x u8
+ *   window cnt   n_chunks x 128 x u16
  *   stream       the exponent codes, concatenated, most significant bit first
  *                (bit 7 of byte 0 is the first bit); ceil(total_bits/8) bytes
  *                rounded up to 16, plus 16 zero bytes
@@ -40,12 +40,13 @@
  *
  * Chunks: element j of the tensor is in chunk j / 32768.  Chunk c owns the
  * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]).  Its bits are cut in
- * 64 lane windows of W = ceil((b1 - b0) / 64) bits: window i is
+ * 128 windows of W = ceil((b1 - b0) / 128) bits: window i is
  * [b0 + i*W, min(b0 + (i+1)*W, b1)).  cnt[c][i] counts the codes that START in
  * window i; gap[c][i] is the offset of the first of them from the window
  * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
  * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
- * the windows.
+ * the windows.  The decoder gives one wavefront to a chunk and two
+ * neighbouring windows to each of its 64 lanes.
  */
 #ifndef DF11_H
 #define DF11_H
@@ -61,7 +62,7 @@ extern "C" {
 #define DF11_ABI_VERSION 1
 #define DF11_HEADER_BYTES 512
 #define DF11_CHUNK_ELEMS 32768
-#define DF11_LANES 64
+#define DF11_WINDOWS 128
 #define DF11_MAX_CODE_LEN 24
 /* Tensors decoded by one kernel launch; larger batches are split. */
 #define DF11_MAX_BATCH 64
@@ -85,7 +86,7 @@ typedef struct {
     uint64_t dims[8];
     uint64_t total_bits;
     uint64_t container_bytes;     /* whole container */
-    uint64_t meta_bytes;          /* header + chunk index + lane index (what df11_plan needs) */
+    uint64_t meta_bytes;          /* header + chunk index + window index (what df11_plan needs) */
     uint64_t bytes_read_per_decode;  /* index + stream + raw bytes a decode reads */
     uint8_t code_len[256];
 } df11_tensor_info;
@@ -94,12 +95,12 @@ typedef struct {
 
 /* Validate a container prefix held in HOST memory and describe it.
  * `host_meta` must hold at least the metadata prefix (header, chunk index,
- * lane index: info->meta_bytes).  When `bytes` covers the whole container the
- * stream padding is checked too.  Checks: magic, version, chunk size, lane
- * count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
+ * window index: info->meta_bytes).  When `bytes` covers the whole container
+ * the stream padding is checked too.  Checks: magic, version, chunk size,
+ * window count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
  * symbol), section offsets and sizes, start bits monotone with out_elem =
  * 32768*c, per chunk: sum of cnt = chunk size, gap < 24 when cnt > 0, gap =
- * 0xFF when cnt = 0, and every window's codes fit the stream.
+ * 0xFF when cnt = 0, and a window's codes fit its share of the stream.
  * `info` may be NULL.  Reads only; allocates nothing on the device.
  * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
 df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info);
@@ -123,8 +124,8 @@ df11_status df11_encode(const uint16_t *host_words, uint64_t n_elems, int ndim,
  * memory holding (at least) the metadata prefix of container t, of
  * host_meta_bytes[t] bytes.  Every prefix is validated (df11_validate).  The
  * plan builds each tensor's decode tables (a 1024-entry first-level table
- * that resolves up to three codes per look-up, and the canonical tables for
- * codes longer than 10 bits) and uploads them, with the per-tensor
+ * that resolves up to three codes per look-up, a second-level table for codes
+ * of 11 to 16 bits, canonical limits for longer codes) and uploads them, with the per-tensor
  * descriptors and the chunk work list, to device `hip_device` in one
  * allocation.  The caller may free host_meta once this returns.
  * flags: reserved, pass 0. */

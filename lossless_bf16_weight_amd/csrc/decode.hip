@@ -7,24 +7,31 @@
 //
 // One workgroup = one wave64.  A wave decodes whole chunks of 32768 elements
 // (64 KiB of BF16 output), one after the other, over a contiguous range of
-// the launch's work items (tensor, chunk):
+// the launch's work items (tensor, chunk).  Per chunk:
 //
 //   1. stage: coalesced 16-byte loads of the chunk's code bytes, byte-swapped
-//      into big-endian 32-bit words in LDS; the chunk's raw bytes are loaded
-//      into registers at the same time (8 bytes per lane per half-block) and
+//      into big-endian 32-bit words in LDS; the chunk's raw bytes go to
+//      registers in the same burst (8 bytes per lane per 512 elements) and
 //      are not needed before step 5, so their latency hides behind decoding;
-//   2. index: each lane reads its window's (gap, cnt); a DPP prefix sum over
-//      the 64 counts gives every lane the chunk position of its first code;
-//   3. decode: each lane walks its window with a 64-bit bit buffer; one look-up
-//      in the LDS first-level table resolves up to three codes of <= 10 bits;
-//      longer codes go through the canonical limit table.  Exponent bytes are
-//      OR-ed into a zeroed 32 KiB LDS tile at their chunk positions;
-//   4. check: a lane must end exactly where the next non-empty window's first
-//      code starts (or at the chunk end); otherwise the plan's flag is set;
-//   5. assemble: per 1024 elements, each lane joins 2 x 8 exponents from the
-//      tile with 2 x 8 raw bytes into BF16 words -- (r & 0x80) << 8 |
-//      e << 7 | (r & 0x7F) -- and writes them with two 16-byte stores that are
-//      contiguous across the wave (1 KiB per store instruction).
+//   2. index: the chunk's bits form 128 equal windows; lane i takes windows
+//      2i and 2i+1.  A DPP prefix sum over the 64 lane totals of the window
+//      code counts gives each window the chunk position of its first code;
+//   3. decode: each lane walks its two windows side by side (two independent
+//      dependency chains).  A look-up peeks 32 bits with one ds_read2_b32 and
+//      a 64-bit shift, then one LDS first-level table entry resolves up to
+//      three codes of <= 10 bits; codes of 11..16 bits use a second-level
+//      table, longer ones the canonical limits.  Exponent bytes (rotated, see
+//      rot_exp) are OR-ed into a zeroed 32 KiB LDS tile at their chunk
+//      positions.  A counted loop with no per-lane control flow runs while no
+//      window can run out (each look-up takes at most three codes); an exact
+//      per-window loop finishes the windows;
+//   4. check: a window must end exactly where the next non-empty window's
+//      first code starts (or at the chunk end); otherwise the plan's flag is
+//      set;
+//   5. assemble: per 1024 elements, each lane joins 2 x 8 tile bytes with 2 x 8
+//      raw bytes into BF16 words (two byte permutes and one bitfield insert
+//      per two words) and writes them with 16-byte stores that are contiguous
+//      across the wave (1 KiB per store instruction).
 //
 // There is no matrix arithmetic here: the path is bound by HBM traffic
 // (about 1.33 bytes read and 2 bytes written per element), with integer
@@ -36,18 +43,32 @@
 namespace df11 {
 
 constexpr int kTileBytes = kChunk;                 // one exponent byte per element
-constexpr int kCodeCap = 15 * 1024;                // staged code bytes per chunk
+// LDS per wave: 14 KiB staged codes + 32 KiB tile + 5.8 KiB tables = 51.8 KiB,
+// so that three waves fit in a compute unit's 160 KiB (the allocation is
+// rounded up, and 52.8 KiB would leave room for only two).
+constexpr int kCodeCap = 14 * 1024;                // staged code bytes per chunk
 constexpr int kCodeWords = kCodeCap / 4;
-constexpr int kBlocks = kChunk / 1024;             // 1024-element blocks per chunk
+constexpr int kHalfBlocks = kChunk / 512;          // 512-element store blocks
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// LDS of one wave.  Staged code word k (big-endian) sits in codes[k + 1],
+// with codes[1] 16-byte aligned; the 12 bytes in front keep codes[0] (read
+// only for positions that are multiples of 32) inside the struct.  The
+// tile's and the tables' bases fold into the instructions' 16-bit offsets.
 struct Lds {
-    uint32_t tile[kTileBytes / 4 + 4];
-    uint32_t codes[kCodeWords];
+    uint32_t pad[3];
+    uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
+    uint8_t tile[kTileBytes + 16];
     LutRecord lut;
 };
+static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0, "LDS alignment");
+static_assert(sizeof(Lds) <= 53248, "three waves per compute unit");
+constexpr uint32_t kDummy = kTileBytes + 8;   // tile bytes nobody reads
+
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
     return __builtin_amdgcn_perm(0u, x, 0x00010203u);
@@ -65,85 +86,191 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return x;
 }
 
-// BF16 words of two elements from their exponents and raw bytes, packed.
-__device__ __forceinline__ uint32_t join2(uint32_t e01, uint32_t r01) {
-    // x = [e1 r1 e0 r0] (bytes from high to low): each half is (e << 8) | r
-    const uint32_t x = __builtin_amdgcn_perm(e01, r01, 0x05010400u);
-    // half -> (r & 0x80) << 8 | e << 7 | (r & 0x7F)
-    return (x & 0x007F007Fu) | ((x >> 1) & 0x7F807F80u) | ((x << 8) & 0x80008000u);
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) x = min(x, (uint32_t)__shfl_xor((int)x, m));
+    return x;
 }
 
-__device__ __forceinline__ u32x4 join8(u32x2 e8, u32x2 r8) {
+// Two BF16 words from two rotated exponent bytes (t) and two raw bytes (r):
+// word = [r & 0x80 | t & 0x7F] [t & 0x80 | r & 0x7F].
+__device__ __forceinline__ uint32_t join2(uint32_t t, uint32_t r, uint32_t sel_p, uint32_t sel_q) {
+    const uint32_t p = __builtin_amdgcn_perm(t, r, sel_p);   // [r1 t1 r0 t0]
+    const uint32_t q = __builtin_amdgcn_perm(t, r, sel_q);   // [t1 r1 t0 r0]
+    return (p & 0x80808080u) | (q & 0x7F7F7F7Fu);
+}
+
+__device__ __forceinline__ u32x4 join8(u32x2 t8, u32x2 r8) {
     u32x4 o;
-    o.x = join2(e8.x, r8.x);
-    o.y = join2(e8.x >> 16, r8.x >> 16);
-    o.z = join2(e8.y, r8.y);
-    o.w = join2(e8.y >> 16, r8.y >> 16);
+    o.x = join2(t8.x, r8.x, 0x01050004u, 0x05010400u);
+    o.y = join2(t8.x, r8.x, 0x03070206u, 0x07030602u);
+    o.z = join2(t8.y, r8.y, 0x01050004u, 0x05010400u);
+    o.w = join2(t8.y, r8.y, 0x03070206u, 0x07030602u);
     return o;
 }
 
-// Decode `rem` codes starting at relative bit `s` of `words` (big-endian
-// 32-bit words, clamped to `n_words`), OR-ing the exponent bytes into the
-// tile from byte position `q`.  Returns the relative bit after the last code.
-template <bool kFromLds>
-__device__ __forceinline__ uint64_t decode_window(Lds &L, const uint32_t *__restrict__ words,
-                                                  uint32_t n_words, uint64_t s, uint32_t q,
-                                                  uint32_t rem, uint32_t &bad) {
-    auto word = [&](uint64_t i) -> uint32_t {
-        const uint64_t j = i < n_words ? i : (uint64_t)n_words - 1;
-        if constexpr (kFromLds) return words[j];
-        else return bswap32(words[j]);
-    };
-    uint64_t rd = s >> 5;
-    const uint32_t sh = (uint32_t)(s & 31);
-    uint64_t buf = (((uint64_t)word(rd) << 32) | word(rd + 1)) << sh;
-    int nb = 64 - (int)sh;
-    rd += 2;
-    uint32_t nxt = word(rd);
-    while (rem > 0) {
-        const uint32_t top = (uint32_t)(buf >> 32);
-        const uint32_t ent = L.lut.l1[top >> (32 - kL1Bits)];
-        uint32_t n = ent >> 28;
-        uint32_t c = (ent >> 24) & 15u;
-        uint32_t syms = ent & 0xFFFFFFu;
-        if (n == 0) {
-            // a code longer than kL1Bits: canonical limits, 24-bit peek
-            const uint32_t v = top >> 8;
-            int l = kL1Bits + 1;
-            while (l <= kMaxLen && v >= L.lut.lim[l]) ++l;
-            if (l > kMaxLen) {
-                bad = 1;
-                l = kMaxLen;
-                syms = 0;
-            } else {
-                syms = L.lut.sorted[(int)(v >> (kMaxLen - l)) + L.lut.base[l]];
-            }
-            n = 1;
-            c = (uint32_t)l;
-        }
-        if (n > rem) {
-            // last look-up of the window: keep only its first `rem` codes
-            n = rem;
-            c = 0;
-            for (uint32_t k = 0; k < n; ++k) c += L.lut.len[(syms >> (8 * k)) & 0xFFu];
-            syms &= (1u << (8 * n)) - 1u;
-        }
-        const uint64_t v64 = (uint64_t)syms << (8 * (q & 3));
-        __hip_atomic_fetch_or(&L.tile[q >> 2], (uint32_t)v64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_or(&L.tile[(q >> 2) + 1], (uint32_t)(v64 >> 32), __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_WORKGROUP);
-        q += n;
-        rem -= n;
-        buf <<= c;
-        nb -= (int)c;
-        if (nb <= 32) {
-            buf |= (uint64_t)nxt << (32 - nb);
-            nb += 32;
-            ++rd;
-            nxt = word(rd);
+// ---- code sources ---------------------------------------------------------
+// A window's position is kept negated, pn = -p (mod 2^32), where p is the
+// bit offset from the source's first word.  The 32 stream bits from p are
+// the funnel shift of words j-1 and j with j = ceil(p / 32) by (-p) mod 32:
+// for p = 32i + s with s > 0 that is (w_i:w_i+1) >> (32 - s), and for s = 0
+// the shift is 0 and yields w_i itself.
+
+struct LdsCodes {
+    static constexpr bool kLds = true;
+    const uint32_t *w;   // w[j] = staged word j-1
+    uint32_t pn_min;     // smallest pn (largest p) whose words are inside
+    __device__ __forceinline__ uint32_t peek_unclamped(uint32_t pn) const {
+        const uint32_t j = (31u - pn) >> 5;
+        return __builtin_amdgcn_alignbit(w[j], w[j + 1], pn);
+    }
+    __device__ __forceinline__ uint32_t peek(uint32_t pn) const {
+        // p <= pmax  <=>  pn >= -pmax (positions are far below 2^31)
+        return peek_unclamped((int32_t)pn < (int32_t)pn_min ? pn_min : pn);
+    }
+};
+
+struct GlobalCodes {
+    static constexpr bool kLds = false;
+    const uint32_t *w;   // w[j] = stream word j-1 (little-endian bytes as stored)
+    uint32_t pn_min;
+    __device__ __forceinline__ uint32_t peek_unclamped(uint32_t pn) const {
+        const uint32_t j = (31u - pn) >> 5;
+        return __builtin_amdgcn_alignbit(bswap32(w[j]), bswap32(w[j + 1]), pn);
+    }
+    __device__ __forceinline__ uint32_t peek(uint32_t pn) const {
+        return peek_unclamped((int32_t)pn < (int32_t)pn_min ? pn_min : pn);
+    }
+};
+
+// First-level style entry for a code longer than kL1Bits at the front of
+// `top`: second-level table, else the canonical limits.  A prefix no valid
+// stream holds sets `bad` and yields a 24-bit code of exponent 0.
+__device__ __forceinline__ uint32_t long_entry(const LutRecord &T, uint32_t top, uint32_t &bad) {
+    const uint32_t i2 = (top >> (32 - kL2Bits)) - T.l2_base;
+    const uint32_t e2 = i2 < T.l2_size ? (uint32_t)T.l2[i2] : 0u;
+    uint32_t sym, len;
+    if (e2) {
+        len = e2 >> 8;
+        sym = e2 & 0xFFu;
+    } else {
+        const uint32_t v = top >> (32 - kMaxLen);
+        uint32_t l = kL1Bits + 1;
+        while (l <= (uint32_t)kMaxLen && v >= T.lim[l]) ++l;
+        if (l > (uint32_t)kMaxLen) {
+            bad = 1;
+            len = kMaxLen;
+            sym = 0;
+        } else {
+            len = l;
+            sym = T.sorted[(int)(v >> (kMaxLen - l)) + T.base[l]];
         }
     }
-    return rd * 32 - (uint64_t)nb;
+    return sym | (len << kEntLenShift) | (1u << kEntCountShift);
+}
+
+template <class Src>
+__device__ __forceinline__ uint32_t entry_at(const Lds &L, const Src &src, uint32_t pn, uint32_t &bad) {
+    const uint32_t top = src.peek(pn);
+    const uint32_t ent = L.lut.l1[top >> (32 - kL1Bits)];
+    return ent ? ent : long_entry(L.lut, top, bad);
+}
+
+__device__ __forceinline__ uint32_t ent_count(uint32_t ent) { return ent >> kEntCountShift; }
+__device__ __forceinline__ uint32_t ent_bits(uint32_t ent) { return (ent >> kEntLenShift) & 31u; }
+
+// Store an entry's three code bytes at tile bytes q..q+2 (byte stores: an
+// unaligned 4-byte store stalls the LDS more than three aligned ones).
+// Bytes past the entry's codes are garbage that a later store of the same
+// window overwrites; callers guarantee they stay inside the window.
+__device__ __forceinline__ void put4(Lds &L, uint32_t q, uint32_t ent) {
+    L.tile[q] = (uint8_t)ent;
+    L.tile[q + 1] = (uint8_t)(ent >> 8);
+    L.tile[q + 2] = (uint8_t)(ent >> 16);
+}
+
+// Decode both windows of this lane.  pa/pb: negated start bits; qa/qb: tile
+// positions; na/nb: code counts; T: look-ups after which every window of the
+// wave still has at least three codes left.  Returns the negated end bits.
+template <class Src>
+__device__ __forceinline__ void decode_pair(Lds &L, const Src &src, uint32_t &pa, uint32_t &pb,
+                                            uint32_t qa, uint32_t qb, uint32_t na, uint32_t nb,
+                                            uint32_t T, uint32_t &bad) {
+    const uint32_t qa0 = qa, qb0 = qb;
+    // 1. counted (the caller keeps the starts at least 24*T bits below the
+    //    source's end, so these peeks need no clamp): every look-up's codes and the garbage behind them stay
+    //    inside the window (at least three codes remain afterwards)
+    for (uint32_t t = 0; t < T; ++t) {
+        uint32_t ta, tb, ea, eb;
+        if constexpr (Src::kLds) {
+            // both windows' LDS round trips overlap: the fences keep the
+            // scheduler from serializing them (addresses | both code reads |
+            // funnel shifts and table indices | both table reads)
+            const uint32_t ja = (31u - pa) >> 5, jb = (31u - pb) >> 5;
+            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t a0 = src.w[ja], a1 = src.w[ja + 1];
+            const uint32_t b0 = src.w[jb], b1 = src.w[jb + 1];
+            __builtin_amdgcn_sched_barrier(0);
+            ta = __builtin_amdgcn_alignbit(a0, a1, pa);
+            tb = __builtin_amdgcn_alignbit(b0, b1, pb);
+            const uint32_t ia = ta >> (32 - kL1Bits), ib = tb >> (32 - kL1Bits);
+            __builtin_amdgcn_sched_barrier(0);
+            ea = L.lut.l1[ia];
+            eb = L.lut.l1[ib];
+        } else {
+            ta = src.peek_unclamped(pa);
+            tb = src.peek_unclamped(pb);
+            ea = L.lut.l1[ta >> (32 - kL1Bits)];
+            eb = L.lut.l1[tb >> (32 - kL1Bits)];
+        }
+        if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
+            if (ea == 0) ea = long_entry(L.lut, ta, bad);
+            if (eb == 0) eb = long_entry(L.lut, tb, bad);
+        }
+        put4(L, qa, ea);
+        put4(L, qb, eb);
+        qa += ent_count(ea);
+        pa -= ent_bits(ea);
+        qb += ent_count(eb);
+        pb -= ent_bits(eb);
+    }
+    // 2. masked: windows with at least four codes left take a look-up (its
+    //    garbage still lands inside), the others wait
+    uint32_t ra = na - (qa - qa0), rb = nb - (qb - qb0);
+    while (__ballot((ra >= 4) | (rb >= 4))) {
+        const bool aa = ra >= 4, ab = rb >= 4;
+        const uint32_t ea = entry_at(L, src, pa, bad);
+        const uint32_t eb = entry_at(L, src, pb, bad);
+        put4(L, aa ? qa : kDummy, ea);
+        put4(L, ab ? qb : kDummy, eb);
+        const uint32_t ka = aa ? ent_count(ea) : 0u, kb = ab ? ent_count(eb) : 0u;
+        qa += ka;
+        ra -= ka;
+        pa -= aa ? ent_bits(ea) : 0u;
+        qb += kb;
+        rb -= kb;
+        pb -= ab ? ent_bits(eb) : 0u;
+    }
+    // 3. exact: the last (at most three) codes of each window, byte stores
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t &pn = w ? pb : pa;
+        uint32_t &q = w ? qb : qa;
+        uint32_t &r = w ? rb : ra;
+        while (r > 0) {
+            const uint32_t ent = entry_at(L, src, pn, bad);
+            uint32_t n = ent_count(ent), c = ent_bits(ent);
+            if (n > r) {
+                n = r;
+                c = 0;
+                for (uint32_t k = 0; k < n; ++k) c += L.lut.len[(ent >> (8 * k)) & 0xFFu];
+            }
+            for (uint32_t k = 0; k < n; ++k) L.tile[q + k] = (uint8_t)(ent >> (8 * k));
+            q += n;
+            r -= n;
+            pn -= c;
+        }
+    }
 }
 
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
@@ -167,9 +294,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         const TensorDesc &d = a.desc[a.tensor_base + tl];
         const uint8_t *__restrict__ C = a.containers[tl];
         uint16_t *__restrict__ out = a.outs[tl];
-        const uint64_t n_elems = d.n_elems;
         const uint64_t elem0 = (uint64_t)chunk * kChunk;
-        const uint32_t nc = (uint32_t)min<uint64_t>(kChunk, n_elems - elem0);
+        const uint32_t nc = (uint32_t)umin64(kChunk, d.n_elems - elem0);
 
         // ---- decode tables of this tensor -> LDS
         if (d.lut_index != cur_lut) {
@@ -180,43 +306,51 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
             cur_lut = d.lut_index;
         }
 
-        // ---- chunk index
+        // ---- chunk index and this lane's two windows
         const uint64_t *ci = reinterpret_cast<const uint64_t *>(C + d.off_ci) + 2 * (uint64_t)chunk;
         const uint64_t b0 = ci[0];
-        const uint64_t b1 = max(ci[2], b0);
-        const uint32_t gap = C[d.off_gap + (uint64_t)chunk * kLanes + lane];
-        const uint32_t cnt = reinterpret_cast<const uint16_t *>(C + d.off_cnt)[(uint64_t)chunk * kLanes + lane];
+        const uint64_t b1 = umax64(ci[2], b0);
+        const uint32_t gaps = reinterpret_cast<const uint16_t *>(C + d.off_gap)[(uint64_t)chunk * 64 + lane];
+        const uint32_t cnts = reinterpret_cast<const uint32_t *>(C + d.off_cnt)[(uint64_t)chunk * 64 + lane];
 
         // ---- stage the code bytes (16-byte aligned window) and prefetch raw
         const uint8_t *stream = C + d.off_stream;
         const uint64_t sbytes = d.stream_bytes;
-        const uint64_t s0 = min<uint64_t>((b0 >> 3) & ~(uint64_t)15, sbytes - 16);
-        const uint64_t s_end = min<uint64_t>((((b1 + 127) >> 3) + 15) & ~(uint64_t)15, sbytes);
+        const uint64_t s0 = umin64((b0 >> 3) & ~(uint64_t)15, sbytes - 16);
+        const uint64_t s_end = umax64(umin64((((b1 + 127) >> 3) + 15) & ~(uint64_t)15, sbytes), s0 + 16);
         const bool staged = s_end <= s0 + kCodeCap;
+        // 32-bit offsets from here on: a staged window is < kCodeCap bytes
+        const uint32_t s_len = (uint32_t)umin64(s_end - s0, kCodeCap);
 
         u32x4 cw[kCodeCap / 1024];
         if (staged) {
 #pragma unroll
             for (int k = 0; k < kCodeCap / 1024; ++k) {
-                const uint64_t off = min<uint64_t>(s0 + 1024 * k + 16 * lane, sbytes - 16);
-                cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + off));
+                // past the chunk's bytes the address repeats (a cache hit, no
+                // extra HBM traffic) so that the load count stays fixed
+                const uint32_t off = min(1024u * k + 16u * lane, s_len - 16u);
+                cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + s0 + off));
             }
         }
-        const uint8_t *raw = C + d.off_raw;
-        const uint64_t raw_last = d.raw_bytes - 8;
-        u32x2 rw[2 * kBlocks];
+        const uint8_t *raw = C + d.off_raw + elem0 + 8 * lane;
+        u32x2 rw[kHalfBlocks];
+        if (nc == (uint32_t)kChunk) {
 #pragma unroll
-        for (int b = 0; b < 2 * kBlocks; ++b) {
-            const uint64_t j = min<uint64_t>(elem0 + 512 * b + 8 * lane, raw_last);
-            rw[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(raw + j));
+            for (int b = 0; b < kHalfBlocks; ++b)
+                rw[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(raw + 512 * b));
+        } else {
+            // the tensor's last chunk: stay inside the raw bytes (padded to 16)
+            const uint8_t *raw0 = C + d.off_raw + elem0;
+            const uint32_t jmax = ((uint32_t)umin64(d.raw_bytes - elem0, 2 * kChunk) - 8u) & ~7u;
+#pragma unroll
+            for (int b = 0; b < kHalfBlocks; ++b)
+                rw[b] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x2 *>(raw0 + min(512u * b + 8u * lane, jmax)));
         }
 
-        // ---- zero the tile; write the staged words
+        // ---- write the staged words (every tile byte of the chunk gets
+        //      written by the decode, so the tile needs no clearing)
         __syncthreads();
-        {
-            u32x4 *t4 = reinterpret_cast<u32x4 *>(L.tile);
-            for (uint32_t i = lane; i < sizeof(L.tile) / 16; i += 64) t4[i] = u32x4{0, 0, 0, 0};
-        }
         if (staged) {
 #pragma unroll
             for (int k = 0; k < kCodeCap / 1024; ++k) {
@@ -225,56 +359,83 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
                 v.y = bswap32(v.y);
                 v.z = bswap32(v.z);
                 v.w = bswap32(v.w);
-                reinterpret_cast<u32x4 *>(L.codes)[64 * k + lane] = v;
+                reinterpret_cast<u32x4 *>(L.codes + 1)[64 * k + lane] = v;
             }
         }
 
-        // ---- lane windows: first code position and output position
-        const uint64_t W = (b1 - b0 + kLanes - 1) / kLanes;
-        const uint32_t incl = wave_inclusive_sum(cnt);
-        const uint32_t q0 = incl - cnt;
-        // never write past the tile, whatever the device bytes say
-        uint32_t rem = q0 < nc ? min(cnt, nc - q0) : 0u;
-        const uint64_t start = b0 + lane * W + (cnt ? gap : 0u);
+        // ---- windows 2*lane (a) and 2*lane+1 (b): starts and output positions
+        const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
+        uint32_t na = cnts & 0xFFFFu, nb = cnts >> 16;
+        const uint32_t incl = wave_inclusive_sum(na + nb);
+        const uint32_t qa = incl - na - nb;
+        const uint32_t qb = qa + na;
+        // never write past the chunk, whatever the device bytes say
+        uint32_t bad = 0;
+        {
+            const uint32_t ca = qa < nc ? min(na, nc - qa) : 0u;
+            const uint32_t cb = qb < nc ? min(nb, nc - qb) : 0u;
+            bad |= (ca != na) | (cb != nb);
+            na = ca;
+            nb = cb;
+        }
+        const uint64_t sa = b0 + (2 * lane) * W + (na ? (gaps & 0xFFu) : 0u);
+        const uint64_t sb = b0 + (2 * lane + 1) * W + (nb ? (gaps >> 8) : 0u);
+        const uint32_t mn = wave_min(min(na, nb));
+        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
         __syncthreads();
 
-        uint32_t bad = 0;
-        uint64_t stop = start;
-        if (rem > 0) {
-            if (staged) {
-                stop = decode_window<true>(L, L.codes, kCodeWords, start - 8 * s0, q0, rem, bad) + 8 * s0;
-            } else {
-                stop = decode_window<false>(L, reinterpret_cast<const uint32_t *>(stream),
-                                            (uint32_t)(sbytes / 4), start, q0, rem, bad);
-            }
+        uint64_t ea, eb;
+        // Window starts relative to the bytes from s0, negated.  Peeks at
+        // p <= pmax stay inside the source; the counted loop moves a window
+        // by at most 24*T bits, so starts are kept at or below pmax - 24*T
+        // (only a container that disagrees with its index starts higher).
+        const uint32_t n_words = (uint32_t)umin64((sbytes - s0) / 4, 1u << 25);
+        const uint32_t pmax = staged ? 32u * (kCodeWords - 1) : 32u * (n_words - 1);
+        T = min(T, pmax / 48u);
+        const uint64_t plim = pmax - 24u * T;
+        uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wraps high when below s0
+        bad |= (pra > plim) | (prb > plim);
+        uint32_t pa = 0u - (uint32_t)umin64(pra, plim), pb = 0u - (uint32_t)umin64(prb, plim);
+        if (staged) {
+            // peeks read codes[j], codes[j+1] with j <= kCodeWords
+            const LdsCodes src{L.codes, 0u - pmax};
+            decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
+        } else {
+            // peeks read words j-1 and j of the stream from s0, j < n_words
+            const GlobalCodes src{reinterpret_cast<const uint32_t *>(stream + s0) - 1, 0u - pmax};
+            decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
         }
+        ea = 8 * s0 + (uint32_t)(0u - pa);
+        eb = 8 * s0 + (uint32_t)(0u - pb);
 
-        // ---- each non-empty window must end where the next one's first code
-        //      starts, the last one at the chunk end
-        const uint64_t mask = __ballot(cnt != 0);
-        const uint64_t next_start = __shfl_down((unsigned long long)start, 1);
+        // ---- every non-empty window ends where the next non-empty window's
+        //      first code starts; the last one at the chunk end
+        const uint64_t mask = __ballot(na + nb != 0);
+        const uint64_t first = na ? sa : sb;          // this lane's first code
         const uint64_t above = lane == 63 ? 0 : (mask >> (lane + 1));
-        if (cnt != 0) {
-            if (above == 0) bad |= stop != b1;
-            else if (above & 1) bad |= stop != next_start;
-        }
-        if (rem != cnt) bad = 1;
+        const uint32_t nxt_lane = above ? lane + 1 + (uint32_t)__builtin_ctzll(above) : lane;
+        const uint64_t nxt_first = __shfl((unsigned long long)first, (int)nxt_lane);
+        const uint64_t after_b = above ? nxt_first : b1;
+        if (nb) bad |= eb != after_b;
+        if (na) bad |= ea != (nb ? sb : after_b);
         bad_any |= bad;
         __syncthreads();
 
         // ---- assemble and store
         uint16_t *o = out + elem0;
 #pragma unroll
-        for (int b = 0; b < 2 * kBlocks; ++b) {
+        for (int b = 0; b < kHalfBlocks; ++b) {
             const uint32_t j = 512 * b + 8 * lane;
             if (512u * b >= nc) break;
-            const u32x2 e8 = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const uint8_t *>(L.tile) + j);
-            const u32x4 v = join8(e8, rw[b]);
+            const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
+            const u32x4 v = join8(t8, rw[b]);
             if (j + 8 <= nc) {
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(o + j));
             } else if (j < nc) {
-                const uint32_t part[4] = {v.x, v.y, v.z, v.w};
-                for (uint32_t k = 0; j + k < nc; ++k) o[j + k] = (uint16_t)(part[k >> 1] >> (16 * (k & 1)));
+                for (uint32_t k = 0; j + k < nc; ++k) {
+                    const uint32_t wd = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
+                    o[j + k] = (uint16_t)(wd >> (16 * (k & 1)));
+                }
             }
         }
     }

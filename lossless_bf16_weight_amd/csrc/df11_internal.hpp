@@ -10,33 +10,58 @@ namespace df11 {
 constexpr uint32_t kVersion = 1;
 constexpr uint32_t kHeader = DF11_HEADER_BYTES;
 constexpr uint32_t kChunk = DF11_CHUNK_ELEMS;
-constexpr int kLanes = DF11_LANES;
+constexpr int kWindows = DF11_WINDOWS;
 constexpr int kMaxLen = DF11_MAX_CODE_LEN;
 
+// Exponent bytes are handled rotated right by one bit inside the decoder,
+// rot(e) = (e >> 1) | (e & 1) << 7, so that a BF16 word splits into the two
+// bytes [sign | e >> 1] and [e & 1 | fraction]: the decode tables hold rot(e)
+// and the join of tile bytes with raw bytes is two byte permutes and one
+// bitfield insert per pair of words.
+#if defined(__HIPCC__)
+#define DF11_HD __host__ __device__
+#else
+#define DF11_HD
+#endif
+DF11_HD constexpr uint8_t rot_exp(unsigned e) {
+    return (uint8_t)(((e >> 1) | (e << 7)) & 0xFFu);
+}
+
 // First-level decode table: indexed by the next kL1Bits bits of the stream.
-// Entry: bits 0..23 up to three exponent bytes (first code in the low byte),
-// bits 24..27 how many stream bits they use, bits 28..29 how many codes (1..3).
-// Entry 0: the next code is longer than kL1Bits (or no code matches: a
-// prefix no valid stream contains), resolved by the canonical tables.
+// Entry: bits 0..23 up to three rotated exponent bytes (first code in the
+// low byte), bits 24..28 how many stream bits they use, bits 29..30 how many
+// codes (1..3).  Entry 0: the next code is longer than kL1Bits (or no code
+// matches: a prefix no valid stream holds).
 constexpr int kL1Bits = 10;
 constexpr int kL1Size = 1 << kL1Bits;
 constexpr int kMaxPerLookup = 3;
+constexpr uint32_t kEntLenShift = 24;
+constexpr uint32_t kEntCountShift = 29;
+// Second-level table for codes of kL1Bits+1 .. kL2Bits bits, indexed by the
+// next kL2Bits bits minus l2_base (= the first such prefix); entry
+// (length << 8) | rot(e), 0 when the code is longer than kL2Bits.
+constexpr int kL2Bits = 16;
+constexpr int kL2Max = 512;
 
 // Per-tensor table record in device memory (and copied whole into LDS).
 struct alignas(16) LutRecord {
     uint32_t l1[kL1Size];
+    uint16_t l2[kL2Max];
     // lim[l]: 24-bit left-aligned exclusive upper bound of the codes of
     // length <= l (l = 1..24); a peeked 24-bit value v has a code of length l
     // exactly when lim[l-1] <= v < lim[l].
     uint32_t lim[32];
     // base[l] = (index of the first length-l symbol in `sorted`) - (its code)
     int32_t base[32];
-    // exponent bytes sorted by (code length, value)
+    // rotated exponent bytes sorted by (code length, exponent)
     uint8_t sorted[256];
-    // code length of every exponent byte (0 = absent)
+    // code length by rotated exponent byte (0 = absent)
     uint8_t len[256];
+    uint32_t l2_base;
+    uint32_t l2_size;
+    uint32_t pad[2];
 };
-static_assert(sizeof(LutRecord) == 4864, "LUT record size");
+static_assert(sizeof(LutRecord) == 5904, "LUT record size");
 
 // Per-tensor descriptor in device memory.
 struct alignas(16) TensorDesc {

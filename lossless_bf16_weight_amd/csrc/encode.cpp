@@ -11,7 +11,7 @@
 // is the context for doing this fast on CPU cores.
 //
 // Parallel plan: histogram per thread slice; one chunk per task for the bit
-// counts, the packing and the lane index (chunks start at known bit offsets
+// counts, the packing and the window index (chunks start at known bit offsets
 // once the per-chunk bit counts are summed); raw bytes per slice.  The output
 // does not depend on the thread count.
 #include <algorithm>
@@ -162,8 +162,8 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
     // layout
     const uint64_t off_ci = kHeader;
     const uint64_t off_gap = up256(off_ci + (n_chunks + 1) * 16);
-    const uint64_t off_cnt = up256(off_gap + n_chunks * kLanes);
-    const uint64_t off_stream = up256(off_cnt + n_chunks * kLanes * 2);
+    const uint64_t off_cnt = up256(off_gap + n_chunks * kWindows);
+    const uint64_t off_stream = up256(off_cnt + n_chunks * kWindows * 2);
     const uint64_t stream_bytes = up16((total_bits + 7) / 8) + 16;
     const uint64_t off_raw = up256(off_stream + stream_bytes);
     const uint64_t raw_bytes = up16(n);
@@ -184,7 +184,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
     wr32(out + 28, kChunk);
     for (int i = 0; i < ndim; ++i) wr64(out + 32 + 8 * i, dims[i]);
     out[96] = kMaxLen;
-    out[97] = kLanes;
+    out[97] = kWindows;
     wr32(out + 100, (uint32_t)n_chunks);
     wr64(out + 104, total_bits);
     wr64(out + 112, off_ci);
@@ -201,26 +201,26 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         wr64(out + off_ci + c * 16 + 8, std::min<uint64_t>(c * kChunk, n));
     }
 
-    // 5. pack each chunk's codes and build its lane index
+    // 5. pack each chunk's codes and build its window index
     uint8_t *stream = out + off_stream;
     parallel_for(n_chunks, threads, [&](uint64_t c) {
         thread_local std::vector<uint8_t> buf;
         const uint64_t lo = c * kChunk, hi = std::min<uint64_t>(n, lo + kChunk);
         const uint64_t b0 = start[c], b1 = start[c + 1];
-        const uint64_t W = (b1 - b0 + kLanes - 1) / kLanes;
+        const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
         const unsigned head = (unsigned)(b0 & 7);
         const uint64_t nbytes = (head + (b1 - b0) + 7) / 8;
         buf.assign(nbytes + 8, 0);
-        unsigned cnt[kLanes] = {};
-        uint8_t gap[kLanes];
+        unsigned cnt[kWindows] = {};
+        uint8_t gap[kWindows];
         memset(gap, 0xFF, sizeof gap);
         uint64_t acc = 0;   // pending bits, right-aligned
         unsigned nacc = head;
         uint64_t at = 0, pos = 0;   // output byte, chunk-relative bit position
         for (uint64_t j = lo; j < hi; ++j) {
             const unsigned e = (w[j] >> 7) & 0xFF;
-            const unsigned lane = (unsigned)(pos / W);
-            if (cnt[lane]++ == 0) gap[lane] = (uint8_t)(pos - lane * W);
+            const unsigned win = (unsigned)(pos / W);
+            if (cnt[win]++ == 0) gap[win] = (uint8_t)(pos - win * W);
             acc = (acc << len[e]) | code[e];
             nacc += len[e];
             pos += len[e];
@@ -237,8 +237,8 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
             if (shared) __atomic_fetch_or(&stream[first + i], buf[i], __ATOMIC_RELAXED);
             else stream[first + i] = buf[i];
         }
-        memcpy(out + off_gap + c * kLanes, gap, kLanes);
-        for (int i = 0; i < kLanes; ++i) wr16(out + off_cnt + c * kLanes * 2 + 2 * i, (uint16_t)cnt[i]);
+        memcpy(out + off_gap + c * kWindows, gap, kWindows);
+        for (int i = 0; i < kWindows; ++i) wr16(out + off_cnt + c * kWindows * 2 + 2 * i, (uint16_t)cnt[i]);
     });
 
     // 6. raw bytes

@@ -80,8 +80,8 @@ Layout layout_for(uint64_t n, uint64_t total_bits) {
     L.total_bits = total_bits;
     L.off_ci = kHeader;
     L.off_gap = up256(L.off_ci + (L.n_chunks + 1) * 16);
-    L.off_cnt = up256(L.off_gap + L.n_chunks * kLanes);
-    L.off_stream = up256(L.off_cnt + L.n_chunks * kLanes * 2);
+    L.off_cnt = up256(L.off_gap + L.n_chunks * kWindows);
+    L.off_stream = up256(L.off_cnt + L.n_chunks * kWindows * 2);
     L.stream_bytes = up16((total_bits + 7) / 8) + 16;
     L.off_raw = up256(L.off_stream + L.stream_bytes);
     L.raw_bytes = up16(n);
@@ -131,8 +131,8 @@ inline int lookup(const Canon &C, int l, uint32_t code) {
 void build_lut(const uint8_t *len, LutRecord &R) {
     memset(&R, 0, sizeof R);
     Canon C = canonical(len);
-    for (int i = 0; i < C.n_sym; ++i) R.sorted[i] = C.sorted[i];
-    memcpy(R.len, len, 256);
+    for (int i = 0; i < C.n_sym; ++i) R.sorted[i] = rot_exp(C.sorted[i]);
+    for (int s = 0; s < 256; ++s) R.len[rot_exp(s)] = len[s];
     for (int l = 0; l < 32; ++l) { R.lim[l] = 0xFFFFFFFFu; R.base[l] = 0; }
     R.lim[0] = 0;
     for (int l = 1; l <= kMaxLen; ++l) {
@@ -141,7 +141,7 @@ void build_lut(const uint8_t *len, LutRecord &R) {
     }
     // First level: greedily resolve up to three whole codes inside the next
     // kL1Bits bits.  A prefix that starts with no code of <= kL1Bits bits
-    // keeps entry 0.
+    // keeps entry 0 (also every prefix no valid stream holds).
     for (uint32_t v = 0; v < (uint32_t)kL1Size; ++v) {
         int pos = 0, n = 0;
         uint32_t syms = 0;
@@ -153,11 +153,25 @@ void build_lut(const uint8_t *len, LutRecord &R) {
                 flen = l;
             }
             if (found < 0) break;
-            syms |= (uint32_t)found << (8 * n);
+            syms |= (uint32_t)rot_exp((unsigned)found) << (8 * n);
             pos += flen;
             ++n;
         }
-        R.l1[v] = n ? (syms | ((uint32_t)pos << 24) | ((uint32_t)n << 28)) : 0u;
+        R.l1[v] = n ? (syms | ((uint32_t)pos << kEntLenShift) | ((uint32_t)n << kEntCountShift)) : 0u;
+    }
+    // Second level: 16-bit prefixes from the first one no code of <= kL1Bits
+    // bits covers.
+    R.l2_base = R.lim[kL1Bits] >> (kMaxLen - kL2Bits);
+    R.l2_size = std::min<uint32_t>((1u << kL2Bits) - R.l2_base, kL2Max);
+    for (uint32_t i = 0; i < R.l2_size; ++i) {
+        const uint32_t v = R.l2_base + i;
+        for (int l = kL1Bits + 1; l <= kL2Bits; ++l) {
+            const int s = lookup(C, l, v >> (kL2Bits - l));
+            if (s >= 0) {
+                R.l2[i] = (uint16_t)((l << 8) | rot_exp((unsigned)s));
+                break;
+            }
+        }
     }
 }
 
@@ -170,7 +184,7 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     if (rd32(c + 12) != 0) return fail(DF11_E_UNSUPPORTED, "flags %#x", rd32(c + 12));
     if (rd32(c + 28) != kChunk) return fail(DF11_E_UNSUPPORTED, "chunk_elems %u", rd32(c + 28));
     if (c[96] != kMaxLen) return fail(DF11_E_UNSUPPORTED, "max_code_len %u", c[96]);
-    if (c[97] != kLanes) return fail(DF11_E_UNSUPPORTED, "lanes %u", c[97]);
+    if (c[97] != kWindows) return fail(DF11_E_UNSUPPORTED, "windows %u", c[97]);
     const uint64_t n = rd64(c + 16), total_bits = rd64(c + 104);
     if (n > (uint64_t(1) << 46)) return fail(DF11_E_UNSUPPORTED, "n_elems %llu", (unsigned long long)n);
     if (total_bits > n * kMaxLen || total_bits < n)
@@ -212,7 +226,7 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
 
     if (bytes < L.off_stream) return fail(DF11_E_FORMAT, "prefix of %zu bytes does not hold the index (%llu)",
                                           bytes, (unsigned long long)L.off_stream);
-    // chunk index and lane windows
+    // chunk index and windows
     for (uint64_t ch = 0; ch <= L.n_chunks; ++ch) {
         const uint8_t *e = c + L.off_ci + ch * 16;
         const uint64_t sb = rd64(e), oe = rd64(e + 8);
@@ -225,21 +239,21 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
         const uint64_t elems = std::min<uint64_t>(kChunk, n - ch * kChunk);
         if (sb > b1 || b1 - sb < elems || b1 - sb > elems * kMaxLen)
             return fail(DF11_E_FORMAT, "chunk %llu bit range", (unsigned long long)ch);
-        const uint64_t W = (b1 - sb + kLanes - 1) / kLanes;
+        const uint64_t W = (b1 - sb + kWindows - 1) / kWindows;
         uint64_t sum = 0;
-        for (int i = 0; i < kLanes; ++i) {
-            const unsigned gap = c[L.off_gap + ch * kLanes + i];
-            const unsigned cnt = rd16(c + L.off_cnt + ch * kLanes * 2 + 2 * i);
+        for (int i = 0; i < kWindows; ++i) {
+            const unsigned gap = c[L.off_gap + ch * kWindows + i];
+            const unsigned cnt = rd16(c + L.off_cnt + ch * kWindows * 2 + 2 * i);
             const uint64_t ws = sb + i * W, we = std::min<uint64_t>(sb + (i + 1) * W, b1);
             sum += cnt;
             if (cnt == 0) {
-                if (gap != 0xFF) return fail(DF11_E_FORMAT, "chunk %llu lane %d: gap without codes", (unsigned long long)ch, i);
+                if (gap != 0xFF) return fail(DF11_E_FORMAT, "chunk %llu window %d: gap without codes", (unsigned long long)ch, i);
                 continue;
             }
             if (gap >= (unsigned)kMaxLen || ws >= b1 || ws + gap >= we || cnt > we - ws - gap)
-                return fail(DF11_E_FORMAT, "chunk %llu lane %d: gap %u cnt %u", (unsigned long long)ch, i, gap, cnt);
+                return fail(DF11_E_FORMAT, "chunk %llu window %d: gap %u cnt %u", (unsigned long long)ch, i, gap, cnt);
         }
-        if (sum != elems) return fail(DF11_E_FORMAT, "chunk %llu: lane counts sum to %llu, not %llu",
+        if (sum != elems) return fail(DF11_E_FORMAT, "chunk %llu: window counts sum to %llu, not %llu",
                                       (unsigned long long)ch, (unsigned long long)sum, (unsigned long long)elems);
     }
     // padding of the stream and the raw section, when the bytes are there
@@ -265,7 +279,7 @@ void fill_info(const Meta &M, df11_tensor_info *info) {
     info->container_bytes = L.total;
     info->meta_bytes = L.off_stream;
     info->bytes_read_per_decode =
-        (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kLanes * 3 + (L.total_bits + 7) / 8 + L.n;
+        (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kWindows * 3 + (L.total_bits + 7) / 8 + L.n;
     memcpy(info->code_len, M.code_len, 256);
 }
 
@@ -491,7 +505,7 @@ extern "C" df11_status df11_check(df11_plan_t p, hipStream_t stream) {
     if (flag) {
         const uint32_t zero = 0;
         HIP_TRY(hipMemcpy(p->d_status, &zero, sizeof zero, hipMemcpyHostToDevice));
-        return fail(DF11_E_CORRUPT, "a decode found a lane whose codes did not end at the next code start");
+        return fail(DF11_E_CORRUPT, "a decode found a window whose codes did not end where the next window's first code starts");
     }
     return DF11_OK;
 }

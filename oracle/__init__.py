@@ -30,7 +30,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 OK, E_ARG, E_FORMAT, E_CORRUPT, E_TRUNCATED = 0, 1, 2, 3, 4
 CHUNK = 32768
-LANES = 64
+WINDOWS = 128
 CAP = 24
 
 
@@ -61,7 +61,7 @@ def _configure(L):
                                 ctypes.c_uint64, u64p]
     L.oracle_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64]
     L.oracle_decode_chunk.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64, u16p]
-    L.oracle_decode_lane.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
+    L.oracle_decode_window.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
                                      u16p, u64p, u64p]
     L.oracle_check.argtypes = [u8p, ctypes.c_uint64]
     return L
@@ -151,17 +151,17 @@ def decode_chunk(container: np.ndarray, chunk: int, n_chunk: int) -> np.ndarray:
     return out
 
 
-def decode_lane(container: np.ndarray, chunk: int, lane: int):
-    """Decode one lane window; returns (words, end_bit)."""
+def decode_window(container: np.ndarray, chunk: int, win: int):
+    """Decode one window of a chunk; returns (words, end_bit)."""
     c = np.ascontiguousarray(container, dtype=np.uint8)
     out = np.zeros(CHUNK, np.uint16)
     n_out = np.zeros(1, np.uint64)
     end = np.zeros(1, np.uint64)
-    st = lib().oracle_decode_lane(_p(c, ctypes.c_uint8), c.size, chunk, lane,
+    st = lib().oracle_decode_window(_p(c, ctypes.c_uint8), c.size, chunk, win,
                                   _p(out, ctypes.c_uint16), _p(n_out, ctypes.c_uint64),
                                   _p(end, ctypes.c_uint64))
     if st:
-        raise OracleError(st, "decode_lane")
+        raise OracleError(st, "decode_window")
     return out[: int(n_out[0])].copy(), int(end[0])
 
 
@@ -186,9 +186,9 @@ def header(container: np.ndarray) -> dict:
     return {
         "n_elems": u64(16), "ndim": ndim,
         "dims": [u64(32 + 8 * i) for i in range(ndim)],
-        "chunk_elems": u32(28), "max_code_len": int(c[96]), "lanes": int(c[97]),
+        "chunk_elems": u32(28), "max_code_len": int(c[96]), "windows": int(c[97]),
         "n_chunks": u32(100), "total_bits": u64(104),
-        "off_chunk_index": u64(112), "off_lane_gap": u64(120), "off_lane_cnt": u64(128),
+        "off_chunk_index": u64(112), "off_win_gap": u64(120), "off_win_cnt": u64(128),
         "off_stream": u64(136), "stream_bytes": u64(144), "off_raw": u64(152),
         "raw_bytes": u64(160), "total_bytes": u64(168),
         "code_len": c[208:464].copy(),

@@ -18,7 +18,7 @@
  *    "Use" (verify): structure, sampled chunks, or full decode.
  *
  * Where the pages are silent (which prefix code, tie-breaks, bit order,
- * chunking, lane windows, padding) this file takes one fixed reading:
+ * chunking, windows, padding) this file takes one fixed reading:
  *  - code: optimal prefix code with maximum length 24, by package-merge
  *    (Larmore and Hirschberg 1990); leaves sorted by (frequency, symbol);
  *    on equal weight a leaf is taken before a package;
@@ -29,22 +29,22 @@
  *    0 is the first bit;
  *  - raw byte: (sign << 7) | fraction, i.e. ((w >> 8) & 0x80) | (w & 0x7F);
  *  - chunks of 32768 elements (64 KiB of BF16 output), each with its start
- *    bit; 64 equal-bit lane windows per chunk with (gap, cnt) per window.
+ *    bit; 128 equal-bit windows per chunk with (gap, cnt) per window.
  *
  * Container version 1 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
  *     0  char[8] magic "DF11HIPC"     8  u32 version (1)   12 u32 flags (0)
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
- *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 lanes
+ *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 windows
  *    98  u16 reserved               100  u32 n_chunks     104 u64 total_bits
- *   112  u64 off_chunk_index        120  u64 off_lane_gap 128 u64 off_lane_cnt
+ *   112  u64 off_chunk_index        120  u64 off_win_gap  128 u64 off_win_cnt
  *   136  u64 off_stream             144  u64 stream_bytes 152 u64 off_raw
  *   160  u64 raw_bytes              168  u64 total_bytes  176 reserved[32]
  *   208  u8 code_len[256]           464  reserved[48]
  *   chunk index: (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
  *                {total_bits, n_elems}
- *   lane gap:    n_chunks x 64 x u8   (0xFF = window holds no code start)
- *   lane cnt:    n_chunks x 64 x u16  (codes that start in the window)
+ *   window gap:  n_chunks x 128 x u8   (0xFF = window holds no code start)
+ *   window cnt:  n_chunks x 128 x u16  (codes that start in the window)
  *   stream:      ceil(total_bits/8) bytes rounded up to 16, plus 16 zero bytes
  *   raw:         n_elems bytes rounded up to 16
  *   Every byte not named above is zero.
@@ -56,7 +56,7 @@
 
 #define CAP 24
 #define CHUNK 32768u
-#define LANES 64
+#define WINDOWS 128
 #define HDR 512u
 
 /* ------------------------------------------------------------------ */
@@ -199,8 +199,8 @@ static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
     L->total_bits = total_bits;
     L->off_ci = HDR;
     L->off_gap = align256(L->off_ci + (L->n_chunks + 1) * 16);
-    L->off_cnt = align256(L->off_gap + L->n_chunks * LANES);
-    L->off_stream = align256(L->off_cnt + L->n_chunks * LANES * 2);
+    L->off_cnt = align256(L->off_gap + L->n_chunks * WINDOWS);
+    L->off_stream = align256(L->off_cnt + L->n_chunks * WINDOWS * 2);
     L->stream_bytes = round16((total_bits + 7) / 8) + 16;
     L->off_raw = align256(L->off_stream + L->stream_bytes);
     L->raw_bytes = round16(n);
@@ -257,7 +257,7 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u32(out + 28, CHUNK);
     for (int i = 0; i < ndim; i++) put_u64(out + 32 + 8 * i, dims[i]);
     out[96] = CAP;
-    out[97] = LANES;
+    out[97] = WINDOWS;
     put_u32(out + 100, (uint32_t)L.n_chunks);
     put_u64(out + 104, total_bits);
     put_u64(out + 112, L.off_ci);
@@ -285,26 +285,27 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u64(out + L.off_ci + L.n_chunks * 16, total_bits);
     put_u64(out + L.off_ci + L.n_chunks * 16 + 8, n);
 
-    /* 5. lane index: 64 windows of W = ceil(chunk bits / 64) bits; per window
-     *    the offset of its first code start and the number of code starts */
+    /* 5. window index: 128 windows of W = ceil(chunk bits / 128) bits; per
+     *    window the offset of its first code start and the number of code
+     *    starts */
     for (uint64_t c = 0; c < L.n_chunks; c++) {
         uint64_t b0 = get_u64(out + L.off_ci + c * 16);
         uint64_t b1 = get_u64(out + L.off_ci + (c + 1) * 16);
-        uint64_t W = (b1 - b0 + LANES - 1) / LANES;
-        uint8_t *gap = out + L.off_gap + c * LANES;
-        uint8_t *cntp = out + L.off_cnt + c * LANES * 2;
-        unsigned cnt[LANES];
+        uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
+        uint8_t *gap = out + L.off_gap + c * WINDOWS;
+        uint8_t *cntp = out + L.off_cnt + c * WINDOWS * 2;
+        unsigned cnt[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
-        for (int i = 0; i < LANES; i++) gap[i] = 0xFF;
+        for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
         uint64_t p = b0;
         uint64_t j_end = (c + 1) * CHUNK < n ? (c + 1) * CHUNK : n;
         for (uint64_t j = c * CHUNK; j < j_end; j++) {
-            uint64_t lane = (p - b0) / W;
-            if (cnt[lane] == 0) gap[lane] = (uint8_t)(p - (b0 + lane * W));
-            cnt[lane]++;
+            uint64_t win = (p - b0) / W;
+            if (cnt[win] == 0) gap[win] = (uint8_t)(p - (b0 + win * W));
+            cnt[win]++;
             p += len[exponent_of(words[j])];
         }
-        for (int i = 0; i < LANES; i++) put_u16(cntp + 2 * i, (uint16_t)cnt[i]);
+        for (int i = 0; i < WINDOWS; i++) put_u16(cntp + 2 * i, (uint16_t)cnt[i]);
     }
 
     /* 6. raw bytes: sign and fraction, as is */
@@ -334,7 +335,7 @@ static int parse(const uint8_t *c, uint64_t bytes, parsed_t *P) {
     uint64_t total_bits = get_u64(c + 104);
     make_layout(n, total_bits, &P->L);
     const layout_t *L = &P->L;
-    if (get_u32(c + 28) != CHUNK || c[96] != CAP || c[97] != LANES) return ORACLE_E_FORMAT;
+    if (get_u32(c + 28) != CHUNK || c[96] != CAP || c[97] != WINDOWS) return ORACLE_E_FORMAT;
     if (get_u32(c + 100) != L->n_chunks) return ORACLE_E_FORMAT;
     if (get_u64(c + 112) != L->off_ci || get_u64(c + 120) != L->off_gap ||
         get_u64(c + 128) != L->off_cnt || get_u64(c + 136) != L->off_stream ||
@@ -407,26 +408,26 @@ int oracle_decode_chunk(const uint8_t *c, uint64_t bytes, uint64_t chunk, uint16
     return pos == get_u64(c + P.L.off_ci + (chunk + 1) * 16) ? ORACLE_OK : ORACLE_E_CORRUPT;
 }
 
-int oracle_decode_lane(const uint8_t *c, uint64_t bytes, uint64_t chunk, int lane,
+int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int win,
                        uint16_t *out, uint64_t *n_out, uint64_t *end_bit) {
     parsed_t P;
     int st = parse(c, bytes, &P);
     if (st) return st;
-    if (chunk >= P.L.n_chunks || lane < 0 || lane >= LANES || !n_out || !end_bit)
+    if (chunk >= P.L.n_chunks || win < 0 || win >= WINDOWS || !n_out || !end_bit)
         return ORACLE_E_ARG;
     const uint8_t *stream = c + P.L.off_stream;
     uint64_t b0 = get_u64(c + P.L.off_ci + chunk * 16);
     uint64_t b1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16);
-    uint64_t W = (b1 - b0 + LANES - 1) / LANES;
-    unsigned gap = c[P.L.off_gap + chunk * LANES + lane];
-    unsigned cnt = get_u16(c + P.L.off_cnt + chunk * LANES * 2 + 2 * lane);
+    uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
+    unsigned gap = c[P.L.off_gap + chunk * WINDOWS + win];
+    unsigned cnt = get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * win);
     /* output position of this window's first code: codes of earlier windows */
     uint64_t before = 0;
-    for (int i = 0; i < lane; i++) before += get_u16(c + P.L.off_cnt + chunk * LANES * 2 + 2 * i);
+    for (int i = 0; i < win; i++) before += get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * i);
     uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8) + before;
     *n_out = cnt;
-    if (cnt == 0) { *end_bit = b0 + lane * W; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
-    uint64_t pos = b0 + lane * W + gap;
+    if (cnt == 0) { *end_bit = b0 + win * W; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
+    uint64_t pos = b0 + win * W + gap;
     for (unsigned k = 0; k < cnt; k++) {
         int e = read_code(&P, stream, &pos);
         if (e < 0) return -e;
@@ -460,7 +461,7 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
     if (present == 1 && kraft != ((uint64_t)1 << (CAP - 1))) return ORACLE_E_FORMAT;
     if (present >= 2 && kraft != ((uint64_t)1 << CAP)) return ORACLE_E_FORMAT;
 
-    /* re-walk the stream: start bits, sentinel, lane windows */
+    /* re-walk the stream: start bits, sentinel, windows */
     const uint8_t *stream = c + L->off_stream;
     uint64_t pos = 0;
     for (uint64_t ch = 0; ch < L->n_chunks; ch++) {
@@ -469,25 +470,25 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
         uint64_t b0 = pos;
         uint64_t b1 = get_u64(ent + 16);
         if (b1 < b0 || b1 > L->total_bits) return ORACLE_E_FORMAT;
-        uint64_t W = (b1 - b0 + LANES - 1) / LANES;
-        unsigned cnt[LANES];
-        int gap[LANES];
+        uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
+        unsigned cnt[WINDOWS];
+        int gap[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
-        for (int i = 0; i < LANES; i++) gap[i] = 0xFF;
+        for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
         uint64_t j_end = (ch + 1) * CHUNK < L->n ? (ch + 1) * CHUNK : L->n;
         for (uint64_t j = ch * CHUNK; j < j_end; j++) {
             if (W == 0) return ORACLE_E_FORMAT;
-            uint64_t lane = (pos - b0) / W;
-            if (lane >= LANES) return ORACLE_E_FORMAT;
-            if (cnt[lane] == 0) gap[lane] = (int)(pos - (b0 + lane * W));
-            cnt[lane]++;
+            uint64_t win = (pos - b0) / W;
+            if (win >= WINDOWS) return ORACLE_E_FORMAT;
+            if (cnt[win] == 0) gap[win] = (int)(pos - (b0 + win * W));
+            cnt[win]++;
             int e = read_code(&P, stream, &pos);
             if (e < 0) return -e;
         }
         if (pos != b1) return ORACLE_E_FORMAT;
-        for (int i = 0; i < LANES; i++) {
-            if (c[L->off_gap + ch * LANES + i] != gap[i]) return ORACLE_E_FORMAT;
-            if (get_u16(c + L->off_cnt + ch * LANES * 2 + 2 * i) != cnt[i]) return ORACLE_E_FORMAT;
+        for (int i = 0; i < WINDOWS; i++) {
+            if (c[L->off_gap + ch * WINDOWS + i] != gap[i]) return ORACLE_E_FORMAT;
+            if (get_u16(c + L->off_cnt + ch * WINDOWS * 2 + 2 * i) != cnt[i]) return ORACLE_E_FORMAT;
         }
     }
     if (pos != L->total_bits) return ORACLE_E_FORMAT;

@@ -49,19 +49,19 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
                   uint8_t *out, uint64_t out_cap, uint64_t *out_bytes);
 
 /* Bit-serial decode of a whole container: reads one bit at a time through
- * the canonical table, ignores the chunk and lane index.  out[n]. */
+ * the canonical table, ignores the chunk and window index.  out[n]. */
 int oracle_decode(const uint8_t *c, uint64_t bytes, uint16_t *out, uint64_t n);
 
 /* Decode one chunk, starting from its start_bit alone (chunk index only). */
 int oracle_decode_chunk(const uint8_t *c, uint64_t bytes, uint64_t chunk, uint16_t *out);
 
-/* Decode the codes of one lane window of a chunk from its gap/cnt entry.
+/* Decode the codes of one window of a chunk from its gap/cnt entry.
  * Writes the cnt decoded words to out and the end bit position to *end_bit. */
-int oracle_decode_lane(const uint8_t *c, uint64_t bytes, uint64_t chunk, int lane,
+int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int win,
                        uint16_t *out, uint64_t *n_out, uint64_t *end_bit);
 
 /* Structural check of a container (header fields, Kraft sum, chunk index
- * against a re-walk of the stream, lane index against the code starts). */
+ * against a re-walk of the stream, window index against the code starts). */
 int oracle_check(const uint8_t *c, uint64_t bytes);
 
 #ifdef __cplusplus

@@ -1,0 +1,154 @@
+"""Host-side checks of libdf11.so (no GPU needed): the library loads and
+exports every function include/df11.h declares; the multi-threaded encoder
+writes exactly the oracle's bytes; the validator accepts the oracle's
+containers and rejects broken ones."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import lossless_bf16_weight_amd as df11
+from lossless_bf16_weight_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "df11.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(df11_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = df11.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.df11_abi_version() == 1
+    assert lib.df11_status_str(2) == b"DF11_E_FORMAT"
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 63, 64, 1000, 32767, 32768, 32769, 100003])
+def test_encoder_matches_oracle_bytes(n):
+    w = W.normal_bf16((n,), seed=n)
+    a = df11.encode(w)
+    b = oracle.encode(w)
+    assert a.size == b.size and (a == b).all()
+
+
+def test_encoder_matches_oracle_on_special_tensors():
+    cases = [
+        W.exhaustive_words(),
+        W.exhaustive_words()[np.random.default_rng(1).permutation(65536)],
+        np.full(70000, 0x3F80, np.uint16),
+        np.where(np.arange(50001) % 7 == 0, 0x0001, 0x8000).astype(np.uint16),
+        W.heavy_tail_bf16((3 * 32768 + 5,), seed=2),
+        W.normal_bf16((3072,), seed=3, mean=1.0, std=0.05),
+    ]
+    for w in cases:
+        a = df11.encode(w)
+        assert (a == oracle.encode(w)).all()
+        assert oracle.check(a) == 0
+
+
+def test_encoder_shapes_and_threads():
+    w = W.normal_bf16((3, 5, 7001), seed=4)
+    ref = oracle.encode(w)
+    for threads in (1, 2, 5, 0):
+        assert (df11.encode(w, threads=threads) == ref).all()
+    info = df11.validate(ref)
+    assert info["ndim"] == 3 and info["dims"] == [3, 5, 7001]
+
+
+def test_validate_accepts_and_describes():
+    w = W.normal_bf16((100000,), seed=5)
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    info = df11.validate(c)
+    assert info["n_elems"] == w.size
+    assert info["n_chunks"] == h["n_chunks"]
+    assert info["total_bits"] == h["total_bits"]
+    assert info["container_bytes"] == c.size
+    assert (info["code_len"] == h["code_len"]).all()
+    n_ch = h["n_chunks"]
+    assert info["bytes_read_per_decode"] == (n_ch + 1) * 16 + n_ch * 128 * 3 + \
+        (h["total_bits"] + 7) // 8 + w.size
+    # the metadata prefix alone is enough
+    assert df11.validate(c[:info["meta_bytes"]])["n_elems"] == w.size
+
+
+def _status(c):
+    return df11.validate_status(c)
+
+
+def test_validate_rejects_broken_containers():
+    w = W.normal_bf16((3 * 32768 + 11,), seed=6)
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    E_FORMAT, E_UNSUPPORTED = 2, 3
+
+    def bad(mutate):
+        x = c.copy()
+        mutate(x)
+        return _status(x)
+
+    def put64(x, off, v):
+        x[off:off + 8] = np.array([v], np.uint64).view(np.uint8)
+
+    assert _status(c) == 0
+    assert bad(lambda x: x.__setitem__(0, ord("X"))) == E_FORMAT                  # magic
+    assert bad(lambda x: x.__setitem__(8, 2)) == E_UNSUPPORTED                   # version
+    assert bad(lambda x: x.__setitem__(97, 64)) == E_UNSUPPORTED                 # windows
+    assert bad(lambda x: x.__setitem__(96, 25)) == E_UNSUPPORTED                 # max length
+    assert bad(lambda x: x.__setitem__(208 + 121, 25)) == E_FORMAT               # length > 24
+    assert bad(lambda x: x.__setitem__(208 + 121, int(x[208 + 121]) + 1)) == E_FORMAT  # Kraft
+    assert bad(lambda x: x.__setitem__(208 + 3, 20)) == E_FORMAT                 # extra symbol
+    ci = h["off_chunk_index"]
+    sb1 = int(c[ci + 16:ci + 24].view(np.uint64)[0])
+    sb2 = int(c[ci + 32:ci + 40].view(np.uint64)[0])
+    assert bad(lambda x: put64(x, ci + 16, sb2 + 1)) == E_FORMAT                 # past the next
+    # (a start bit moved by a few bits can still look consistent: the index
+    # alone cannot tell; the decoder's window-end check reports it)
+    assert bad(lambda x: put64(x, ci + 16, 0)) == E_FORMAT                       # not monotone
+    assert bad(lambda x: put64(x, ci + 24, 5)) == E_FORMAT                       # out_elem
+    cnt0 = h["off_win_cnt"]
+    assert bad(lambda x: x.__setitem__(cnt0, int(x[cnt0]) + 1)) == E_FORMAT      # counts sum
+    gap0 = h["off_win_gap"]
+    assert bad(lambda x: x.__setitem__(gap0 + 7, 30)) == E_FORMAT                # gap >= 24
+
+    def empty_with_gap(x):
+        # move window 5's codes to window 4 and give window 5 a gap
+        k = cnt0 + 2 * 5
+        c5 = int(x[k:k + 2].view(np.uint16)[0])
+        x[k:k + 2] = np.array([0], np.uint16).view(np.uint8)
+        k4 = cnt0 + 2 * 4
+        x[k4:k4 + 2] = (x[k4:k4 + 2].view(np.uint16) + c5).view(np.uint8)
+    assert bad(empty_with_gap) == E_FORMAT
+    assert _status(c[:h["off_win_cnt"] + 10]) == E_FORMAT                        # truncated
+    assert _status(c[:100]) == E_FORMAT
+    assert bad(lambda x: x.__setitem__(h["off_raw"] + w.size, 1)) == E_FORMAT    # raw padding
+    assert bad(lambda x: x.__setitem__(200, 1)) == E_FORMAT                      # reserved
+
+
+def test_validate_rejects_inconsistent_sizes():
+    w = W.normal_bf16((1000,), seed=7)
+    c = oracle.encode(w)
+    x = c.copy()
+    x[16:24] = np.array([999], np.uint64).view(np.uint8)     # n_elems vs shape
+    assert _status(x) == 2
+    x = c.copy()
+    x[104:112] = np.array([12], np.uint64).view(np.uint8)    # total_bits too small
+    assert _status(x) == 2
+
+
+def test_plan_rejects_bad_input_without_a_gpu():
+    # validation happens before any device call
+    w = W.normal_bf16((1000,), seed=8)
+    c = oracle.encode(w)
+    with pytest.raises(df11.DF11Error) as e:
+        df11.Plan([c[:64]])
+    assert e.value.status == 2
+    assert "DF11_E_FORMAT" in str(e.value)

@@ -247,7 +247,7 @@ SHA_FLUX_VEC15 = "2b2473e3773fe5e667f7ad4200ca4c1759ab147ce158cc046af508385c0501
 # ------------------------------------------------------------ the index --
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 32767, 32768, 32769, 3 * 32768 + 1000])
-def test_chunk_and_lane_index_reproduce_the_source(n):
+def test_chunk_and_window_index_reproduce_the_source(n):
     w = W.normal_bf16((n,), seed=n)
     c = oracle.encode(w)
     assert oracle.check(c) == oracle.OK
@@ -259,21 +259,21 @@ def test_chunk_and_lane_index_reproduce_the_source(n):
         lo, hi = ch * 32768, min(n, (ch + 1) * 32768)
         # a chunk decodes from its start bit alone (df11pack, sampled chunks)
         assert (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all()
-        # the 64 lane windows decode exactly their cnt codes, back to back
+        # the 128 windows decode exactly their cnt codes, back to back
         parts, ends = [], []
         b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
-        Wb = (b1 - b0 + 63) // 64
-        for lane in range(64):
-            words, end = oracle.decode_lane(c, ch, lane)
+        Wb = (b1 - b0 + 127) // 128
+        for win in range(128):
+            words, end = oracle.decode_window(c, ch, win)
             parts.append(words)
             if len(words):
-                ends.append((lane, end))
+                ends.append((win, end))
                 # the window's last code starts inside it and may run past it
-                assert b0 + (lane + 1) * Wb <= end or end == b1
-                assert end - min(b1, b0 + (lane + 1) * Wb) < 24
+                assert b0 + (win + 1) * Wb <= end or end == b1
+                assert end - min(b1, b0 + (win + 1) * Wb) < 24
         assert (np.concatenate(parts) == w[lo:hi]).all()
         assert ends[-1][1] == b1
-        gap = c[h["off_lane_gap"] + 64 * ch:h["off_lane_gap"] + 64 * ch + 64]
+        gap = c[h["off_win_gap"] + 128 * ch:h["off_win_gap"] + 128 * ch + 128]
         assert ((gap < 24) | (gap == 0xFF)).all()
 
 
@@ -318,10 +318,10 @@ def test_corruption_is_detected():
     bad[0] ^= 1                                      # magic
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_lane_gap"] + 5] ^= 1                  # a lane gap
+    bad[h["off_win_gap"] + 5] ^= 1                   # a window gap
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_lane_cnt"] + 10] ^= 1                 # a lane count
+    bad[h["off_win_cnt"] + 10] ^= 1                  # a window count
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
     bad[208 + 121] += 1                              # a code length: Kraft breaks

@@ -37,12 +37,12 @@ MUTATIONS = [
      "stream[pos / 8] |= (uint8_t)(0x01u << (pos % 8));", 0),
     ("both bit writer and reader least significant bit first",
      None, None, 0),
-    ("lane gap off by one",
-     "gap[lane] = (uint8_t)(p - (b0 + lane * W));",
-     "gap[lane] = (uint8_t)(p - (b0 + lane * W) + 1);", 0),
-    ("lane window rounds down",
-     "uint64_t W = (b1 - b0 + LANES - 1) / LANES;",
-     "uint64_t W = (b1 - b0) / LANES + 1;", 0),
+    ("window gap off by one",
+     "gap[win] = (uint8_t)(p - (b0 + win * W));",
+     "gap[win] = (uint8_t)(p - (b0 + win * W) + 1);", 0),
+    ("window width rounds down",
+     "uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;",
+     "uint64_t W = (b1 - b0) / WINDOWS + 1;", 0),
     ("chunk start bit recorded after the first code",
      "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos);",
      "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos + 1);", 0),
@@ -89,7 +89,7 @@ def _pins_pass() -> bool:
             strings = {s: format(int(code[s]), "0%db" % int(ln[s])) for s in range(256) if ln[s]}
             if tiny.canonical_code_strings([int(x) for x in ln]) != strings:
                 return False
-        # Gaussian tensor with a ragged tail: index, lanes, sampled chunks
+        # Gaussian tensor with a ragged tail: index, windows, sampled chunks
         w = W.normal_bf16((2 * 32768 + 777,), seed=4)
         c = oracle.encode(w)
         if oracle.check(c) != 0 or not (oracle.decode(c, w.size) == w).all():
@@ -100,7 +100,7 @@ def _pins_pass() -> bool:
             lo, hi = ch * 32768, min(w.size, (ch + 1) * 32768)
             if not (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all():
                 return False
-            parts = [oracle.decode_lane(c, ch, lane)[0] for lane in range(64)]
+            parts = [oracle.decode_window(c, ch, win)[0] for win in range(128)]
             if not (np.concatenate(parts) == w[lo:hi]).all():
                 return False
         return True
