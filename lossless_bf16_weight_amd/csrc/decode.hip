@@ -273,6 +273,94 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, uint32_t &pa
     }
 }
 
+// Loads of data that no thread writes during the kernel (work list,
+// descriptors, chunk index) through the constant address space: with a
+// uniform address they become scalar loads, which wait on their own counter
+// instead of behind the vector loads and stores in flight.
+template <class T>
+__device__ __forceinline__ T const_load(const T *p) {
+    return *(const __attribute__((address_space(4))) T *)p;
+}
+
+// One work item (a chunk of a tensor) and where its bytes are.
+struct Item {
+    const uint8_t *stream;   // the container's sections
+    const uint8_t *raw;      //   (raw: from the chunk's first element)
+    const uint8_t *gap;
+    const uint8_t *cnt;
+    uint16_t *out;           // from the chunk's first element
+    uint64_t b0, b1;         // the chunk's stream bits
+    uint64_t s0;             // first staged stream byte (16-byte aligned)
+    uint64_t stream_bytes;
+    uint32_t raw_left;       // raw bytes from the chunk's first element (<= 64 KiB)
+    uint32_t chunk, nc;      // chunk index, elements
+    uint32_t s_len;          // staged bytes
+    uint32_t staged;         // the chunk's codes fit the LDS area
+    uint32_t lut;
+};
+
+__device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
+    uint32_t tl, chunk;
+    if (a.work) {
+        const uint32_t w = const_load(a.work + item);
+        tl = w >> kItemChunkBits;
+        chunk = w & kItemChunkMask;
+    } else {
+        tl = 0;
+        chunk = item;
+    }
+    Item it;
+    const TensorDesc *d = a.desc + a.tensor_base + tl;
+    const uint8_t *C = a.containers[tl];
+    const uint64_t elem0 = (uint64_t)chunk * kChunk;
+    it.stream = C + const_load(&d->off_stream);
+    it.raw = C + const_load(&d->off_raw) + elem0;
+    it.gap = C + const_load(&d->off_gap);
+    it.cnt = C + const_load(&d->off_cnt);
+    it.out = a.outs[tl] + elem0;
+    it.chunk = chunk;
+    it.nc = (uint32_t)umin64(kChunk, const_load(&d->n_elems) - elem0);
+    it.raw_left = (uint32_t)umin64(const_load(&d->raw_bytes) - elem0, 2 * kChunk);
+    it.lut = const_load(&d->lut_index);
+    const uint64_t *ci = reinterpret_cast<const uint64_t *>(C + const_load(&d->off_ci)) + 2 * (uint64_t)chunk;
+    it.b0 = const_load(ci);
+    it.b1 = umax64(const_load(ci + 2), it.b0);
+    const uint64_t sbytes = const_load(&d->stream_bytes);
+    it.stream_bytes = sbytes;
+    it.s0 = umin64((it.b0 >> 3) & ~(uint64_t)15, sbytes - 16);
+    const uint64_t s_end = umax64(umin64((((it.b1 + 127) >> 3) + 15) & ~(uint64_t)15, sbytes), it.s0 + 16);
+    it.staged = s_end <= it.s0 + kCodeCap ? 1u : 0u;
+    it.s_len = (uint32_t)umin64(s_end - it.s0, kCodeCap);
+    return it;
+}
+
+// The staged code bytes of an item: 16 bytes per lane per 1 KiB.  Past the
+// chunk's bytes the address repeats (a cache hit, no extra HBM traffic) so
+// that the load count stays fixed.
+__device__ __forceinline__ void load_codes(const Item &it, uint32_t lane, u32x4 (&cw)[kCodeCap / 1024]) {
+    const uint8_t *stream = it.stream + it.s0;
+#pragma unroll
+    for (int k = 0; k < kCodeCap / 1024; ++k) {
+        const uint32_t off = min(1024u * k + 16u * lane, it.s_len - 16u);
+        cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + off));
+    }
+}
+
+// Raw bytes of store block b (elements 512b + 8 lane .. +8) of an item; a
+// partial chunk reads inside its (16-byte padded) raw bytes only.
+__device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t lane, int b) {
+    uint32_t j = 512u * b + 8u * lane;
+    if (it.nc != (uint32_t)kChunk) j = min(j, (it.raw_left - 8u) & ~7u);
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(it.raw + j));
+}
+
+// Both windows' (gap, cnt) of this lane: gaps in the low 16 bits of x, the
+// two counts in y.
+__device__ __forceinline__ u32x2 load_windows(const Item &it, uint32_t lane) {
+    const uint64_t w = (uint64_t)it.chunk * 64 + lane;
+    return u32x2{reinterpret_cast<const uint16_t *>(it.gap)[w], reinterpret_cast<const uint32_t *>(it.cnt)[w]};
+}
+
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     __shared__ Lds L;
     const uint32_t lane = threadIdx.x;
@@ -280,78 +368,45 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     const uint32_t end = (uint32_t)((uint64_t)a.n_items * (blockIdx.x + 1) / gridDim.x);
     uint32_t cur_lut = 0xFFFFFFFFu;
     uint32_t bad_any = 0;
+    if (begin >= end) return;
+
+    // Software pipeline over the wave's items: while item i decodes, the
+    // code bytes of item i+1 are in flight, and its raw bytes are requested
+    // block by block as item i's assembly frees the registers.
+    u32x4 cw[kCodeCap / 1024];
+    u32x2 rw[kHalfBlocks];
+    u32x2 win;
+    {
+        const Item it = load_item(a, begin);
+        if (it.staged) load_codes(it, lane, cw);
+#pragma unroll
+        for (int b = 0; b < kHalfBlocks; ++b) rw[b] = load_raw(it, lane, b);
+        win = load_windows(it, lane);
+    }
 
     for (uint32_t item = begin; item < end; ++item) {
-        uint32_t tl, chunk;
-        if (a.work) {
-            const uint32_t w = a.work[item];
-            tl = w >> kItemChunkBits;
-            chunk = w & kItemChunkMask;
-        } else {
-            tl = 0;
-            chunk = item;
-        }
-        const TensorDesc &d = a.desc[a.tensor_base + tl];
-        const uint8_t *__restrict__ C = a.containers[tl];
-        uint16_t *__restrict__ out = a.outs[tl];
-        const uint64_t elem0 = (uint64_t)chunk * kChunk;
-        const uint32_t nc = (uint32_t)umin64(kChunk, d.n_elems - elem0);
+        // (items are re-read from the work list, not carried over: the
+        // scalar cache holds them)
+        const Item it = load_item(a, item);
+        const bool more = item + 1 < end;
+        const Item nx = load_item(a, more ? item + 1 : item);
+        const u32x2 win_nx = more ? load_windows(nx, lane) : win;
 
         // ---- decode tables of this tensor -> LDS
-        if (d.lut_index != cur_lut) {
+        const uint32_t lut = it.lut;
+        if (lut != cur_lut) {
             __syncthreads();
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + d.lut_index);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + lut);
             u32x4 *dst = reinterpret_cast<u32x4 *>(&L.lut);
             for (uint32_t i = lane; i < sizeof(LutRecord) / 16; i += 64) dst[i] = src[i];
-            cur_lut = d.lut_index;
+            cur_lut = lut;
         }
 
-        // ---- chunk index and this lane's two windows
-        const uint64_t *ci = reinterpret_cast<const uint64_t *>(C + d.off_ci) + 2 * (uint64_t)chunk;
-        const uint64_t b0 = ci[0];
-        const uint64_t b1 = umax64(ci[2], b0);
-        const uint32_t gaps = reinterpret_cast<const uint16_t *>(C + d.off_gap)[(uint64_t)chunk * 64 + lane];
-        const uint32_t cnts = reinterpret_cast<const uint32_t *>(C + d.off_cnt)[(uint64_t)chunk * 64 + lane];
-
-        // ---- stage the code bytes (16-byte aligned window) and prefetch raw
-        const uint8_t *stream = C + d.off_stream;
-        const uint64_t sbytes = d.stream_bytes;
-        const uint64_t s0 = umin64((b0 >> 3) & ~(uint64_t)15, sbytes - 16);
-        const uint64_t s_end = umax64(umin64((((b1 + 127) >> 3) + 15) & ~(uint64_t)15, sbytes), s0 + 16);
-        const bool staged = s_end <= s0 + kCodeCap;
-        // 32-bit offsets from here on: a staged window is < kCodeCap bytes
-        const uint32_t s_len = (uint32_t)umin64(s_end - s0, kCodeCap);
-
-        u32x4 cw[kCodeCap / 1024];
-        if (staged) {
-#pragma unroll
-            for (int k = 0; k < kCodeCap / 1024; ++k) {
-                // past the chunk's bytes the address repeats (a cache hit, no
-                // extra HBM traffic) so that the load count stays fixed
-                const uint32_t off = min(1024u * k + 16u * lane, s_len - 16u);
-                cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + s0 + off));
-            }
-        }
-        const uint8_t *raw = C + d.off_raw + elem0 + 8 * lane;
-        u32x2 rw[kHalfBlocks];
-        if (nc == (uint32_t)kChunk) {
-#pragma unroll
-            for (int b = 0; b < kHalfBlocks; ++b)
-                rw[b] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(raw + 512 * b));
-        } else {
-            // the tensor's last chunk: stay inside the raw bytes (padded to 16)
-            const uint8_t *raw0 = C + d.off_raw + elem0;
-            const uint32_t jmax = ((uint32_t)umin64(d.raw_bytes - elem0, 2 * kChunk) - 8u) & ~7u;
-#pragma unroll
-            for (int b = 0; b < kHalfBlocks; ++b)
-                rw[b] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x2 *>(raw0 + min(512u * b + 8u * lane, jmax)));
-        }
-
-        // ---- write the staged words (every tile byte of the chunk gets
-        //      written by the decode, so the tile needs no clearing)
+        // ---- the staged words to LDS (every tile byte of the chunk gets
+        //      written by the decode, so the tile needs no clearing), then the
+        //      next item's code bytes into the freed registers
         __syncthreads();
-        if (staged) {
+        if (it.staged) {
 #pragma unroll
             for (int k = 0; k < kCodeCap / 1024; ++k) {
                 u32x4 v = cw[k];
@@ -362,10 +417,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
                 reinterpret_cast<u32x4 *>(L.codes + 1)[64 * k + lane] = v;
             }
         }
+        if (more && nx.staged) load_codes(nx, lane, cw);
 
         // ---- windows 2*lane (a) and 2*lane+1 (b): starts and output positions
+        const uint64_t b0 = it.b0, b1 = it.b1, s0 = it.s0;
+        const uint32_t nc = it.nc;
         const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
-        uint32_t na = cnts & 0xFFFFu, nb = cnts >> 16;
+        uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
         const uint32_t incl = wave_inclusive_sum(na + nb);
         const uint32_t qa = incl - na - nb;
         const uint32_t qb = qa + na;
@@ -378,35 +436,36 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
             na = ca;
             nb = cb;
         }
-        const uint64_t sa = b0 + (2 * lane) * W + (na ? (gaps & 0xFFu) : 0u);
-        const uint64_t sb = b0 + (2 * lane + 1) * W + (nb ? (gaps >> 8) : 0u);
+        const uint64_t sa = b0 + (2 * lane) * W + (na ? (win.x & 0xFFu) : 0u);
+        const uint64_t sb = b0 + (2 * lane + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
         const uint32_t mn = wave_min(min(na, nb));
         uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
         __syncthreads();
 
-        uint64_t ea, eb;
         // Window starts relative to the bytes from s0, negated.  Peeks at
         // p <= pmax stay inside the source; the counted loop moves a window
         // by at most 24*T bits, so starts are kept at or below pmax - 24*T
         // (only a container that disagrees with its index starts higher).
+        const uint64_t sbytes = it.stream_bytes;
         const uint32_t n_words = (uint32_t)umin64((sbytes - s0) / 4, 1u << 25);
-        const uint32_t pmax = staged ? 32u * (kCodeWords - 1) : 32u * (n_words - 1);
+        const uint32_t pmax = it.staged ? 32u * (kCodeWords - 1) : 32u * (n_words - 1);
         T = min(T, pmax / 48u);
         const uint64_t plim = pmax - 24u * T;
-        uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wraps high when below s0
+        const uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wrap high when below s0
         bad |= (pra > plim) | (prb > plim);
         uint32_t pa = 0u - (uint32_t)umin64(pra, plim), pb = 0u - (uint32_t)umin64(prb, plim);
-        if (staged) {
+        if (it.staged) {
             // peeks read codes[j], codes[j+1] with j <= kCodeWords
             const LdsCodes src{L.codes, 0u - pmax};
             decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
         } else {
             // peeks read words j-1 and j of the stream from s0, j < n_words
-            const GlobalCodes src{reinterpret_cast<const uint32_t *>(stream + s0) - 1, 0u - pmax};
+            const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream + s0) - 1,
+                                  0u - pmax};
             decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
         }
-        ea = 8 * s0 + (uint32_t)(0u - pa);
-        eb = 8 * s0 + (uint32_t)(0u - pb);
+        const uint64_t ea = 8 * s0 + (uint32_t)(0u - pa);
+        const uint64_t eb = 8 * s0 + (uint32_t)(0u - pb);
 
         // ---- every non-empty window ends where the next non-empty window's
         //      first code starts; the last one at the chunk end
@@ -421,23 +480,37 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         bad_any |= bad;
         __syncthreads();
 
-        // ---- assemble and store
-        uint16_t *o = out + elem0;
+        // ---- assemble and store the whole 512-element blocks; each block's
+        //      raw registers take the next item's bytes right after use
+        uint16_t *o = it.out;
+        const uint32_t full = nc / 512;
 #pragma unroll
         for (int b = 0; b < kHalfBlocks; ++b) {
-            const uint32_t j = 512 * b + 8 * lane;
-            if (512u * b >= nc) break;
-            const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
-            const u32x4 v = join8(t8, rw[b]);
-            if (j + 8 <= nc) {
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(o + j));
-            } else if (j < nc) {
-                for (uint32_t k = 0; j + k < nc; ++k) {
-                    const uint32_t wd = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
-                    o[j + k] = (uint16_t)(wd >> (16 * (k & 1)));
+            if ((uint32_t)b < full) {
+                const uint32_t j = 512 * b + 8 * lane;
+                const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
+                __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
+            }
+            if (more) rw[b] = load_raw(nx, lane, b);
+        }
+        // ---- the ragged last block of a tensor (raw bytes fetched again)
+        if (full * 512 < nc) {
+            const uint32_t j = full * 512 + 8 * lane;
+            if (j < nc) {
+                const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
+                const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
+                const u32x4 v = join8(t8, r8);
+                if (j + 8 <= nc) {
+                    *reinterpret_cast<u32x4 *>(o + j) = v;
+                } else {
+                    for (uint32_t k = 0; j + k < nc; ++k) {
+                        const uint32_t wd = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;
+                        o[j + k] = (uint16_t)(wd >> (16 * (k & 1)));
+                    }
                 }
             }
         }
+        win = win_nx;
     }
     if (__ballot(bad_any) && lane == 0) atomicOr(a.status, 1u);
 }
