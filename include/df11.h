@@ -11,22 +11,22 @@
  * bit.  The weights stay compressed in GPU memory and are decoded on the GPU
  * when they are needed (mlx-dfloat project page, introduction).
  *
- * Container version 1 (one tensor = one container = one code table; all
+ * Container version 2 (one tensor = one container = one code table; all
  * integers little-endian; every section starts on a 256-byte boundary):
  *
  *   header (512 bytes)
- *      0 char[8] magic "DF11HIPC"    8 u32 version = 1      12 u32 flags = 0
+ *      0 char[8] magic "DF11HIPC"    8 u32 version = 2      12 u32 flags = 0
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
- *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 windows = 128
- *     98 u16 0                     100 u32 n_chunks       104 u64 total_bits
- *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_cnt
+ *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 0
+ *     98 u16 windows = 512         100 u32 n_chunks       104 u64 total_bits
+ *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_first
  *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
  *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
  *    208 u8 code_len[256]          464 u8[48] 0
  *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
  *                entry is { total_bits, n_elems }
- *   window gap   n_chunks x 128 x u8
- *   window cnt   n_chunks x 128 x u16
+ *   window gap   n_chunks x 512 x u8
+ *   window first n_chunks x 512 x u16
  *   stream       the exponent codes, concatenated, most significant bit first
  *                (bit 7 of byte 0 is the first bit); ceil(total_bits/8) bytes
  *                rounded up to 16, plus 16 zero bytes
@@ -40,13 +40,14 @@
  *
  * Chunks: element j of the tensor is in chunk j / 32768.  Chunk c owns the
  * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]).  Its bits are cut in
- * 128 windows of W = ceil((b1 - b0) / 128) bits: window i is
- * [b0 + i*W, min(b0 + (i+1)*W, b1)).  cnt[c][i] counts the codes that START in
- * window i; gap[c][i] is the offset of the first of them from the window
- * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
- * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
- * the windows.  The decoder gives one wavefront to a chunk and two
- * neighbouring windows to each of its 64 lanes.
+ * 512 windows of W = ceil((b1 - b0) / 512) bits: window i is
+ * [b0 + i*W, min(b0 + (i+1)*W, b1)).  first[c][i] counts the chunk's codes
+ * that start before bit b0 + i*W, so the codes that START in window i are
+ * elements out_elem[c] + first[c][i] .. out_elem[c] + first[c][i+1] - 1
+ * (first[c][512] standing for the chunk's element count); gap[c][i] is the
+ * offset of the first of them from the window start (always < 24), or 0xFF
+ * when the window holds no code start.  The decoder gives one 256-lane
+ * workgroup to a chunk and two neighbouring windows to each lane.
  */
 #ifndef DF11_H
 #define DF11_H
@@ -62,7 +63,7 @@ extern "C" {
 #define DF11_ABI_VERSION 1
 #define DF11_HEADER_BYTES 512
 #define DF11_CHUNK_ELEMS 32768
-#define DF11_WINDOWS 128
+#define DF11_WINDOWS 512
 #define DF11_MAX_CODE_LEN 24
 /* Tensors decoded by one kernel launch; larger batches are split. */
 #define DF11_MAX_BATCH 64
@@ -99,8 +100,9 @@ typedef struct {
  * the stream padding is checked too.  Checks: magic, version, chunk size,
  * window count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
  * symbol), section offsets and sizes, start bits monotone with out_elem =
- * 32768*c, per chunk: sum of cnt = chunk size, gap < 24 when cnt > 0, gap =
- * 0xFF when cnt = 0, and a window's codes fit its share of the stream.
+ * 32768*c, per chunk: first[0] = 0, first non-decreasing and at most the
+ * chunk size, gap < 24 for a window that holds code starts and 0xFF for one
+ * that holds none, and a window's codes fit its share of the stream.
  * `info` may be NULL.  Reads only; allocates nothing on the device.
  * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
 df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info);
@@ -108,7 +110,7 @@ df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info 
 /* Size bound of the container for n elements (any data). */
 uint64_t df11_container_bound(uint64_t n_elems);
 
-/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-1
+/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-2
  * container in HOST memory `out` (capacity `out_cap`, at least
  * df11_container_bound(n)).  dims[ndim] is the shape (ndim <= 8, product =
  * n; ndim = 0 means a scalar, n = 1).  `threads` = 0 uses every hardware

@@ -5,33 +5,33 @@
 // and its exponent byte, which is stored as a variable-length prefix code in
 // one bitstream; output words are bit-identical to the originals.
 //
-// One workgroup = one wave64.  A wave decodes whole chunks of 32768 elements
-// (64 KiB of BF16 output), one after the other, over a contiguous range of
-// the launch's work items (tensor, chunk).  Per chunk:
+// One workgroup = four wave64s (256 lanes) decodes whole chunks of 32768
+// elements (64 KiB of BF16 output), one after the other, over a contiguous
+// range of the launch's work items (tensor, chunk).  Per chunk:
 //
 //   1. stage: coalesced 16-byte loads of the chunk's code bytes, byte-swapped
-//      into big-endian 32-bit words in LDS; the chunk's raw bytes go to
-//      registers in the same burst (8 bytes per lane per 512 elements) and
-//      are not needed before step 5, so their latency hides behind decoding;
-//   2. index: the chunk's bits form 128 equal windows; lane i takes windows
-//      2i and 2i+1.  A DPP prefix sum over the 64 lane totals of the window
-//      code counts gives each window the chunk position of its first code;
+//      into big-endian 32-bit words in LDS; the chunk's raw bytes wait in
+//      registers (8 bytes per lane per 2048 elements) until step 5.  Both are
+//      requested while the previous chunk decodes;
+//   2. index: the chunk's bits form 512 equal windows; lane i takes windows
+//      2i and 2i+1.  The index gives each window the offset of its first
+//      code and the chunk position of its first output word;
 //   3. decode: each lane walks its two windows side by side (two independent
-//      dependency chains).  A look-up peeks 32 bits with one ds_read2_b32 and
-//      a 64-bit shift, then one LDS first-level table entry resolves up to
-//      three codes of <= 10 bits; codes of 11..16 bits use a second-level
-//      table, longer ones the canonical limits.  Exponent bytes (rotated, see
-//      rot_exp) are OR-ed into a zeroed 32 KiB LDS tile at their chunk
-//      positions.  A counted loop with no per-lane control flow runs while no
-//      window can run out (each look-up takes at most three codes); an exact
-//      per-window loop finishes the windows;
+//      dependency chains; 512 chains per workgroup).  A look-up peeks 32 bits
+//      with one ds_read2_b32 and a funnel shift, then one LDS first-level
+//      table entry resolves up to three codes of <= 10 bits; codes of 11..16
+//      bits use a second-level table, longer ones the canonical limits.
+//      Exponent bytes (rotated, see rot_exp) go to a 32 KiB LDS tile at their
+//      chunk positions.  A counted loop with no per-lane control flow runs
+//      while no window of the wave can run out (each look-up takes at most
+//      three codes); a masked loop and an exact per-window loop finish;
 //   4. check: a window must end exactly where the next non-empty window's
 //      first code starts (or at the chunk end); otherwise the plan's flag is
 //      set;
-//   5. assemble: per 1024 elements, each lane joins 2 x 8 tile bytes with 2 x 8
-//      raw bytes into BF16 words (two byte permutes and one bitfield insert
-//      per two words) and writes them with 16-byte stores that are contiguous
-//      across the wave (1 KiB per store instruction).
+//   5. assemble: per 2048 elements, each lane joins 8 tile bytes with 8 raw
+//      bytes into BF16 words (two byte permutes and one bitfield insert per
+//      two words) and writes them with one 16-byte store, contiguous across
+//      the wave (1 KiB per store instruction).
 //
 // There is no matrix arithmetic here: the path is bound by HBM traffic
 // (about 1.33 bytes read and 2 bytes written per element), with integer
@@ -42,13 +42,18 @@
 
 namespace df11 {
 
+constexpr int kThreads = 256;                      // lanes per workgroup
+constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = kChunk;                 // one exponent byte per element
-// LDS per wave: 14 KiB staged codes + 32 KiB tile + 5.8 KiB tables = 51.8 KiB,
-// so that three waves fit in a compute unit's 160 KiB (the allocation is
-// rounded up, and 52.8 KiB would leave room for only two).
+// LDS per workgroup: 14 KiB staged codes + 32 KiB tile + 5.8 KiB tables =
+// 51.8 KiB, so that three workgroups fit in a compute unit's 160 KiB (the
+// allocation is rounded up, and 52.8 KiB would leave room for only two).
 constexpr int kCodeCap = 14 * 1024;                // staged code bytes per chunk
 constexpr int kCodeWords = kCodeCap / 4;
-constexpr int kHalfBlocks = kChunk / 512;          // 512-element store blocks
+constexpr int kCodeLoads = (kCodeCap + 16 * kThreads - 1) / (16 * kThreads);
+constexpr int kBlockElems = 8 * kThreads;          // elements per store block
+constexpr int kBlocks = kChunk / kBlockElems;
+static_assert(2 * kThreads == kWindows, "two windows per lane");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -62,9 +67,12 @@ struct Lds {
     uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
     uint8_t tile[kTileBytes + 16];
     LutRecord lut;
+    // per wave: bit offset from the chunk start of the first code of its
+    // first non-empty window (~0: all its windows are empty)
+    uint32_t wave_first[kWaves];
 };
 static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0, "LDS alignment");
-static_assert(sizeof(Lds) <= 53248, "three waves per compute unit");
+static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
 constexpr uint32_t kDummy = kTileBytes + 8;   // tile bytes nobody reads
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
@@ -72,18 +80,6 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
     return __builtin_amdgcn_perm(0u, x, 0x00010203u);
-}
-
-// Inclusive prefix sum over the 64 lanes of the wave, with DPP row shifts
-// inside each row of 16 lanes and row broadcasts between rows.
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-    return x;
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
@@ -284,16 +280,16 @@ __device__ __forceinline__ T const_load(const T *p) {
 
 // One work item (a chunk of a tensor) and where its bytes are.
 struct Item {
-    const uint8_t *stream;   // the container's sections
-    const uint8_t *raw;      //   (raw: from the chunk's first element)
-    const uint8_t *gap;
-    const uint8_t *cnt;
-    uint16_t *out;           // from the chunk's first element
+    const uint8_t *stream;   // the container's stream section
+    const uint8_t *raw;      // raw bytes from the chunk's first element
+    const uint8_t *gap;      // the chunk's window gaps
+    const uint8_t *first;    // the chunk's window first-code positions
+    uint16_t *out;           // output from the chunk's first element
     uint64_t b0, b1;         // the chunk's stream bits
     uint64_t s0;             // first staged stream byte (16-byte aligned)
     uint64_t stream_bytes;
     uint32_t raw_left;       // raw bytes from the chunk's first element (<= 64 KiB)
-    uint32_t chunk, nc;      // chunk index, elements
+    uint32_t nc;             // elements
     uint32_t s_len;          // staged bytes
     uint32_t staged;         // the chunk's codes fit the LDS area
     uint32_t lut;
@@ -315,10 +311,9 @@ __device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
     const uint64_t elem0 = (uint64_t)chunk * kChunk;
     it.stream = C + const_load(&d->off_stream);
     it.raw = C + const_load(&d->off_raw) + elem0;
-    it.gap = C + const_load(&d->off_gap);
-    it.cnt = C + const_load(&d->off_cnt);
+    it.gap = C + const_load(&d->off_gap) + (uint64_t)chunk * kWindows;
+    it.first = C + const_load(&d->off_first) + (uint64_t)chunk * kWindows * 2;
     it.out = a.outs[tl] + elem0;
-    it.chunk = chunk;
     it.nc = (uint32_t)umin64(kChunk, const_load(&d->n_elems) - elem0);
     it.raw_left = (uint32_t)umin64(const_load(&d->raw_bytes) - elem0, 2 * kChunk);
     it.lut = const_load(&d->lut_index);
@@ -334,54 +329,64 @@ __device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
     return it;
 }
 
-// The staged code bytes of an item: 16 bytes per lane per 1 KiB.  Past the
+// The staged code bytes of an item: 16 bytes per lane per 4 KiB.  Past the
 // chunk's bytes the address repeats (a cache hit, no extra HBM traffic) so
 // that the load count stays fixed.
-__device__ __forceinline__ void load_codes(const Item &it, uint32_t lane, u32x4 (&cw)[kCodeCap / 1024]) {
+__device__ __forceinline__ void load_codes(const Item &it, uint32_t tid, u32x4 (&cw)[kCodeLoads]) {
     const uint8_t *stream = it.stream + it.s0;
 #pragma unroll
-    for (int k = 0; k < kCodeCap / 1024; ++k) {
-        const uint32_t off = min(1024u * k + 16u * lane, it.s_len - 16u);
+    for (int k = 0; k < kCodeLoads; ++k) {
+        const uint32_t off = min(16u * kThreads * k + 16u * tid, it.s_len - 16u);
         cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + off));
     }
 }
 
-// Raw bytes of store block b (elements 512b + 8 lane .. +8) of an item; a
+// Raw bytes of store block b (elements 2048b + 8 tid .. +8) of an item; a
 // partial chunk reads inside its (16-byte padded) raw bytes only.
-__device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t lane, int b) {
-    uint32_t j = 512u * b + 8u * lane;
+__device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t tid, int b) {
+    uint32_t j = kBlockElems * b + 8u * tid;
     if (it.nc != (uint32_t)kChunk) j = min(j, (it.raw_left - 8u) & ~7u);
     return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(it.raw + j));
 }
 
-// Both windows' (gap, cnt) of this lane: gaps in the low 16 bits of x, the
-// two counts in y.
-__device__ __forceinline__ u32x2 load_windows(const Item &it, uint32_t lane) {
-    const uint64_t w = (uint64_t)it.chunk * 64 + lane;
-    return u32x2{reinterpret_cast<const uint16_t *>(it.gap)[w], reinterpret_cast<const uint32_t *>(it.cnt)[w]};
+// The index entries of this lane's windows 2 tid and 2 tid + 1: x = both
+// gaps (low byte: window 2 tid), y = both first-code positions (low half:
+// window 2 tid), z = the first-code position of window 2 tid + 2 (the
+// chunk's element count after the last window).
+struct Windows {
+    uint32_t x, y, z;
+};
+__device__ __forceinline__ Windows load_windows(const Item &it, uint32_t tid) {
+    Windows v;
+    v.x = reinterpret_cast<const uint16_t *>(it.gap)[tid];
+    v.y = reinterpret_cast<const uint32_t *>(it.first)[tid];
+    v.z = tid + 1 < (uint32_t)kThreads ? (uint32_t)reinterpret_cast<const uint16_t *>(it.first)[2 * tid + 2]
+                                       : it.nc;
+    return v;
 }
 
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     __shared__ Lds L;
-    const uint32_t lane = threadIdx.x;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u, wave = tid >> 6;
     const uint32_t begin = (uint32_t)((uint64_t)a.n_items * blockIdx.x / gridDim.x);
     const uint32_t end = (uint32_t)((uint64_t)a.n_items * (blockIdx.x + 1) / gridDim.x);
     uint32_t cur_lut = 0xFFFFFFFFu;
     uint32_t bad_any = 0;
     if (begin >= end) return;
 
-    // Software pipeline over the wave's items: while item i decodes, the
-    // code bytes of item i+1 are in flight, and its raw bytes are requested
-    // block by block as item i's assembly frees the registers.
-    u32x4 cw[kCodeCap / 1024];
-    u32x2 rw[kHalfBlocks];
-    u32x2 win;
+    // Software pipeline over the workgroup's items: while item i decodes,
+    // the code bytes of item i+1 are in flight, and its raw bytes are
+    // requested block by block as item i's assembly frees the registers.
+    u32x4 cw[kCodeLoads];
+    u32x2 rw[kBlocks];
+    Windows win;
     {
         const Item it = load_item(a, begin);
-        if (it.staged) load_codes(it, lane, cw);
+        if (it.staged) load_codes(it, tid, cw);
 #pragma unroll
-        for (int b = 0; b < kHalfBlocks; ++b) rw[b] = load_raw(it, lane, b);
-        win = load_windows(it, lane);
+        for (int b = 0; b < kBlocks; ++b) rw[b] = load_raw(it, tid, b);
+        win = load_windows(it, tid);
     }
 
     for (uint32_t item = begin; item < end; ++item) {
@@ -390,56 +395,59 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         const Item it = load_item(a, item);
         const bool more = item + 1 < end;
         const Item nx = load_item(a, more ? item + 1 : item);
-        const u32x2 win_nx = more ? load_windows(nx, lane) : win;
+        const Windows win_nx = more ? load_windows(nx, tid) : win;
+
+        // ---- the previous item's tile and staged words are no longer read
+        __syncthreads();
 
         // ---- decode tables of this tensor -> LDS
         const uint32_t lut = it.lut;
         if (lut != cur_lut) {
-            __syncthreads();
             const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + lut);
             u32x4 *dst = reinterpret_cast<u32x4 *>(&L.lut);
-            for (uint32_t i = lane; i < sizeof(LutRecord) / 16; i += 64) dst[i] = src[i];
+            for (uint32_t i = tid; i < sizeof(LutRecord) / 16; i += kThreads) dst[i] = src[i];
             cur_lut = lut;
         }
 
         // ---- the staged words to LDS (every tile byte of the chunk gets
         //      written by the decode, so the tile needs no clearing), then the
         //      next item's code bytes into the freed registers
-        __syncthreads();
         if (it.staged) {
 #pragma unroll
-            for (int k = 0; k < kCodeCap / 1024; ++k) {
-                u32x4 v = cw[k];
-                v.x = bswap32(v.x);
-                v.y = bswap32(v.y);
-                v.z = bswap32(v.z);
-                v.w = bswap32(v.w);
-                reinterpret_cast<u32x4 *>(L.codes + 1)[64 * k + lane] = v;
+            for (int k = 0; k < kCodeLoads; ++k) {
+                if (16u * kThreads * k + 16u * tid < (uint32_t)kCodeCap) {
+                    u32x4 v = cw[k];
+                    v.x = bswap32(v.x);
+                    v.y = bswap32(v.y);
+                    v.z = bswap32(v.z);
+                    v.w = bswap32(v.w);
+                    reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * k + tid] = v;
+                }
             }
         }
-        if (more && nx.staged) load_codes(nx, lane, cw);
+        if (more && nx.staged) load_codes(nx, tid, cw);
 
-        // ---- windows 2*lane (a) and 2*lane+1 (b): starts and output positions
+        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions;
+        //      never write past the chunk, whatever the device bytes say
         const uint64_t b0 = it.b0, b1 = it.b1, s0 = it.s0;
         const uint32_t nc = it.nc;
         const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
-        uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
-        const uint32_t incl = wave_inclusive_sum(na + nb);
-        const uint32_t qa = incl - na - nb;
-        const uint32_t qb = qa + na;
-        // never write past the chunk, whatever the device bytes say
         uint32_t bad = 0;
-        {
-            const uint32_t ca = qa < nc ? min(na, nc - qa) : 0u;
-            const uint32_t cb = qb < nc ? min(nb, nc - qb) : 0u;
-            bad |= (ca != na) | (cb != nb);
-            na = ca;
-            nb = cb;
-        }
-        const uint64_t sa = b0 + (2 * lane) * W + (na ? (win.x & 0xFFu) : 0u);
-        const uint64_t sb = b0 + (2 * lane + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
+        const uint32_t qa = min(win.y & 0xFFFFu, nc);
+        const uint32_t qb = min(max(win.y >> 16, qa), nc);
+        const uint32_t qe = min(max(win.z, qb), nc);
+        bad |= (qa != (win.y & 0xFFFFu)) | (qb != (win.y >> 16)) | (qe != win.z);
+        const uint32_t na = qb - qa, nb = qe - qb;
+        const uint64_t sa = b0 + (2 * tid) * W + (na ? (win.x & 0xFFu) : 0u);
+        const uint64_t sb = b0 + (2 * tid + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
         const uint32_t mn = wave_min(min(na, nb));
         uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
+
+        // the wave's first code (for the end check of the wave below)
+        const uint64_t mask = __ballot(na + nb != 0);
+        const uint64_t first = na ? sa : sb;          // this lane's first code
+        const uint64_t wf = __shfl((unsigned long long)first, mask ? (int)__builtin_ctzll(mask) : 0);
+        if (lane == 0) L.wave_first[wave] = mask ? (uint32_t)(wf - b0) : 0xFFFFFFFFu;
         __syncthreads();
 
         // Window starts relative to the bytes from s0, negated.  Peeks at
@@ -466,36 +474,47 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         }
         const uint64_t ea = 8 * s0 + (uint32_t)(0u - pa);
         const uint64_t eb = 8 * s0 + (uint32_t)(0u - pb);
+        __syncthreads();
 
         // ---- every non-empty window ends where the next non-empty window's
         //      first code starts; the last one at the chunk end
-        const uint64_t mask = __ballot(na + nb != 0);
-        const uint64_t first = na ? sa : sb;          // this lane's first code
-        const uint64_t above = lane == 63 ? 0 : (mask >> (lane + 1));
-        const uint32_t nxt_lane = above ? lane + 1 + (uint32_t)__builtin_ctzll(above) : lane;
-        const uint64_t nxt_first = __shfl((unsigned long long)first, (int)nxt_lane);
-        const uint64_t after_b = above ? nxt_first : b1;
-        if (nb) bad |= eb != after_b;
-        if (na) bad |= ea != (nb ? sb : after_b);
-        bad_any |= bad;
-        __syncthreads();
+        {
+            const uint64_t above = lane == 63 ? 0 : (mask >> (lane + 1));
+            const uint32_t nxt_lane = above ? lane + 1 + (uint32_t)__builtin_ctzll(above) : lane;
+            const uint64_t nxt_first = __shfl((unsigned long long)first, (int)nxt_lane);
+            uint64_t after_b = b1;
+            if (above) {
+                after_b = nxt_first;
+            } else {
+                for (uint32_t w = wave + 1; w < (uint32_t)kWaves; ++w) {
+                    const uint32_t f = L.wave_first[w];
+                    if (f != 0xFFFFFFFFu) {
+                        after_b = b0 + f;
+                        break;
+                    }
+                }
+            }
+            if (nb) bad |= eb != after_b;
+            if (na) bad |= ea != (nb ? sb : after_b);
+            bad_any |= bad;
+        }
 
-        // ---- assemble and store the whole 512-element blocks; each block's
+        // ---- assemble and store the whole 2048-element blocks; each block's
         //      raw registers take the next item's bytes right after use
         uint16_t *o = it.out;
-        const uint32_t full = nc / 512;
+        const uint32_t full = nc / kBlockElems;
 #pragma unroll
-        for (int b = 0; b < kHalfBlocks; ++b) {
+        for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
-                const uint32_t j = 512 * b + 8 * lane;
+                const uint32_t j = kBlockElems * b + 8 * tid;
                 const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
                 __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
             }
-            if (more) rw[b] = load_raw(nx, lane, b);
+            if (more) rw[b] = load_raw(nx, tid, b);
         }
         // ---- the ragged last block of a tensor (raw bytes fetched again)
-        if (full * 512 < nc) {
-            const uint32_t j = full * 512 + 8 * lane;
+        if (full * kBlockElems < nc) {
+            const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
                 const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
                 const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
@@ -516,7 +535,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs &args, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(64), 0, stream, args);
+    hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(kThreads), 0, stream, args);
     return hipGetLastError();
 }
 
@@ -524,7 +543,7 @@ int decode_wgs_per_cu() {
     static int cached = 0;
     if (!cached) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel, 64, 0) != hipSuccess || n <= 0) n = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel, kThreads, 0) != hipSuccess || n <= 0) n = 1;
         cached = n;
     }
     return cached;

@@ -6,8 +6,8 @@
 
 namespace df11 {
 
-// Container version 1 constants (layout documented in include/df11.h).
-constexpr uint32_t kVersion = 1;
+// Container version 2 constants (layout documented in include/df11.h).
+constexpr uint32_t kVersion = 2;
 constexpr uint32_t kHeader = DF11_HEADER_BYTES;
 constexpr uint32_t kChunk = DF11_CHUNK_ELEMS;
 constexpr int kWindows = DF11_WINDOWS;
@@ -68,7 +68,7 @@ struct alignas(16) TensorDesc {
     uint64_t n_elems;
     uint64_t off_ci;
     uint64_t off_gap;
-    uint64_t off_cnt;
+    uint64_t off_first;
     uint64_t off_stream;
     uint64_t stream_bytes;
     uint64_t off_raw;

@@ -11,7 +11,7 @@
  * fraction, which is kept as one raw byte.  Decoding must give back every
  * word bit for bit (same page, introduction and "Status", milestone 1).
  *
- * The container layout written here is this project's own (version 1); its
+ * The container layout written here is this project's own (version 2); its
  * fields are documented next to the writer in df11_oracle.c.
  */
 #ifndef DF11_ORACLE_H
@@ -42,7 +42,7 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code);
 /* Upper bound on the container size for n words. */
 uint64_t oracle_container_bound(uint64_t n);
 
-/* Encode n BF16 words (as uint16) into a version-1 container.
+/* Encode n BF16 words (as uint16) into a version-2 container.
  * dims[ndim] is the tensor shape (ndim <= 8, product must equal n).
  * Returns ORACLE_OK and the container size in *out_bytes. */
 int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims,
@@ -55,8 +55,9 @@ int oracle_decode(const uint8_t *c, uint64_t bytes, uint16_t *out, uint64_t n);
 /* Decode one chunk, starting from its start_bit alone (chunk index only). */
 int oracle_decode_chunk(const uint8_t *c, uint64_t bytes, uint64_t chunk, uint16_t *out);
 
-/* Decode the codes of one window of a chunk from its gap/cnt entry.
- * Writes the cnt decoded words to out and the end bit position to *end_bit. */
+/* Decode the codes of one window of a chunk from its (gap, first) entries.
+ * Writes the window's decoded words to out, their number to *n_out and the
+ * end bit position to *end_bit. */
 int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int win,
                        uint16_t *out, uint64_t *n_out, uint64_t *end_bit);
 

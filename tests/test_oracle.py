@@ -259,11 +259,12 @@ def test_chunk_and_window_index_reproduce_the_source(n):
         lo, hi = ch * 32768, min(n, (ch + 1) * 32768)
         # a chunk decodes from its start bit alone (df11pack, sampled chunks)
         assert (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all()
-        # the 128 windows decode exactly their cnt codes, back to back
+        # the windows decode exactly their codes, back to back
+        NW = oracle.WINDOWS
         parts, ends = [], []
         b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
-        Wb = (b1 - b0 + 127) // 128
-        for win in range(128):
+        Wb = (b1 - b0 + NW - 1) // NW
+        for win in range(NW):
             words, end = oracle.decode_window(c, ch, win)
             parts.append(words)
             if len(words):
@@ -273,8 +274,21 @@ def test_chunk_and_window_index_reproduce_the_source(n):
                 assert end - min(b1, b0 + (win + 1) * Wb) < 24
         assert (np.concatenate(parts) == w[lo:hi]).all()
         assert ends[-1][1] == b1
-        gap = c[h["off_win_gap"] + 128 * ch:h["off_win_gap"] + 128 * ch + 128]
+        gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
         assert ((gap < 24) | (gap == 0xFF)).all()
+        # the index from first principles: every code's start bit from the
+        # source's exponents and the header's code lengths; a window's gap is
+        # its first start's offset, its "first" the starts before it
+        ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
+        starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
+        edges = b0 + Wb * np.arange(NW)
+        want_first = np.searchsorted(starts, edges, side="left")
+        first = c[h["off_win_first"] + 2 * NW * ch:h["off_win_first"] + 2 * NW * (ch + 1)].view(np.uint16)
+        assert (first == want_first).all()
+        has = (np.append(want_first[1:], hi - lo) > want_first) & (edges < b1)
+        idx = np.minimum(want_first, hi - lo - 1)
+        want_gap = np.where(has, starts[idx] - edges, 0xFF)
+        assert (gap == want_gap).all()
 
 
 def test_degenerate_tensors():
@@ -321,7 +335,7 @@ def test_corruption_is_detected():
     bad[h["off_win_gap"] + 5] ^= 1                   # a window gap
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_win_cnt"] + 10] ^= 1                  # a window count
+    bad[h["off_win_first"] + 10] ^= 1                # a window's first code
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
     bad[208 + 121] += 1                              # a code length: Kraft breaks

@@ -40,6 +40,9 @@ MUTATIONS = [
     ("window gap off by one",
      "gap[win] = (uint8_t)(p - (b0 + win * W));",
      "gap[win] = (uint8_t)(p - (b0 + win * W) + 1);", 0),
+    ("window first counts its own codes",
+     "put_u16(firstp + 2 * i, (uint16_t)before);",
+     "put_u16(firstp + 2 * i, (uint16_t)(before + cnt[i]));", 0),
     ("window width rounds down",
      "uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;",
      "uint64_t W = (b1 - b0) / WINDOWS + 1;", 0),
@@ -100,7 +103,7 @@ def _pins_pass() -> bool:
             lo, hi = ch * 32768, min(w.size, (ch + 1) * 32768)
             if not (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all():
                 return False
-            parts = [oracle.decode_window(c, ch, win)[0] for win in range(128)]
+            parts = [oracle.decode_window(c, ch, win)[0] for win in range(oracle.WINDOWS)]
             if not (np.concatenate(parts) == w[lo:hi]).all():
                 return False
         return True
