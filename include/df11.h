@@ -19,14 +19,14 @@
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
  *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 0
  *     98 u16 windows = 512         100 u32 n_chunks       104 u64 total_bits
- *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_first
+ *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_cnt
  *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
  *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
  *    208 u8 code_len[256]          464 u8[48] 0
  *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
  *                entry is { total_bits, n_elems }
  *   window gap   n_chunks x 512 x u8
- *   window first n_chunks x 512 x u16
+ *   window cnt   n_chunks x 512 x u16
  *   stream       the exponent codes, concatenated, most significant bit first
  *                (bit 7 of byte 0 is the first bit); ceil(total_bits/8) bytes
  *                rounded up to 16, plus 16 zero bytes
@@ -41,13 +41,13 @@
  * Chunks: element j of the tensor is in chunk j / 32768.  Chunk c owns the
  * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]).  Its bits are cut in
  * 512 windows of W = ceil((b1 - b0) / 512) bits: window i is
- * [b0 + i*W, min(b0 + (i+1)*W, b1)).  first[c][i] counts the chunk's codes
- * that start before bit b0 + i*W, so the codes that START in window i are
- * elements out_elem[c] + first[c][i] .. out_elem[c] + first[c][i+1] - 1
- * (first[c][512] standing for the chunk's element count); gap[c][i] is the
- * offset of the first of them from the window start (always < 24), or 0xFF
- * when the window holds no code start.  The decoder gives one 256-lane
- * workgroup to a chunk and two neighbouring windows to each lane.
+ * [b0 + i*W, min(b0 + (i+1)*W, b1)).  cnt[c][i] counts the codes that START in
+ * window i; gap[c][i] is the offset of the first of them from the window
+ * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
+ * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
+ * the windows.  The decoder gives one 256-lane workgroup to a chunk and two
+ * neighbouring windows to each lane, and forms the prefix sum with one
+ * wavefront scan per wave plus the totals of the waves below.
  */
 #ifndef DF11_H
 #define DF11_H
@@ -100,9 +100,8 @@ typedef struct {
  * the stream padding is checked too.  Checks: magic, version, chunk size,
  * window count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
  * symbol), section offsets and sizes, start bits monotone with out_elem =
- * 32768*c, per chunk: first[0] = 0, first non-decreasing and at most the
- * chunk size, gap < 24 for a window that holds code starts and 0xFF for one
- * that holds none, and a window's codes fit its share of the stream.
+ * 32768*c, per chunk: sum of cnt = chunk size, gap < 24 when cnt > 0, gap =
+ * 0xFF when cnt = 0, and a window's codes fit its share of the stream.
  * `info` may be NULL.  Reads only; allocates nothing on the device.
  * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
 df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info);

@@ -14,8 +14,9 @@
 //      registers (8 bytes per lane per 2048 elements) until step 5.  Both are
 //      requested while the previous chunk decodes;
 //   2. index: the chunk's bits form 512 equal windows; lane i takes windows
-//      2i and 2i+1.  The index gives each window the offset of its first
-//      code and the chunk position of its first output word;
+//      2i and 2i+1.  A DPP prefix sum over each wave's lane totals of the
+//      window code counts, plus the totals of the waves below (through LDS),
+//      gives each window the chunk position of its first code;
 //   3. decode: each lane walks its two windows side by side (two independent
 //      dependency chains; 512 chains per workgroup).  A look-up peeks 32 bits
 //      with one ds_read2_b32 and a funnel shift, then one LDS first-level
@@ -68,8 +69,10 @@ struct Lds {
     uint8_t tile[kTileBytes + 16];
     LutRecord lut;
     // per wave: bit offset from the chunk start of the first code of its
-    // first non-empty window (~0: all its windows are empty)
+    // first non-empty window (~0: all its windows are empty), and the number
+    // of codes its windows hold
     uint32_t wave_first[kWaves];
+    uint32_t wave_total[kWaves];
 };
 static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0, "LDS alignment");
 static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
@@ -80,6 +83,18 @@ __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > 
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
     return __builtin_amdgcn_perm(0u, x, 0x00010203u);
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave, with DPP row shifts
+// inside each row of 16 lanes and row broadcasts between rows.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
 }
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
@@ -283,7 +298,7 @@ struct Item {
     const uint8_t *stream;   // the container's stream section
     const uint8_t *raw;      // raw bytes from the chunk's first element
     const uint8_t *gap;      // the chunk's window gaps
-    const uint8_t *first;    // the chunk's window first-code positions
+    const uint8_t *cnt;      // the chunk's window code counts
     uint16_t *out;           // output from the chunk's first element
     uint64_t b0, b1;         // the chunk's stream bits
     uint64_t s0;             // first staged stream byte (16-byte aligned)
@@ -312,7 +327,7 @@ __device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
     it.stream = C + const_load(&d->off_stream);
     it.raw = C + const_load(&d->off_raw) + elem0;
     it.gap = C + const_load(&d->off_gap) + (uint64_t)chunk * kWindows;
-    it.first = C + const_load(&d->off_first) + (uint64_t)chunk * kWindows * 2;
+    it.cnt = C + const_load(&d->off_cnt) + (uint64_t)chunk * kWindows * 2;
     it.out = a.outs[tl] + elem0;
     it.nc = (uint32_t)umin64(kChunk, const_load(&d->n_elems) - elem0);
     it.raw_left = (uint32_t)umin64(const_load(&d->raw_bytes) - elem0, 2 * kChunk);
@@ -350,19 +365,10 @@ __device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t tid, int b) {
 }
 
 // The index entries of this lane's windows 2 tid and 2 tid + 1: x = both
-// gaps (low byte: window 2 tid), y = both first-code positions (low half:
-// window 2 tid), z = the first-code position of window 2 tid + 2 (the
-// chunk's element count after the last window).
-struct Windows {
-    uint32_t x, y, z;
-};
-__device__ __forceinline__ Windows load_windows(const Item &it, uint32_t tid) {
-    Windows v;
-    v.x = reinterpret_cast<const uint16_t *>(it.gap)[tid];
-    v.y = reinterpret_cast<const uint32_t *>(it.first)[tid];
-    v.z = tid + 1 < (uint32_t)kThreads ? (uint32_t)reinterpret_cast<const uint16_t *>(it.first)[2 * tid + 2]
-                                       : it.nc;
-    return v;
+// gaps (low byte: window 2 tid), y = both code counts (low half: window
+// 2 tid).
+__device__ __forceinline__ u32x2 load_windows(const Item &it, uint32_t tid) {
+    return u32x2{reinterpret_cast<const uint16_t *>(it.gap)[tid], reinterpret_cast<const uint32_t *>(it.cnt)[tid]};
 }
 
 __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
@@ -380,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     // requested block by block as item i's assembly frees the registers.
     u32x4 cw[kCodeLoads];
     u32x2 rw[kBlocks];
-    Windows win;
+    u32x2 win;
     {
         const Item it = load_item(a, begin);
         if (it.staged) load_codes(it, tid, cw);
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const Item it = load_item(a, item);
         const bool more = item + 1 < end;
         const Item nx = load_item(a, more ? item + 1 : item);
-        const Windows win_nx = more ? load_windows(nx, tid) : win;
+        const u32x2 win_nx = more ? load_windows(nx, tid) : win;
 
         // ---- the previous item's tile and staged words are no longer read
         __syncthreads();
@@ -427,28 +433,37 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         }
         if (more && nx.staged) load_codes(nx, tid, cw);
 
-        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions;
-        //      never write past the chunk, whatever the device bytes say
+        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions
         const uint64_t b0 = it.b0, b1 = it.b1, s0 = it.s0;
         const uint32_t nc = it.nc;
         const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
-        uint32_t bad = 0;
-        const uint32_t qa = min(win.y & 0xFFFFu, nc);
-        const uint32_t qb = min(max(win.y >> 16, qa), nc);
-        const uint32_t qe = min(max(win.z, qb), nc);
-        bad |= (qa != (win.y & 0xFFFFu)) | (qb != (win.y >> 16)) | (qe != win.z);
-        const uint32_t na = qb - qa, nb = qe - qb;
+        uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
+        const uint32_t incl = wave_inclusive_sum(na + nb);
         const uint64_t sa = b0 + (2 * tid) * W + (na ? (win.x & 0xFFu) : 0u);
         const uint64_t sb = b0 + (2 * tid + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
-        const uint32_t mn = wave_min(min(na, nb));
-        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
-
-        // the wave's first code (for the end check of the wave below)
+        // the wave's code total and first code, for the waves above it
         const uint64_t mask = __ballot(na + nb != 0);
         const uint64_t first = na ? sa : sb;          // this lane's first code
         const uint64_t wf = __shfl((unsigned long long)first, mask ? (int)__builtin_ctzll(mask) : 0);
+        if (lane == 63) L.wave_total[wave] = incl;
         if (lane == 0) L.wave_first[wave] = mask ? (uint32_t)(wf - b0) : 0xFFFFFFFFu;
         __syncthreads();
+
+        uint32_t base = 0;
+        for (uint32_t w = 0; w < wave; ++w) base += L.wave_total[w];
+        const uint32_t qa = base + incl - na - nb;
+        const uint32_t qb = qa + na;
+        // never write past the chunk, whatever the device bytes say
+        uint32_t bad = 0;
+        {
+            const uint32_t ca = qa < nc ? min(na, nc - qa) : 0u;
+            const uint32_t cb = qb < nc ? min(nb, nc - qb) : 0u;
+            bad |= (ca != na) | (cb != nb);
+            na = ca;
+            nb = cb;
+        }
+        const uint32_t mn = wave_min(min(na, nb));
+        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
 
         // Window starts relative to the bytes from s0, negated.  Peeks at
         // p <= pmax stay inside the source; the counted loop moves a window

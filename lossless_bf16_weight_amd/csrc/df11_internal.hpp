@@ -68,7 +68,7 @@ struct alignas(16) TensorDesc {
     uint64_t n_elems;
     uint64_t off_ci;
     uint64_t off_gap;
-    uint64_t off_first;
+    uint64_t off_cnt;
     uint64_t off_stream;
     uint64_t stream_bytes;
     uint64_t off_raw;

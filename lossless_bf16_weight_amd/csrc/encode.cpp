@@ -162,8 +162,8 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
     // layout
     const uint64_t off_ci = kHeader;
     const uint64_t off_gap = up256(off_ci + (n_chunks + 1) * 16);
-    const uint64_t off_first = up256(off_gap + n_chunks * kWindows);
-    const uint64_t off_stream = up256(off_first + n_chunks * kWindows * 2);
+    const uint64_t off_cnt = up256(off_gap + n_chunks * kWindows);
+    const uint64_t off_stream = up256(off_cnt + n_chunks * kWindows * 2);
     const uint64_t stream_bytes = up16((total_bits + 7) / 8) + 16;
     const uint64_t off_raw = up256(off_stream + stream_bytes);
     const uint64_t raw_bytes = up16(n);
@@ -189,7 +189,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
     wr64(out + 104, total_bits);
     wr64(out + 112, off_ci);
     wr64(out + 120, off_gap);
-    wr64(out + 128, off_first);
+    wr64(out + 128, off_cnt);
     wr64(out + 136, off_stream);
     wr64(out + 144, stream_bytes);
     wr64(out + 152, off_raw);
@@ -238,11 +238,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
             else stream[first + i] = buf[i];
         }
         memcpy(out + off_gap + c * kWindows, gap, kWindows);
-        unsigned before = 0;   // the chunk's codes that start before window i
-        for (int i = 0; i < kWindows; ++i) {
-            wr16(out + off_first + c * kWindows * 2 + 2 * i, (uint16_t)before);
-            before += cnt[i];
-        }
+        for (int i = 0; i < kWindows; ++i) wr16(out + off_cnt + c * kWindows * 2 + 2 * i, (uint16_t)cnt[i]);
     });
 
     // 6. raw bytes

@@ -70,7 +70,7 @@ namespace {
 
 struct Layout {
     uint64_t n, n_chunks, total_bits;
-    uint64_t off_ci, off_gap, off_first, off_stream, stream_bytes, off_raw, raw_bytes, total;
+    uint64_t off_ci, off_gap, off_cnt, off_stream, stream_bytes, off_raw, raw_bytes, total;
 };
 
 Layout layout_for(uint64_t n, uint64_t total_bits) {
@@ -80,8 +80,8 @@ Layout layout_for(uint64_t n, uint64_t total_bits) {
     L.total_bits = total_bits;
     L.off_ci = kHeader;
     L.off_gap = up256(L.off_ci + (L.n_chunks + 1) * 16);
-    L.off_first = up256(L.off_gap + L.n_chunks * kWindows);
-    L.off_stream = up256(L.off_first + L.n_chunks * kWindows * 2);
+    L.off_cnt = up256(L.off_gap + L.n_chunks * kWindows);
+    L.off_stream = up256(L.off_cnt + L.n_chunks * kWindows * 2);
     L.stream_bytes = up16((total_bits + 7) / 8) + 16;
     L.off_raw = up256(L.off_stream + L.stream_bytes);
     L.raw_bytes = up16(n);
@@ -194,7 +194,7 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     const Layout &L = M.L;
     if (L.n_chunks > kItemChunkMask) return fail(DF11_E_UNSUPPORTED, "%llu chunks", (unsigned long long)L.n_chunks);
     if (rd32(c + 100) != L.n_chunks) return fail(DF11_E_FORMAT, "n_chunks field");
-    if (rd64(c + 112) != L.off_ci || rd64(c + 120) != L.off_gap || rd64(c + 128) != L.off_first ||
+    if (rd64(c + 112) != L.off_ci || rd64(c + 120) != L.off_gap || rd64(c + 128) != L.off_cnt ||
         rd64(c + 136) != L.off_stream || rd64(c + 144) != L.stream_bytes ||
         rd64(c + 152) != L.off_raw || rd64(c + 160) != L.raw_bytes || rd64(c + 168) != L.total)
         return fail(DF11_E_FORMAT, "section offsets or sizes do not match the layout");
@@ -240,16 +240,11 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
         if (sb > b1 || b1 - sb < elems || b1 - sb > elems * kMaxLen)
             return fail(DF11_E_FORMAT, "chunk %llu bit range", (unsigned long long)ch);
         const uint64_t W = (b1 - sb + kWindows - 1) / kWindows;
-        const uint8_t *first = c + L.off_first + ch * kWindows * 2;
-        if (rd16(first) != 0) return fail(DF11_E_FORMAT, "chunk %llu: window 0 does not start at code 0", (unsigned long long)ch);
+        uint64_t sum = 0;
         for (int i = 0; i < kWindows; ++i) {
             const unsigned gap = c[L.off_gap + ch * kWindows + i];
-            const unsigned f0 = rd16(first + 2 * i);
-            const unsigned f1 = i + 1 < kWindows ? rd16(first + 2 * i + 2) : (unsigned)elems;
-            if (f1 < f0 || f1 > elems)
-                return fail(DF11_E_FORMAT, "chunk %llu window %d: first codes %u, %u of %llu",
-                            (unsigned long long)ch, i, f0, f1, (unsigned long long)elems);
-            const unsigned cnt = f1 - f0;
+            const unsigned cnt = rd16(c + L.off_cnt + ch * kWindows * 2 + 2 * i);
+            sum += cnt;
             const uint64_t ws = sb + i * W, we = std::min<uint64_t>(sb + (i + 1) * W, b1);
             if (cnt == 0) {
                 if (gap != 0xFF) return fail(DF11_E_FORMAT, "chunk %llu window %d: gap without codes", (unsigned long long)ch, i);
@@ -258,6 +253,8 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
             if (gap >= (unsigned)kMaxLen || ws >= b1 || ws + gap >= we || cnt > we - ws - gap)
                 return fail(DF11_E_FORMAT, "chunk %llu window %d: gap %u cnt %u", (unsigned long long)ch, i, gap, cnt);
         }
+        if (sum != elems) return fail(DF11_E_FORMAT, "chunk %llu: window counts sum to %llu, not %llu",
+                                      (unsigned long long)ch, (unsigned long long)sum, (unsigned long long)elems);
     }
     // padding of the stream and the raw section, when the bytes are there
     if (bytes >= L.total) {
@@ -369,7 +366,7 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
         d.n_elems = L.n;
         d.off_ci = L.off_ci;
         d.off_gap = L.off_gap;
-        d.off_first = L.off_first;
+        d.off_cnt = L.off_cnt;
         d.off_stream = L.off_stream;
         d.stream_bytes = L.stream_bytes;
         d.off_raw = L.off_raw;

@@ -191,7 +191,7 @@ def header(container: np.ndarray) -> dict:
         "dims": [u64(32 + 8 * i) for i in range(ndim)],
         "chunk_elems": u32(28), "max_code_len": int(c[96]), "windows": u16(98),
         "n_chunks": u32(100), "total_bits": u64(104),
-        "off_chunk_index": u64(112), "off_win_gap": u64(120), "off_win_first": u64(128),
+        "off_chunk_index": u64(112), "off_win_gap": u64(120), "off_win_cnt": u64(128),
         "off_stream": u64(136), "stream_bytes": u64(144), "off_raw": u64(152),
         "raw_bytes": u64(160), "total_bytes": u64(168),
         "code_len": c[208:464].copy(),

@@ -29,9 +29,7 @@
  *    0 is the first bit;
  *  - raw byte: (sign << 7) | fraction, i.e. ((w >> 8) & 0x80) | (w & 0x7F);
  *  - chunks of 32768 elements (64 KiB of BF16 output), each with its start
- *    bit; 512 equal-bit windows per chunk, with per window the offset of its
- *    first code start (gap) and the number of the chunk's codes that start
- *    before it (first).
+ *    bit; 512 equal-bit windows per chunk with (gap, cnt) per window.
  *
  * Container version 2 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
@@ -39,16 +37,14 @@
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
  *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 reserved
  *    98  u16 windows                100  u32 n_chunks     104 u64 total_bits
- *   112  u64 off_chunk_index        120  u64 off_win_gap  128 u64 off_win_first
+ *   112  u64 off_chunk_index        120  u64 off_win_gap  128 u64 off_win_cnt
  *   136  u64 off_stream             144  u64 stream_bytes 152 u64 off_raw
  *   160  u64 raw_bytes              168  u64 total_bytes  176 reserved[32]
  *   208  u8 code_len[256]           464  reserved[48]
- *   chunk index:  (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
- *                 {total_bits, n_elems}
- *   window gap:   n_chunks x 512 x u8   (0xFF = window holds no code start)
- *   window first: n_chunks x 512 x u16  (the chunk's codes that start before
- *                 the window's first bit; window i holds first[i+1] - first[i]
- *                 code starts, the last one chunk_elems - first[511])
+ *   chunk index: (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
+ *                {total_bits, n_elems}
+ *   window gap:  n_chunks x 512 x u8   (0xFF = window holds no code start)
+ *   window cnt:  n_chunks x 512 x u16  (codes that start in the window)
  *   stream:      ceil(total_bits/8) bytes rounded up to 16, plus 16 zero bytes
  *   raw:         n_elems bytes rounded up to 16
  *   Every byte not named above is zero.
@@ -195,7 +191,7 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code) {
 /* ------------------------------------------------------------------ */
 typedef struct {
     uint64_t n, n_chunks, total_bits;
-    uint64_t off_ci, off_gap, off_first, off_stream, stream_bytes, off_raw, raw_bytes, total;
+    uint64_t off_ci, off_gap, off_cnt, off_stream, stream_bytes, off_raw, raw_bytes, total;
 } layout_t;
 
 static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
@@ -204,8 +200,8 @@ static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
     L->total_bits = total_bits;
     L->off_ci = HDR;
     L->off_gap = align256(L->off_ci + (L->n_chunks + 1) * 16);
-    L->off_first = align256(L->off_gap + L->n_chunks * WINDOWS);
-    L->off_stream = align256(L->off_first + L->n_chunks * WINDOWS * 2);
+    L->off_cnt = align256(L->off_gap + L->n_chunks * WINDOWS);
+    L->off_stream = align256(L->off_cnt + L->n_chunks * WINDOWS * 2);
     L->stream_bytes = round16((total_bits + 7) / 8) + 16;
     L->off_raw = align256(L->off_stream + L->stream_bytes);
     L->raw_bytes = round16(n);
@@ -267,7 +263,7 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u64(out + 104, total_bits);
     put_u64(out + 112, L.off_ci);
     put_u64(out + 120, L.off_gap);
-    put_u64(out + 128, L.off_first);
+    put_u64(out + 128, L.off_cnt);
     put_u64(out + 136, L.off_stream);
     put_u64(out + 144, L.stream_bytes);
     put_u64(out + 152, L.off_raw);
@@ -291,30 +287,26 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u64(out + L.off_ci + L.n_chunks * 16 + 8, n);
 
     /* 5. window index: 512 windows of W = ceil(chunk bits / 512) bits; per
-     *    window the offset of its first code start from the window's first
-     *    bit, and how many of the chunk's codes start before that bit */
+     *    window the offset of its first code start and the number of code
+     *    starts */
     for (uint64_t c = 0; c < L.n_chunks; c++) {
         uint64_t b0 = get_u64(out + L.off_ci + c * 16);
         uint64_t b1 = get_u64(out + L.off_ci + (c + 1) * 16);
         uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
         uint8_t *gap = out + L.off_gap + c * WINDOWS;
-        uint8_t *firstp = out + L.off_first + c * WINDOWS * 2;
+        uint8_t *cntp = out + L.off_cnt + c * WINDOWS * 2;
         unsigned cnt[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
         for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
         uint64_t p = b0;
         uint64_t j_end = (c + 1) * CHUNK < n ? (c + 1) * CHUNK : n;
         for (uint64_t j = c * CHUNK; j < j_end; j++) {
-            uint64_t win = (p - b0) / W;      /* the window the code starts in */
+            uint64_t win = (p - b0) / W;
             if (cnt[win] == 0) gap[win] = (uint8_t)(p - (b0 + win * W));
             cnt[win]++;
             p += len[exponent_of(words[j])];
         }
-        unsigned before = 0;                  /* codes of the earlier windows */
-        for (int i = 0; i < WINDOWS; i++) {
-            put_u16(firstp + 2 * i, (uint16_t)before);
-            before += cnt[i];
-        }
+        for (int i = 0; i < WINDOWS; i++) put_u16(cntp + 2 * i, (uint16_t)cnt[i]);
     }
 
     /* 6. raw bytes: sign and fraction, as is */
@@ -347,7 +339,7 @@ static int parse(const uint8_t *c, uint64_t bytes, parsed_t *P) {
     if (get_u32(c + 28) != CHUNK || c[96] != CAP || get_u16(c + 98) != WINDOWS) return ORACLE_E_FORMAT;
     if (get_u32(c + 100) != L->n_chunks) return ORACLE_E_FORMAT;
     if (get_u64(c + 112) != L->off_ci || get_u64(c + 120) != L->off_gap ||
-        get_u64(c + 128) != L->off_first || get_u64(c + 136) != L->off_stream ||
+        get_u64(c + 128) != L->off_cnt || get_u64(c + 136) != L->off_stream ||
         get_u64(c + 144) != L->stream_bytes || get_u64(c + 152) != L->off_raw ||
         get_u64(c + 160) != L->raw_bytes || get_u64(c + 168) != L->total)
         return ORACLE_E_FORMAT;
@@ -429,20 +421,15 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
     uint64_t b1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16);
     uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
     unsigned gap = c[P.L.off_gap + chunk * WINDOWS + win];
-    /* output position of this window's first code: the codes before it; its
-     * code count: up to the next window's first code, or the chunk's end */
-    const uint8_t *firstp = c + P.L.off_first + chunk * WINDOWS * 2;
-    uint64_t e0 = get_u64(c + P.L.off_ci + chunk * 16 + 8);
-    uint64_t e1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16 + 8);
-    uint64_t before = get_u16(firstp + 2 * win);
-    uint64_t after = win + 1 < WINDOWS ? get_u16(firstp + 2 * (win + 1)) : e1 - e0;
-    if (after < before || e0 + after > e1) return ORACLE_E_FORMAT;
-    uint64_t cnt = after - before;
-    uint64_t j0 = e0 + before;
+    unsigned cnt = get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * win);
+    /* output position of this window's first code: codes of earlier windows */
+    uint64_t before = 0;
+    for (int i = 0; i < win; i++) before += get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * i);
+    uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8) + before;
     *n_out = cnt;
     if (cnt == 0) { *end_bit = b0 + win * W; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
     uint64_t pos = b0 + win * W + gap;
-    for (uint64_t k = 0; k < cnt; k++) {
+    for (unsigned k = 0; k < cnt; k++) {
         int e = read_code(&P, stream, &pos);
         if (e < 0) return -e;
         if (out) out[k] = join((unsigned)e, c[P.L.off_raw + j0 + k]);
@@ -502,12 +489,7 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
         if (pos != b1) return ORACLE_E_FORMAT;
         for (int i = 0; i < WINDOWS; i++) {
             if (c[L->off_gap + ch * WINDOWS + i] != gap[i]) return ORACLE_E_FORMAT;
-        }
-        /* first[i]: the codes that start in windows before i */
-        unsigned before = 0;
-        for (int i = 0; i < WINDOWS; i++) {
-            if (get_u16(c + L->off_first + ch * WINDOWS * 2 + 2 * i) != before) return ORACLE_E_FORMAT;
-            before += cnt[i];
+            if (get_u16(c + L->off_cnt + ch * WINDOWS * 2 + 2 * i) != cnt[i]) return ORACLE_E_FORMAT;
         }
     }
     if (pos != L->total_bits) return ORACLE_E_FORMAT;

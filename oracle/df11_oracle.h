@@ -55,9 +55,9 @@ int oracle_decode(const uint8_t *c, uint64_t bytes, uint16_t *out, uint64_t n);
 /* Decode one chunk, starting from its start_bit alone (chunk index only). */
 int oracle_decode_chunk(const uint8_t *c, uint64_t bytes, uint64_t chunk, uint16_t *out);
 
-/* Decode the codes of one window of a chunk from its (gap, first) entries.
- * Writes the window's decoded words to out, their number to *n_out and the
- * end bit position to *end_bit. */
+/* Decode the codes of one window of a chunk from its (gap, cnt) entries.
+ * Writes the cnt decoded words to out, cnt to *n_out and the end bit
+ * position to *end_bit. */
 int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int win,
                        uint16_t *out, uint64_t *n_out, uint64_t *end_bit);
 

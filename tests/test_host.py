@@ -116,25 +116,20 @@ def test_validate_rejects_broken_containers():
     # alone cannot tell; the decoder's window-end check reports it)
     assert bad(lambda x: put64(x, ci + 16, 0)) == E_FORMAT                       # not monotone
     assert bad(lambda x: put64(x, ci + 24, 5)) == E_FORMAT                       # out_elem
-    f0 = h["off_win_first"]
-
-    def put16(x, off, v):
-        x[off:off + 2] = np.array([v], np.uint16).view(np.uint8)
-
-    def get16(x, off):
-        return int(x[off:off + 2].view(np.uint16)[0])
-    assert bad(lambda x: put16(x, f0, 1)) == E_FORMAT                            # first[0] != 0
-    assert bad(lambda x: put16(x, f0 + 2 * 9, get16(x, f0 + 2 * 11))) == E_FORMAT  # not monotone
-    last = f0 + 2 * 511 + 2 * 512 * 3                                            # ragged chunk's
-    assert bad(lambda x: put16(x, last, 12)) == E_FORMAT                         # past its end
+    cnt0 = h["off_win_cnt"]
+    assert bad(lambda x: x.__setitem__(cnt0, int(x[cnt0]) + 1)) == E_FORMAT      # counts sum
     gap0 = h["off_win_gap"]
     assert bad(lambda x: x.__setitem__(gap0 + 7, 30)) == E_FORMAT                # gap >= 24
 
     def empty_with_gap(x):
-        # window 5 gives its codes to window 4 and keeps its gap
-        put16(x, f0 + 2 * 5, get16(x, f0 + 2 * 6))
+        # move window 5's codes to window 4 and give window 5 a gap
+        k = cnt0 + 2 * 5
+        c5 = int(x[k:k + 2].view(np.uint16)[0])
+        x[k:k + 2] = np.array([0], np.uint16).view(np.uint8)
+        k4 = cnt0 + 2 * 4
+        x[k4:k4 + 2] = (x[k4:k4 + 2].view(np.uint16) + c5).view(np.uint8)
     assert bad(empty_with_gap) == E_FORMAT
-    assert _status(c[:h["off_win_first"] + 10]) == E_FORMAT                      # truncated
+    assert _status(c[:h["off_win_cnt"] + 10]) == E_FORMAT                        # truncated
     assert _status(c[:100]) == E_FORMAT
     assert bad(lambda x: x.__setitem__(h["off_raw"] + w.size, 1)) == E_FORMAT    # raw padding
     assert bad(lambda x: x.__setitem__(200, 1)) == E_FORMAT                      # reserved

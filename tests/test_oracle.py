@@ -277,17 +277,17 @@ def test_chunk_and_window_index_reproduce_the_source(n):
         gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
         assert ((gap < 24) | (gap == 0xFF)).all()
         # the index from first principles: every code's start bit from the
-        # source's exponents and the header's code lengths; a window's gap is
-        # its first start's offset, its "first" the starts before it
+        # source's exponents and the header's code lengths; a window's cnt is
+        # the number of starts inside it, its gap the first one's offset
         ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
         starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
         edges = b0 + Wb * np.arange(NW)
-        want_first = np.searchsorted(starts, edges, side="left")
-        first = c[h["off_win_first"] + 2 * NW * ch:h["off_win_first"] + 2 * NW * (ch + 1)].view(np.uint16)
-        assert (first == want_first).all()
-        has = (np.append(want_first[1:], hi - lo) > want_first) & (edges < b1)
-        idx = np.minimum(want_first, hi - lo - 1)
-        want_gap = np.where(has, starts[idx] - edges, 0xFF)
+        before = np.searchsorted(starts, edges, side="left")
+        want_cnt = np.diff(np.append(before, hi - lo))
+        cnt = c[h["off_win_cnt"] + 2 * NW * ch:h["off_win_cnt"] + 2 * NW * (ch + 1)].view(np.uint16)
+        assert (cnt == want_cnt).all()
+        idx = np.minimum(before, hi - lo - 1)
+        want_gap = np.where(want_cnt > 0, starts[idx] - edges, 0xFF)
         assert (gap == want_gap).all()
 
 
@@ -335,7 +335,7 @@ def test_corruption_is_detected():
     bad[h["off_win_gap"] + 5] ^= 1                   # a window gap
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_win_first"] + 10] ^= 1                # a window's first code
+    bad[h["off_win_cnt"] + 10] ^= 1                  # a window count
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
     bad[208 + 121] += 1                              # a code length: Kraft breaks

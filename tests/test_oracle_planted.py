@@ -40,9 +40,9 @@ MUTATIONS = [
     ("window gap off by one",
      "gap[win] = (uint8_t)(p - (b0 + win * W));",
      "gap[win] = (uint8_t)(p - (b0 + win * W) + 1);", 0),
-    ("window first counts its own codes",
-     "put_u16(firstp + 2 * i, (uint16_t)before);",
-     "put_u16(firstp + 2 * i, (uint16_t)(before + cnt[i]));", 0),
+    ("window count misses a code that starts on the window's first bit",
+     "            cnt[win]++;",
+     "            cnt[win] += (p != b0 + win * W);", 0),
     ("window width rounds down",
      "uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;",
      "uint64_t W = (b1 - b0) / WINDOWS + 1;", 0),
