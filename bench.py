@@ -13,6 +13,8 @@ Prints one JSON line:
                  stream), against the MI355X peak of 8 TB/s; `traffic` holds
                  the HBM bytes per launch measured with rocprofv3 counters
                  when they were taken on the current kernel source, else null
+  bw_control     the same read and write byte counts moved by a kernel that
+                 does no decoding (df11_bw_control), as the practical ceiling
   cpu_baseline   the CPU oracle's bit-serial decoder on the host cores, over a
                  bounded sample of the same containers
 Inputs are synthetic: seeded N(0, 0.02) weights rounded to BF16.
@@ -175,6 +177,23 @@ def main():
     durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
     avg_ms = sum(durs_ms) / len(durs_ms)
 
+    # bandwidth control: the same read and write sizes, no decoding
+    ctl_src = torch.empty((bytes_read + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+    ctl_src.fill_(1)
+    ctl_dst = torch.empty(bytes_written, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        df11.bw_control(ctl_src, ctl_dst, stream=stream)
+    c_starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    c_ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(n_ev):
+        c_starts[i].record(stream)
+        df11.bw_control(ctl_src, ctl_dst, stream=stream)
+        c_ends[i].record(stream)
+    torch.cuda.synchronize()
+    ctl_ms = sum(s.elapsed_time(e) for s, e in zip(c_starts, c_ends)) / n_ev
+    ctl_gbs = (ctl_src.numel() + ctl_dst.numel()) / (ctl_ms * 1e-3) / 1e9
+    del ctl_src, ctl_dst
+
     # bit-exact against the source words
     df11.check(plan, stream=stream)
     exact = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) for w, o in zip(words, outs))
@@ -216,6 +235,15 @@ def main():
             "kernel": "df11::decode_kernel",
             "kernel_ms_avg": round(avg_ms, 5),
             "kernel_ms_min": round(durs_ms[0], 5),
+        },
+        # the same bytes moved with no decoding (df11_bw_control): the HBM
+        # rate this access pattern reaches on this GPU
+        "bw_control": {
+            "value": round(ctl_gbs, 1),
+            "unit": "GB/s",
+            "ms": round(ctl_ms, 5),
+            "frac_of_peak": round(ctl_gbs / PEAK_HBM_GBS, 4),
+            "decode_over_control": round(achieved / ctl_gbs, 4),
         },
     }
     if not args.no_cpu_baseline:

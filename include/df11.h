@@ -164,6 +164,22 @@ df11_status df11_decode_batch(df11_plan_t plan, const void *const *d_containers,
  * lane whose codes did not end where the index says the next one starts. */
 df11_status df11_check(df11_plan_t plan, hipStream_t stream);
 
+/* ------------------------------------------------------------ measurement */
+
+/* Bandwidth control: enqueue on `stream` a kernel that reads src_bytes from
+ * DEVICE memory d_src and writes dst_bytes to DEVICE memory d_dst with the
+ * access pattern of a decode (16-byte non-temporal loads and stores,
+ * contiguous ranges per workgroup) and no decoding; every source byte is read
+ * and every output byte written.  Called with a decode's read and write
+ * sizes, its rate is the HBM ceiling for that decode -- the analogue of the
+ * control condition in the mlx-dfloat project page's overhead benchmark (the
+ * same path without the decoding).  Sizes: multiples of 16, at least 16,
+ * below 2^40 bytes; pointers 16-byte aligned, regions not overlapping.  The
+ * output bytes are unspecified.  Never allocates or synchronizes.
+ * Returns DF11_OK, DF11_E_ARG or DF11_E_HIP. */
+df11_status df11_bw_control(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
+                            int hip_device, hipStream_t stream);
+
 /* ------------------------------------------------------------------- misc */
 
 /* Text of the last non-OK status on this thread (never NULL). */

@@ -6,5 +6,5 @@ HIP library `libdf11.so` decodes containers back into bit-identical BF16
 tensors in GPU memory.  See include/df11.h for the C ABI and the container
 layout.
 """
-from ._lib import (DF11Error, Plan, check, container_bound, decode, decode_batch, encode,  # noqa: F401
-                   lib, validate, validate_status)
+from ._lib import (DF11Error, Plan, bw_control, check, container_bound, decode,  # noqa: F401
+                   decode_batch, encode, lib, validate, validate_status)

@@ -20,6 +20,7 @@ SOURCES = [
     ("host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("encode.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("decode.hip", DEVICE),
+    ("control.hip", DEVICE),
 ]
 
 

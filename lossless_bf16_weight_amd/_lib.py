@@ -53,7 +53,7 @@ _lib = None
 EXPORTS = [
     "df11_validate", "df11_container_bound", "df11_encode", "df11_plan", "df11_plan_destroy",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
-    "df11_status_str", "df11_abi_version",
+    "df11_status_str", "df11_abi_version", "df11_bw_control",
 ]
 
 
@@ -93,6 +93,8 @@ def lib():
     L.df11_status_str.restype = ctypes.c_char_p
     L.df11_abi_version.argtypes = []
     L.df11_abi_version.restype = ctypes.c_int
+    L.df11_bw_control.argtypes = [vp, u64, vp, u64, ctypes.c_int, vp]
+    L.df11_bw_control.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -203,6 +205,13 @@ def decode_batch(plan: Plan, containers: List, outs: List, stream=None):
     cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in containers])
     op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     _raise(lib().df11_decode_batch(plan.handle, cp, op, _stream_handle(stream)))
+
+
+def bw_control(src, dst, device: int = 0, stream=None):
+    """Enqueue the bandwidth-control kernel: read all of `src`, write all of
+    `dst` (device tensors, sizes multiples of 16 bytes), no decoding."""
+    _raise(lib().df11_bw_control(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),
+                                 dst.numel() * dst.element_size(), device, _stream_handle(stream)))
 
 
 def check(plan: Plan, stream=None):

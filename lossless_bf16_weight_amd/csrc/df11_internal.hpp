@@ -100,4 +100,9 @@ hipError_t launch_decode(const DecodeArgs &args, int grid, hipStream_t stream);
 // Workgroups of the decode kernel that fit on one compute unit at once.
 int decode_wgs_per_cu();
 
+// Launches the bandwidth-control kernel (control.hip): reads src_bytes, writes
+// dst_bytes (both multiples of 16, pointers 16-byte aligned).
+hipError_t launch_bw_control(const void *src, uint64_t src_bytes, void *dst, uint64_t dst_bytes,
+                             int grid, hipStream_t stream);
+
 }  // namespace df11

@@ -495,6 +495,25 @@ extern "C" df11_status df11_decode_batch(df11_plan_t p, const void *const *d_con
     return DF11_OK;
 }
 
+extern "C" df11_status df11_bw_control(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
+                                       int hip_device, hipStream_t stream) {
+    if (!d_src || !d_dst) return fail(DF11_E_ARG, "NULL buffer");
+    if (((uintptr_t)d_src | (uintptr_t)d_dst) & 15) return fail(DF11_E_ARG, "buffers must be 16-byte aligned");
+    if (src_bytes < 16 || dst_bytes < 16 || (src_bytes | dst_bytes) & 15)
+        return fail(DF11_E_ARG, "sizes must be positive multiples of 16");
+    if (src_bytes >= (uint64_t(1) << 40) || dst_bytes >= (uint64_t(1) << 40))
+        return fail(DF11_E_ARG, "sizes must be below 2^40 bytes");
+    const uintptr_t s0 = (uintptr_t)d_src, d0 = (uintptr_t)d_dst;
+    if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return fail(DF11_E_ARG, "regions overlap");
+    DeviceGuard guard(hip_device);
+    if (guard.err != hipSuccess) return fail(DF11_E_HIP, "hipSetDevice(%d): %s", hip_device, hipGetErrorString(guard.err));
+    int n_cu = 0;
+    HIP_TRY(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device));
+    if (n_cu <= 0) return fail(DF11_E_HIP, "device %d: no compute units", hip_device);
+    HIP_TRY(launch_bw_control(d_src, src_bytes, d_dst, dst_bytes, n_cu * 32, stream));
+    return DF11_OK;
+}
+
 extern "C" df11_status df11_check(df11_plan_t p, hipStream_t stream) {
     if (!p) return fail(DF11_E_ARG, "plan is NULL");
     DeviceGuard guard(p->device);

@@ -255,3 +255,19 @@ def test_workload_flux_dit_block():
     ws, cs = _full_workload(W.flux_dit_block())
     _sampled_oracle_chunks(cs[-1], ws[-1])
     _sampled_oracle_chunks(cs[12], ws[12])
+
+
+def test_bw_control_moves_every_byte():
+    """The bandwidth control reads the source and writes every output unit."""
+    torch = _torch()
+    src = torch.full((3 * 4096 + 16,), 1, dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(5 * 4096 + 32, dtype=torch.uint8, device="cuda")
+    df11.bw_control(src, dst)
+    torch.cuda.synchronize()
+    words = dst.view(torch.int32).reshape(-1, 4).cpu().numpy().astype(np.int64) & 0xFFFFFFFF
+    assert (words[:, 1:] == 0x01010101).all()
+    assert (words[:, 0] == (0x01010101 ^ np.arange(words.shape[0]))).all()
+    with pytest.raises(df11.DF11Error):
+        df11.bw_control(src[:15], dst)                # size not a multiple of 16
+    with pytest.raises(df11.DF11Error):
+        df11.bw_control(src, src)                     # overlapping regions
