@@ -46,10 +46,11 @@ namespace df11 {
 constexpr int kThreads = 256;                      // lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = kChunk;                 // one exponent byte per element
-// LDS per workgroup: 14 KiB staged codes + 32 KiB tile + 5.8 KiB tables =
+constexpr uint32_t kTilePadded = kTileBytes + kTileBytes / 32;   // 4 pad bytes per 128
+// LDS per workgroup: 13 KiB staged codes + 33 KiB tile + 5.8 KiB tables =
 // 51.8 KiB, so that three workgroups fit in a compute unit's 160 KiB (the
 // allocation is rounded up, and 52.8 KiB would leave room for only two).
-constexpr int kCodeCap = 14 * 1024;                // staged code bytes per chunk
+constexpr int kCodeCap = 13 * 1024;                // staged code bytes per chunk
 constexpr int kCodeWords = kCodeCap / 4;
 constexpr int kCodeLoads = (kCodeCap + 16 * kThreads - 1) / (16 * kThreads);
 constexpr int kBlockElems = 8 * kThreads;          // elements per store block
@@ -66,7 +67,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct Lds {
     uint32_t pad[3];
     uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
-    uint8_t tile[kTileBytes + 16];
+    uint8_t tile[kTilePadded + 16];
     LutRecord lut;
     // per wave: bit offset from the chunk start of the first code of its
     // first non-empty window (~0: all its windows are empty), and the number
@@ -76,7 +77,7 @@ struct Lds {
 };
 static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0, "LDS alignment");
 static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
-constexpr uint32_t kDummy = kTileBytes + 8;   // tile bytes nobody reads
+constexpr uint32_t kDummy = kTilePadded;   // a tile dword nobody reads
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -190,98 +191,157 @@ __device__ __forceinline__ uint32_t entry_at(const Lds &L, const Src &src, uint3
 __device__ __forceinline__ uint32_t ent_count(uint32_t ent) { return ent >> kEntCountShift; }
 __device__ __forceinline__ uint32_t ent_bits(uint32_t ent) { return (ent >> kEntLenShift) & 31u; }
 
-// Store an entry's three code bytes at tile bytes q..q+2 (byte stores: an
-// unaligned 4-byte store stalls the LDS more than three aligned ones).
-// Bytes past the entry's codes are garbage that a later store of the same
-// window overwrites; callers guarantee they stay inside the window.
-__device__ __forceinline__ void put4(Lds &L, uint32_t q, uint32_t ent) {
-    L.tile[q] = (uint8_t)ent;
-    L.tile[q + 1] = (uint8_t)(ent >> 8);
-    L.tile[q + 2] = (uint8_t)(ent >> 16);
+// One window's decoder.  Output bytes are gathered per tile dword: `acc`
+// holds the bytes of q's dword below q (the higher bytes are zero), and every
+// look-up stores that dword whole.  A dword that holds the end of one window
+// and the start of the next is stored by both windows' chains, each with
+// zeros in the other's bytes; so no chain stores its window's first dword
+// during the decode: it keeps it in `head`, and after a barrier every chain
+// writes its first-dword bytes one by one.  The last dword a chain stores
+// (after its last look-up, from acc when that look-up crossed into it) may
+// hold bytes past its window's end (decoded codes of the next window: the
+// right values, or zeros), which the next window's first-dword bytes
+// overwrite.
+struct Chain {
+    uint32_t pn;     // negated stream position of the next code
+    uint32_t q;      // chunk position of the next output byte
+    uint32_t acc;    // bytes of q's tile dword below q
+    uint32_t q0, qe; // the window's first position and end
+    uint32_t head;   // the window's first tile dword (bytes from q0 & 3 on)
+};
+
+// The tile dword that holds chunk position q: 4 pad bytes after every 128
+// positions, so that the dwords lanes store at the same time (their
+// windows' outputs start about 64 positions apart) spread over the banks.
+__device__ __forceinline__ uint32_t tile_dword(uint32_t q) { return (q + ((q >> 7) << 2)) & ~3u; }
+
+template <bool kHead>
+__device__ __forceinline__ void emit(Lds &L, Chain &c, uint32_t ent) {
+    const uint32_t f8 = (c.q & 3u) << 3;
+    const uint64_t x = (uint64_t)(ent & 0xFFFFFFu) << f8;   // entry bytes at q and on
+    const uint32_t lo = c.acc | (uint32_t)x;
+    uint32_t a = tile_dword(c.q);
+    if (kHead) {
+        const bool in_head = ((c.q ^ c.q0) >> 2) == 0u;
+        c.head = in_head ? lo : c.head;
+        a = in_head ? kDummy : a;
+    }
+    *reinterpret_cast<uint32_t *>(L.tile + a) = lo;
+    const uint32_t qn = c.q + ent_count(ent);
+    c.acc = ((qn ^ c.q) >> 2) ? (uint32_t)(x >> 32) : lo;
+    c.q = qn;
+    c.pn -= ent_bits(ent);
 }
 
-// Decode both windows of this lane.  pa/pb: negated start bits; qa/qb: tile
-// positions; na/nb: code counts; T: look-ups after which every window of the
-// wave still has at least three codes left.  Returns the negated end bits.
+// Both chains' look-up entries, their LDS round trips overlapped (the fences
+// keep the scheduler from serializing them: addresses | both code reads |
+// funnel shifts and table indices | both table reads).  kClamp: clamp the
+// peek positions to the source.
+template <bool kClamp, class Src>
+__device__ __forceinline__ void entries(const Lds &L, const Src &src, uint32_t pa, uint32_t pb,
+                                        uint32_t &ea, uint32_t &eb, uint32_t &bad) {
+    uint32_t ta, tb;
+    if (kClamp) {
+        pa = (int32_t)pa < (int32_t)src.pn_min ? src.pn_min : pa;
+        pb = (int32_t)pb < (int32_t)src.pn_min ? src.pn_min : pb;
+    }
+    if constexpr (Src::kLds) {
+        const uint32_t ja = (31u - pa) >> 5, jb = (31u - pb) >> 5;
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t a0 = src.w[ja], a1 = src.w[ja + 1];
+        const uint32_t b0 = src.w[jb], b1 = src.w[jb + 1];
+        __builtin_amdgcn_sched_barrier(0);
+        ta = __builtin_amdgcn_alignbit(a0, a1, pa);
+        tb = __builtin_amdgcn_alignbit(b0, b1, pb);
+        const uint32_t ia = ta >> (32 - kL1Bits), ib = tb >> (32 - kL1Bits);
+        __builtin_amdgcn_sched_barrier(0);
+        ea = L.lut.l1[ia];
+        eb = L.lut.l1[ib];
+    } else {
+        ta = src.peek_unclamped(pa);
+        tb = src.peek_unclamped(pb);
+        ea = L.lut.l1[ta >> (32 - kL1Bits)];
+        eb = L.lut.l1[tb >> (32 - kL1Bits)];
+    }
+    if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
+        if (ea == 0) ea = long_entry(L.lut, ta, bad);
+        if (eb == 0) eb = long_entry(L.lut, tb, bad);
+    }
+}
+
+__device__ __forceinline__ void flush_tail(Lds &L, const Chain &c) {
+    if (c.qe > c.q0 && (c.q & ~3u) < c.qe && ((c.q ^ c.q0) >> 2) != 0u)
+        *reinterpret_cast<uint32_t *>(L.tile + tile_dword(c.q)) = c.acc;
+}
+
+// Bits taken by the first n codes of an entry (n <= its count).
+__device__ __forceinline__ uint32_t entry_bits(const Lds &L, uint32_t ent, uint32_t n) {
+    if (n >= ent_count(ent)) return ent_bits(ent);
+    uint32_t c = 0;
+    for (uint32_t k = 0; k < n; ++k) c += L.lut.len[(ent >> (8 * k)) & 0xFFu];
+    return c;
+}
+
+// Decode both windows of this lane.  T: look-ups after which no window of
+// the wave has run out of codes.  On return A.pn / B.pn are the negated end
+// positions of the windows' codes (the next code after each window's last).
 template <class Src>
-__device__ __forceinline__ void decode_pair(Lds &L, const Src &src, uint32_t &pa, uint32_t &pb,
-                                            uint32_t qa, uint32_t qb, uint32_t na, uint32_t nb,
-                                            uint32_t T, uint32_t &bad) {
-    const uint32_t qa0 = qa, qb0 = qb;
+__device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Chain &B, uint32_t T,
+                                            uint32_t &bad) {
+    uint32_t ea, eb;
     // 1. counted (the caller keeps the starts at least 24*T bits below the
-    //    source's end, so these peeks need no clamp): every look-up's codes and the garbage behind them stay
-    //    inside the window (at least three codes remain afterwards)
-    for (uint32_t t = 0; t < T; ++t) {
-        uint32_t ta, tb, ea, eb;
-        if constexpr (Src::kLds) {
-            // both windows' LDS round trips overlap: the fences keep the
-            // scheduler from serializing them (addresses | both code reads |
-            // funnel shifts and table indices | both table reads)
-            const uint32_t ja = (31u - pa) >> 5, jb = (31u - pb) >> 5;
-            __builtin_amdgcn_sched_barrier(0);
-            const uint32_t a0 = src.w[ja], a1 = src.w[ja + 1];
-            const uint32_t b0 = src.w[jb], b1 = src.w[jb + 1];
-            __builtin_amdgcn_sched_barrier(0);
-            ta = __builtin_amdgcn_alignbit(a0, a1, pa);
-            tb = __builtin_amdgcn_alignbit(b0, b1, pb);
-            const uint32_t ia = ta >> (32 - kL1Bits), ib = tb >> (32 - kL1Bits);
-            __builtin_amdgcn_sched_barrier(0);
-            ea = L.lut.l1[ia];
-            eb = L.lut.l1[ib];
-        } else {
-            ta = src.peek_unclamped(pa);
-            tb = src.peek_unclamped(pb);
-            ea = L.lut.l1[ta >> (32 - kL1Bits)];
-            eb = L.lut.l1[tb >> (32 - kL1Bits)];
-        }
-        if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
-            if (ea == 0) ea = long_entry(L.lut, ta, bad);
-            if (eb == 0) eb = long_entry(L.lut, tb, bad);
-        }
-        put4(L, qa, ea);
-        put4(L, qb, eb);
-        qa += ent_count(ea);
-        pa -= ent_bits(ea);
-        qb += ent_count(eb);
-        pb -= ent_bits(eb);
+    //    source's end, so these peeks need no clamp); a chain leaves its
+    //    window's first dword within four look-ups
+    uint32_t t = 0;
+    for (; t < T && t < 4u; ++t) {
+        entries<false>(L, src, A.pn, B.pn, ea, eb, bad);
+        emit<true>(L, A, ea);
+        emit<true>(L, B, eb);
     }
-    // 2. masked: windows with at least four codes left take a look-up (its
-    //    garbage still lands inside), the others wait
-    uint32_t ra = na - (qa - qa0), rb = nb - (qb - qb0);
-    while (__ballot((ra >= 4) | (rb >= 4))) {
-        const bool aa = ra >= 4, ab = rb >= 4;
-        const uint32_t ea = entry_at(L, src, pa, bad);
-        const uint32_t eb = entry_at(L, src, pb, bad);
-        put4(L, aa ? qa : kDummy, ea);
-        put4(L, ab ? qb : kDummy, eb);
-        const uint32_t ka = aa ? ent_count(ea) : 0u, kb = ab ? ent_count(eb) : 0u;
-        qa += ka;
-        ra -= ka;
-        pa -= aa ? ent_bits(ea) : 0u;
-        qb += kb;
-        rb -= kb;
-        pb -= ab ? ent_bits(eb) : 0u;
+    for (; t < T; ++t) {
+        entries<false>(L, src, A.pn, B.pn, ea, eb, bad);
+        emit<false>(L, A, ea);
+        emit<false>(L, B, eb);
     }
-    // 3. exact: the last (at most three) codes of each window, byte stores
+    // 2. masked: each window until its last code; the state before a
+    //    window's last look-up is kept to find where its last code ends
+    uint32_t pa_r = A.pn, qa_r = A.q, ea_r = 0, pb_r = B.pn, qb_r = B.q, eb_r = 0;
+    while (__ballot((A.q < A.qe) | (B.q < B.qe))) {
+        const bool aa = A.q < A.qe, ab = B.q < B.qe;
+        entries<true>(L, src, A.pn, B.pn, ea, eb, bad);
+        if (aa) {
+            pa_r = A.pn;
+            qa_r = A.q;
+            ea_r = ea;
+            emit<true>(L, A, ea);
+        }
+        if (ab) {
+            pb_r = B.pn;
+            qb_r = B.q;
+            eb_r = eb;
+            emit<true>(L, B, eb);
+        }
+    }
+    if (A.qe > A.q0) A.pn = pa_r - entry_bits(L, ea_r, A.qe - qa_r);
+    if (B.qe > B.q0) B.pn = pb_r - entry_bits(L, eb_r, B.qe - qb_r);
+    // 3. a last look-up that crossed into a new dword left that dword's
+    //    bytes in acc: store them when the window reaches into it (and it is
+    //    not the window's first dword)
+    flush_tail(L, A);
+    flush_tail(L, B);
+}
+
+// After every chain's dword stores (and a barrier): the window's bytes in
+// its first tile dword, one by one.
+__device__ __forceinline__ void write_head(Lds &L, const Chain &c) {
+    const uint32_t n = c.qe - c.q0;
+    const uint32_t f = c.q0 & 3u;
+    const uint32_t m = n < 4u - f ? n : 4u - f;
+    const uint32_t a = tile_dword(c.q0) + f;
 #pragma unroll
-    for (int w = 0; w < 2; ++w) {
-        uint32_t &pn = w ? pb : pa;
-        uint32_t &q = w ? qb : qa;
-        uint32_t &r = w ? rb : ra;
-        while (r > 0) {
-            const uint32_t ent = entry_at(L, src, pn, bad);
-            uint32_t n = ent_count(ent), c = ent_bits(ent);
-            if (n > r) {
-                n = r;
-                c = 0;
-                for (uint32_t k = 0; k < n; ++k) c += L.lut.len[(ent >> (8 * k)) & 0xFFu];
-            }
-            for (uint32_t k = 0; k < n; ++k) L.tile[q + k] = (uint8_t)(ent >> (8 * k));
-            q += n;
-            r -= n;
-            pn -= c;
-        }
-    }
+    for (uint32_t k = 0; k < 3; ++k)
+        if (k < m) L.tile[a + k] = (uint8_t)(c.head >> (8 * (f + k)));
+    if (m == 4u) L.tile[a + 3] = (uint8_t)(c.head >> 24);
 }
 
 // Loads of data that no thread writes during the kernel (work list,
@@ -463,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             nb = cb;
         }
         const uint32_t mn = wave_min(min(na, nb));
-        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 3 ? (mn - 3) / kMaxPerLookup : 0u);
+        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 1 ? (mn - 1) / kMaxPerLookup : 0u);
 
         // Window starts relative to the bytes from s0, negated.  Peeks at
         // p <= pmax stay inside the source; the counted loop moves a window
@@ -476,19 +536,23 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint64_t plim = pmax - 24u * T;
         const uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wrap high when below s0
         bad |= (pra > plim) | (prb > plim);
-        uint32_t pa = 0u - (uint32_t)umin64(pra, plim), pb = 0u - (uint32_t)umin64(prb, plim);
+        Chain A{0u - (uint32_t)umin64(pra, plim), qa, 0u, qa, qa + na, 0u};
+        Chain B{0u - (uint32_t)umin64(prb, plim), qb, 0u, qb, qb + nb, 0u};
         if (it.staged) {
             // peeks read codes[j], codes[j+1] with j <= kCodeWords
             const LdsCodes src{L.codes, 0u - pmax};
-            decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
+            decode_pair(L, src, A, B, T, bad);
         } else {
             // peeks read words j-1 and j of the stream from s0, j < n_words
             const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream + s0) - 1,
                                   0u - pmax};
-            decode_pair(L, src, pa, pb, qa, qb, na, nb, T, bad);
+            decode_pair(L, src, A, B, T, bad);
         }
-        const uint64_t ea = 8 * s0 + (uint32_t)(0u - pa);
-        const uint64_t eb = 8 * s0 + (uint32_t)(0u - pb);
+        const uint64_t ea = 8 * s0 + (uint32_t)(0u - A.pn);
+        const uint64_t eb = 8 * s0 + (uint32_t)(0u - B.pn);
+        __syncthreads();
+        write_head(L, A);
+        write_head(L, B);
         __syncthreads();
 
         // ---- every non-empty window ends where the next non-empty window's
@@ -522,7 +586,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
                 const uint32_t j = kBlockElems * b + 8 * tid;
-                const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
+                const uint32_t ta = tile_dword(j);
+                const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
+                                       *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
                 __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
             }
             if (more) rw[b] = load_raw(nx, tid, b);
@@ -532,7 +598,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
                 const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
-                const u32x2 t8 = *reinterpret_cast<const u32x2 *>(L.tile + j);
+                const uint32_t ta = tile_dword(j);
+                const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
+                                       *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
                 const u32x4 v = join8(t8, r8);
                 if (j + 8 <= nc) {
                     *reinterpret_cast<u32x4 *>(o + j) = v;
