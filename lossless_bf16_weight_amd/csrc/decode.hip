@@ -122,51 +122,56 @@ __device__ __forceinline__ u32x4 join8(u32x2 t8, u32x2 r8) {
 }
 
 // ---- code sources ---------------------------------------------------------
-// A window's position is kept negated, pn = -p (mod 2^32), where p is the
-// bit offset from the source's first word.  The 32 stream bits from p are
-// the funnel shift of words j-1 and j with j = ceil(p / 32) by (-p) mod 32:
-// for p = 32i + s with s > 0 that is (w_i:w_i+1) >> (32 - s), and for s = 0
-// the shift is 0 and yields w_i itself.
+// Source words hold the stream least significant bit first: bit i of word k
+// is stream bit 32 (k - 1) + i (the stream itself is most significant bit
+// first within each byte, so a stored word is byte-swapped and bit-reversed
+// on its way in).  A window's position is kept as P = p + 30, p its stream
+// bit offset from the source's first word: the funnel shift of words k+1:k
+// with k = P / 32 by P mod 32 then yields the stream bits from p - 2 on, so
+// that bits 2..11 are the next 10 stream bits -- already the byte offset of
+// their first-level table entry (the table is indexed by those bits in
+// stream order, first bit lowest).
+
+__device__ __forceinline__ uint32_t lsb_first(uint32_t stored) {
+    return __builtin_bitreverse32(bswap32(stored));
+}
+
+constexpr uint32_t kPosBias = 30;
 
 struct LdsCodes {
     static constexpr bool kLds = true;
-    const uint32_t *w;   // w[j] = staged word j-1
-    uint32_t pn_min;     // smallest pn (largest p) whose words are inside
-    __device__ __forceinline__ uint32_t peek_unclamped(uint32_t pn) const {
-        const uint32_t j = (31u - pn) >> 5;
-        return __builtin_amdgcn_alignbit(w[j], w[j + 1], pn);
-    }
-    __device__ __forceinline__ uint32_t peek(uint32_t pn) const {
-        // p <= pmax  <=>  pn >= -pmax (positions are far below 2^31)
-        return peek_unclamped((int32_t)pn < (int32_t)pn_min ? pn_min : pn);
+    const uint32_t *w;   // w[k] = staged word k-1, least significant bit first
+    uint32_t pmax;       // largest P whose words are inside
+    __device__ __forceinline__ uint32_t peek(uint32_t P) const {
+        const uint32_t k = P >> 5;
+        return __builtin_amdgcn_alignbit(w[k + 1], w[k], P);
     }
 };
 
 struct GlobalCodes {
     static constexpr bool kLds = false;
-    const uint32_t *w;   // w[j] = stream word j-1 (little-endian bytes as stored)
-    uint32_t pn_min;
-    __device__ __forceinline__ uint32_t peek_unclamped(uint32_t pn) const {
-        const uint32_t j = (31u - pn) >> 5;
-        return __builtin_amdgcn_alignbit(bswap32(w[j]), bswap32(w[j + 1]), pn);
-    }
-    __device__ __forceinline__ uint32_t peek(uint32_t pn) const {
-        return peek_unclamped((int32_t)pn < (int32_t)pn_min ? pn_min : pn);
+    const uint32_t *w;   // w[k] = stream word k-1, as stored
+    uint32_t pmax;
+    __device__ __forceinline__ uint32_t peek(uint32_t P) const {
+        const uint32_t k = P >> 5;
+        return __builtin_amdgcn_alignbit(lsb_first(w[k + 1]), lsb_first(w[k]), P);
     }
 };
 
-// First-level style entry for a code longer than kL1Bits at the front of
-// `top`: second-level table, else the canonical limits.  A prefix no valid
-// stream holds sets `bad` and yields a 24-bit code of exponent 0.
+// First-level style entry for a code longer than kL1Bits that starts at bit
+// 2 of the peeked word `top`: second-level table, else the canonical limits.
+// A prefix no valid stream holds sets `bad` and yields a 24-bit code of
+// exponent 0.
 __device__ __forceinline__ uint32_t long_entry(const LutRecord &T, uint32_t top, uint32_t &bad) {
-    const uint32_t i2 = (top >> (32 - kL2Bits)) - T.l2_base;
+    const uint32_t msb = __builtin_bitreverse32(top >> 2);   // next 30 bits, first bit highest
+    const uint32_t i2 = (msb >> (32 - kL2Bits)) - T.l2_base;
     const uint32_t e2 = i2 < T.l2_size ? (uint32_t)T.l2[i2] : 0u;
     uint32_t sym, len;
     if (e2) {
         len = e2 >> 8;
         sym = e2 & 0xFFu;
     } else {
-        const uint32_t v = top >> (32 - kMaxLen);
+        const uint32_t v = msb >> (32 - kMaxLen);
         uint32_t l = kL1Bits + 1;
         while (l <= (uint32_t)kMaxLen && v >= T.lim[l]) ++l;
         if (l > (uint32_t)kMaxLen) {
@@ -181,87 +186,39 @@ __device__ __forceinline__ uint32_t long_entry(const LutRecord &T, uint32_t top,
     return sym | (len << kEntLenShift) | (1u << kEntCountShift);
 }
 
-template <class Src>
-__device__ __forceinline__ uint32_t entry_at(const Lds &L, const Src &src, uint32_t pn, uint32_t &bad) {
-    const uint32_t top = src.peek(pn);
-    const uint32_t ent = L.lut.l1[top >> (32 - kL1Bits)];
-    return ent ? ent : long_entry(L.lut, top, bad);
-}
-
 __device__ __forceinline__ uint32_t ent_count(uint32_t ent) { return ent >> kEntCountShift; }
 __device__ __forceinline__ uint32_t ent_bits(uint32_t ent) { return (ent >> kEntLenShift) & 31u; }
 
-// One window's decoder.  Output bytes are gathered per tile dword: `acc`
-// holds the bytes of q's dword below q (the higher bytes are zero), and every
-// look-up stores that dword whole.  A dword that holds the end of one window
-// and the start of the next is stored by both windows' chains, each with
-// zeros in the other's bytes; so no chain stores its window's first dword
-// during the decode: it keeps it in `head`, and after a barrier every chain
-// writes its first-dword bytes one by one.  The last dword a chain stores
-// (after its last look-up, from acc when that look-up crossed into it) may
-// hold bytes past its window's end (decoded codes of the next window: the
-// right values, or zeros), which the next window's first-dword bytes
-// overwrite.
-struct Chain {
-    uint32_t pn;     // negated stream position of the next code
-    uint32_t q;      // chunk position of the next output byte
-    uint32_t acc;    // bytes of q's tile dword below q
-    uint32_t q0, qe; // the window's first position and end
-    uint32_t head;   // the window's first tile dword (bytes from q0 & 3 on)
-};
-
-// The tile dword that holds chunk position q: 4 pad bytes after every 128
-// positions, so that the dwords lanes store at the same time (their
-// windows' outputs start about 64 positions apart) spread over the banks.
-__device__ __forceinline__ uint32_t tile_dword(uint32_t q) { return (q + ((q >> 7) << 2)) & ~3u; }
-
-template <bool kHead>
-__device__ __forceinline__ void emit(Lds &L, Chain &c, uint32_t ent) {
-    const uint32_t f8 = (c.q & 3u) << 3;
-    const uint64_t x = (uint64_t)(ent & 0xFFFFFFu) << f8;   // entry bytes at q and on
-    const uint32_t lo = c.acc | (uint32_t)x;
-    uint32_t a = tile_dword(c.q);
-    if (kHead) {
-        const bool in_head = ((c.q ^ c.q0) >> 2) == 0u;
-        c.head = in_head ? lo : c.head;
-        a = in_head ? kDummy : a;
-    }
-    *reinterpret_cast<uint32_t *>(L.tile + a) = lo;
-    const uint32_t qn = c.q + ent_count(ent);
-    c.acc = ((qn ^ c.q) >> 2) ? (uint32_t)(x >> 32) : lo;
-    c.q = qn;
-    c.pn -= ent_bits(ent);
-}
-
 // Both chains' look-up entries, their LDS round trips overlapped (the fences
 // keep the scheduler from serializing them: addresses | both code reads |
-// funnel shifts and table indices | both table reads).  kClamp: clamp the
-// peek positions to the source.
+// funnel shifts and table offsets | both table reads).  kClamp: clamp the
+// positions to the source.
 template <bool kClamp, class Src>
 __device__ __forceinline__ void entries(const Lds &L, const Src &src, uint32_t pa, uint32_t pb,
                                         uint32_t &ea, uint32_t &eb, uint32_t &bad) {
-    uint32_t ta, tb;
     if (kClamp) {
-        pa = (int32_t)pa < (int32_t)src.pn_min ? src.pn_min : pa;
-        pb = (int32_t)pb < (int32_t)src.pn_min ? src.pn_min : pb;
+        pa = min(pa, src.pmax);
+        pb = min(pb, src.pmax);
     }
+    uint32_t ta, tb;
+    const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
     if constexpr (Src::kLds) {
-        const uint32_t ja = (31u - pa) >> 5, jb = (31u - pb) >> 5;
+        const uint32_t ka = pa >> 5, kb = pb >> 5;
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t a0 = src.w[ja], a1 = src.w[ja + 1];
-        const uint32_t b0 = src.w[jb], b1 = src.w[jb + 1];
+        const uint32_t a0 = src.w[ka], a1 = src.w[ka + 1];
+        const uint32_t b0 = src.w[kb], b1 = src.w[kb + 1];
         __builtin_amdgcn_sched_barrier(0);
-        ta = __builtin_amdgcn_alignbit(a0, a1, pa);
-        tb = __builtin_amdgcn_alignbit(b0, b1, pb);
-        const uint32_t ia = ta >> (32 - kL1Bits), ib = tb >> (32 - kL1Bits);
+        ta = __builtin_amdgcn_alignbit(a1, a0, pa);
+        tb = __builtin_amdgcn_alignbit(b1, b0, pb);
+        const uint32_t oa = ta & ((kL1Size - 1) << 2), ob = tb & ((kL1Size - 1) << 2);
         __builtin_amdgcn_sched_barrier(0);
-        ea = L.lut.l1[ia];
-        eb = L.lut.l1[ib];
+        ea = *reinterpret_cast<const uint32_t *>(l1 + oa);
+        eb = *reinterpret_cast<const uint32_t *>(l1 + ob);
     } else {
-        ta = src.peek_unclamped(pa);
-        tb = src.peek_unclamped(pb);
-        ea = L.lut.l1[ta >> (32 - kL1Bits)];
-        eb = L.lut.l1[tb >> (32 - kL1Bits)];
+        ta = src.peek(pa);
+        tb = src.peek(pb);
+        ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
+        eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
     }
     if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
         if (ea == 0) ea = long_entry(L.lut, ta, bad);
@@ -269,10 +226,56 @@ __device__ __forceinline__ void entries(const Lds &L, const Src &src, uint32_t p
     }
 }
 
-__device__ __forceinline__ void flush_tail(Lds &L, const Chain &c) {
-    if (c.qe > c.q0 && (c.q & ~3u) < c.qe && ((c.q ^ c.q0) >> 2) != 0u)
-        *reinterpret_cast<uint32_t *>(L.tile + tile_dword(c.q)) = c.acc;
+// One window's decoder.  Output bytes are gathered per tile dword: `acc`
+// holds the bytes of the current dword below the next position (the higher
+// bytes are zero), and every look-up stores that dword whole.  A dword that
+// holds the end of one window and the start of the next is stored by both
+// windows' chains, each with zeros in the other's bytes; so no chain stores
+// its window's first dword during the decode: it keeps it in `head`, and
+// after a barrier every chain writes its first-dword bytes one by one.  The
+// last dword a chain stores (after its last look-up, from acc when that
+// look-up crossed into it) may hold bytes past its window's end (decoded
+// codes of the next window: the right values, or zeros), which the next
+// window's first-dword bytes overwrite.
+struct Chain {
+    uint32_t P;      // stream position of the next code, plus kPosBias
+    uint32_t dw;     // tile dword of the next output position
+    uint32_t f8;     // 8 x the next output position's byte in that dword
+    uint32_t acc;    // that dword's bytes below the next position
+    uint32_t q0, qe; // the window's first output position and its end
+    uint32_t head;   // the window's first tile dword (its bytes from q0 & 3 on)
+};
+
+// Byte offset in the tile of dword dw: 4 pad bytes after every 128, so that
+// the dwords lanes store at the same time (their windows' outputs start
+// about 64 positions apart) spread over the banks.
+__device__ __forceinline__ uint32_t tile_off(uint32_t dw) { return (dw + (dw >> 5)) << 2; }
+
+// Chain c takes look-up entry ent (its bytes go to the tile dword at the
+// next output position); kHead: the chain may still be in its window's
+// first dword.  kMasked: an inactive chain (ent = 0 then) stores to the
+// dummy dword and keeps its state.
+template <bool kHead, bool kMasked = false>
+__device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent, bool active = true) {
+    const uint64_t x = (uint64_t)(ent & 0xFFFFFFu) << c.f8;   // the entry's bytes from f8 on
+    const uint32_t lo = c.acc | (uint32_t)x;
+    uint32_t addr = tile_off(c.dw);
+    if (kHead) {
+        const bool in_head = c.dw == (c.q0 >> 2);
+        c.head = in_head ? lo : c.head;
+        addr = in_head ? kDummy : addr;
+    }
+    if (kMasked) addr = active ? addr : kDummy;
+    *reinterpret_cast<uint32_t *>(L.tile + addr) = lo;
+    const uint32_t f8n = c.f8 + (ent_count(ent) << 3);
+    const bool crossed = f8n >= 32u;
+    c.acc = crossed ? (uint32_t)(x >> 32) : lo;
+    c.dw += crossed ? 1u : 0u;
+    c.f8 = f8n & 31u;
+    c.P += ent_bits(ent);
 }
+
+__device__ __forceinline__ uint32_t out_pos(const Chain &c) { return (c.dw << 2) + (c.f8 >> 3); }
 
 // Bits taken by the first n codes of an entry (n <= its count).
 __device__ __forceinline__ uint32_t entry_bits(const Lds &L, uint32_t ent, uint32_t n) {
@@ -282,9 +285,14 @@ __device__ __forceinline__ uint32_t entry_bits(const Lds &L, uint32_t ent, uint3
     return c;
 }
 
+__device__ __forceinline__ void flush_tail(Lds &L, const Chain &c) {
+    if (c.qe > c.q0 && (c.dw << 2) < c.qe && c.dw != (c.q0 >> 2))
+        *reinterpret_cast<uint32_t *>(L.tile + tile_off(c.dw)) = c.acc;
+}
+
 // Decode both windows of this lane.  T: look-ups after which no window of
-// the wave has run out of codes.  On return A.pn / B.pn are the negated end
-// positions of the windows' codes (the next code after each window's last).
+// the wave has run out of codes.  On return A.P / B.P hold the stream
+// positions (plus kPosBias) where the windows' last codes end.
 template <class Src>
 __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Chain &B, uint32_t T,
                                             uint32_t &bad) {
@@ -294,36 +302,40 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
     //    window's first dword within four look-ups
     uint32_t t = 0;
     for (; t < T && t < 4u; ++t) {
-        entries<false>(L, src, A.pn, B.pn, ea, eb, bad);
-        emit<true>(L, A, ea);
-        emit<true>(L, B, eb);
+        entries<false>(L, src, A.P, B.P, ea, eb, bad);
+        step<true>(L, A, ea);
+        step<true>(L, B, eb);
     }
     for (; t < T; ++t) {
-        entries<false>(L, src, A.pn, B.pn, ea, eb, bad);
-        emit<false>(L, A, ea);
-        emit<false>(L, B, eb);
+        entries<false>(L, src, A.P, B.P, ea, eb, bad);
+        step<false>(L, A, ea);
+        step<false>(L, B, eb);
     }
-    // 2. masked: each window until its last code; the state before a
-    //    window's last look-up is kept to find where its last code ends
-    uint32_t pa_r = A.pn, qa_r = A.q, ea_r = 0, pb_r = B.pn, qb_r = B.q, eb_r = 0;
-    while (__ballot((A.q < A.qe) | (B.q < B.qe))) {
-        const bool aa = A.q < A.qe, ab = B.q < B.qe;
-        entries<true>(L, src, A.pn, B.pn, ea, eb, bad);
-        if (aa) {
-            pa_r = A.pn;
-            qa_r = A.q;
-            ea_r = ea;
-            emit<true>(L, A, ea);
-        }
-        if (ab) {
-            pb_r = B.pn;
-            qb_r = B.q;
-            eb_r = eb;
-            emit<true>(L, B, eb);
-        }
+    // 2. masked, without branches: a finished window stores to the dummy
+    //    dword and keeps its state; the state before each window's last
+    //    look-up is kept to find where its last code ends
+    int32_t ra = (int32_t)(A.qe - out_pos(A)), rb = (int32_t)(B.qe - out_pos(B));
+    uint32_t pa_r = A.P, ra_r = 0, ea_r = 0, pb_r = B.P, rb_r = 0, eb_r = 0;
+    bool any = __ballot((ra > 0) | (rb > 0)) != 0;
+    while (any) {
+        const bool aa = ra > 0, ab = rb > 0;
+        entries<true>(L, src, A.P, B.P, ea, eb, bad);
+        ea = aa ? ea : 0u;
+        eb = ab ? eb : 0u;
+        pa_r = aa ? A.P : pa_r;
+        ra_r = aa ? (uint32_t)ra : ra_r;
+        ea_r = aa ? ea : ea_r;
+        pb_r = ab ? B.P : pb_r;
+        rb_r = ab ? (uint32_t)rb : rb_r;
+        eb_r = ab ? eb : eb_r;
+        ra -= (int32_t)ent_count(ea);
+        rb -= (int32_t)ent_count(eb);
+        step<true, true>(L, A, ea, aa);
+        step<true, true>(L, B, eb, ab);
+        any = __ballot((ra > 0) | (rb > 0)) != 0;
     }
-    if (A.qe > A.q0) A.pn = pa_r - entry_bits(L, ea_r, A.qe - qa_r);
-    if (B.qe > B.q0) B.pn = pb_r - entry_bits(L, eb_r, B.qe - qb_r);
+    if (A.qe > A.q0) A.P = pa_r + entry_bits(L, ea_r, ra_r);
+    if (B.qe > B.q0) B.P = pb_r + entry_bits(L, eb_r, rb_r);
     // 3. a last look-up that crossed into a new dword left that dword's
     //    bytes in acc: store them when the window reaches into it (and it is
     //    not the window's first dword)
@@ -337,11 +349,10 @@ __device__ __forceinline__ void write_head(Lds &L, const Chain &c) {
     const uint32_t n = c.qe - c.q0;
     const uint32_t f = c.q0 & 3u;
     const uint32_t m = n < 4u - f ? n : 4u - f;
-    const uint32_t a = tile_dword(c.q0) + f;
+    const uint32_t a = tile_off(c.q0 >> 2) + f;
 #pragma unroll
-    for (uint32_t k = 0; k < 3; ++k)
+    for (uint32_t k = 0; k < 4; ++k)
         if (k < m) L.tile[a + k] = (uint8_t)(c.head >> (8 * (f + k)));
-    if (m == 4u) L.tile[a + 3] = (uint8_t)(c.head >> 24);
 }
 
 // Loads of data that no thread writes during the kernel (work list,
@@ -483,10 +494,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             for (int k = 0; k < kCodeLoads; ++k) {
                 if (16u * kThreads * k + 16u * tid < (uint32_t)kCodeCap) {
                     u32x4 v = cw[k];
-                    v.x = bswap32(v.x);
-                    v.y = bswap32(v.y);
-                    v.z = bswap32(v.z);
-                    v.w = bswap32(v.w);
+                    v.x = lsb_first(v.x);
+                    v.y = lsb_first(v.y);
+                    v.z = lsb_first(v.z);
+                    v.w = lsb_first(v.w);
                     reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * k + tid] = v;
                 }
             }
@@ -525,10 +536,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint32_t mn = wave_min(min(na, nb));
         uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 1 ? (mn - 1) / kMaxPerLookup : 0u);
 
-        // Window starts relative to the bytes from s0, negated.  Peeks at
-        // p <= pmax stay inside the source; the counted loop moves a window
-        // by at most 24*T bits, so starts are kept at or below pmax - 24*T
-        // (only a container that disagrees with its index starts higher).
+        // Window starts as bit offsets from s0.  Peeks at p <= pmax stay
+        // inside the source; the counted loop moves a window by at most 24*T
+        // bits, so starts are kept at or below pmax - 24*T (only a container
+        // that disagrees with its index starts higher).
         const uint64_t sbytes = it.stream_bytes;
         const uint32_t n_words = (uint32_t)umin64((sbytes - s0) / 4, 1u << 25);
         const uint32_t pmax = it.staged ? 32u * (kCodeWords - 1) : 32u * (n_words - 1);
@@ -536,20 +547,20 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint64_t plim = pmax - 24u * T;
         const uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wrap high when below s0
         bad |= (pra > plim) | (prb > plim);
-        Chain A{0u - (uint32_t)umin64(pra, plim), qa, 0u, qa, qa + na, 0u};
-        Chain B{0u - (uint32_t)umin64(prb, plim), qb, 0u, qb, qb + nb, 0u};
+        Chain A{(uint32_t)umin64(pra, plim) + kPosBias, qa >> 2, (qa & 3u) << 3, 0u, qa, qa + na, 0u};
+        Chain B{(uint32_t)umin64(prb, plim) + kPosBias, qb >> 2, (qb & 3u) << 3, 0u, qb, qb + nb, 0u};
         if (it.staged) {
-            // peeks read codes[j], codes[j+1] with j <= kCodeWords
-            const LdsCodes src{L.codes, 0u - pmax};
+            // peeks read codes[k], codes[k+1] with k = P / 32 <= kCodeWords
+            const LdsCodes src{L.codes, pmax + kPosBias};
             decode_pair(L, src, A, B, T, bad);
         } else {
-            // peeks read words j-1 and j of the stream from s0, j < n_words
+            // peeks read words k-1 and k of the stream from s0, k < n_words
             const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream + s0) - 1,
-                                  0u - pmax};
+                                  pmax + kPosBias};
             decode_pair(L, src, A, B, T, bad);
         }
-        const uint64_t ea = 8 * s0 + (uint32_t)(0u - A.pn);
-        const uint64_t eb = 8 * s0 + (uint32_t)(0u - B.pn);
+        const uint64_t ea = 8 * s0 + (A.P - kPosBias);
+        const uint64_t eb = 8 * s0 + (B.P - kPosBias);
         __syncthreads();
         write_head(L, A);
         write_head(L, B);
@@ -586,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
                 const uint32_t j = kBlockElems * b + 8 * tid;
-                const uint32_t ta = tile_dword(j);
+                const uint32_t ta = tile_off(j >> 2);
                 const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
                                        *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
                 __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
@@ -598,7 +609,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
                 const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
-                const uint32_t ta = tile_dword(j);
+                const uint32_t ta = tile_off(j >> 2);
                 const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
                                        *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
                 const u32x4 v = join8(t8, r8);

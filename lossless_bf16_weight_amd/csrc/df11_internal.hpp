@@ -27,7 +27,8 @@ DF11_HD constexpr uint8_t rot_exp(unsigned e) {
     return (uint8_t)(((e >> 1) | (e << 7)) & 0xFFu);
 }
 
-// First-level decode table: indexed by the next kL1Bits bits of the stream.
+// First-level decode table: indexed by the next kL1Bits bits of the stream,
+// the first of them the lowest index bit.
 // Entry: bits 0..23 up to three rotated exponent bytes (first code in the
 // low byte), bits 24..28 how many stream bits they use, bits 29..30 how many
 // codes (1..3).  Entry 0: the next code is longer than kL1Bits (or no code

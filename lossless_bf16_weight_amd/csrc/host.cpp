@@ -157,7 +157,10 @@ void build_lut(const uint8_t *len, LutRecord &R) {
             pos += flen;
             ++n;
         }
-        R.l1[v] = n ? (syms | ((uint32_t)pos << kEntLenShift) | ((uint32_t)n << kEntCountShift)) : 0u;
+        // indexed by the 10 bits in stream order, first bit lowest (the
+        // decoder reads its code words least significant bit first)
+        const uint32_t rv = __builtin_bitreverse32(v) >> (32 - kL1Bits);
+        R.l1[rv] = n ? (syms | ((uint32_t)pos << kEntLenShift) | ((uint32_t)n << kEntCountShift)) : 0u;
     }
     // Second level: 16-bit prefixes from the first one no code of <= kL1Bits
     // bits covers.
