@@ -126,8 +126,9 @@ df11_status df11_encode(const uint16_t *host_words, uint64_t n_elems, int ndim,
  * host_meta_bytes[t] bytes.  Every prefix is validated (df11_validate).  The
  * plan builds each tensor's decode tables (a 1024-entry first-level table
  * that resolves up to three codes per look-up, a second-level table for codes
- * of 11 to 16 bits, canonical limits for longer codes) and uploads them, with the per-tensor
- * descriptors and the chunk work list, to device `hip_device` in one
+ * of 11 to 16 bits, canonical limits for longer codes) and uploads them, with
+ * one 64-byte record per chunk (where its stream, window index and raw bytes
+ * lie, from the validated chunk index), to device `hip_device` in one
  * allocation.  The caller may free host_meta once this returns.
  * flags: reserved, pass 0. */
 df11_status df11_plan(const void *const *host_meta, const size_t *host_meta_bytes,
@@ -146,10 +147,11 @@ df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info)
  * bytes as the prefix given to df11_plan).  d_out: DEVICE pointer to
  * n_elems * 2 bytes (16-byte aligned), not overlapping the container.
  * Enqueues on `stream` and returns; never allocates and never synchronizes
- * (safe under stream capture).  Memory safety does not depend on the
- * device bytes: a container that differs from the planned one gives wrong
- * words and sets the plan's corruption flag (see df11_check), never an
- * out-of-bounds access. */
+ * (safe under stream capture).  The chunk start bits come from the plan;
+ * the window index, the stream and the raw bytes from d_container.  Memory
+ * safety does not depend on the device bytes: a container that differs from
+ * the planned one gives wrong words and sets the plan's corruption flag (see
+ * df11_check), never an out-of-bounds access. */
 df11_status df11_decode(df11_plan_t plan, int tensor, const void *d_container,
                         void *d_out, hipStream_t stream);
 

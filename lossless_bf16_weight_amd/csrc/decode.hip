@@ -50,7 +50,6 @@ constexpr uint32_t kTilePadded = kTileBytes + kTileBytes / 32;   // 4 pad bytes 
 // LDS per workgroup: 13 KiB staged codes + 33 KiB tile + 5.8 KiB tables =
 // 51.8 KiB, so that three workgroups fit in a compute unit's 160 KiB (the
 // allocation is rounded up, and 52.8 KiB would leave room for only two).
-constexpr int kCodeCap = 13 * 1024;                // staged code bytes per chunk
 constexpr int kCodeWords = kCodeCap / 4;
 constexpr int kCodeLoads = (kCodeCap + 16 * kThreads - 1) / (16 * kThreads);
 constexpr int kBlockElems = 8 * kThreads;          // elements per store block
@@ -366,52 +365,40 @@ __device__ __forceinline__ T const_load(const T *p) {
 
 // One work item (a chunk of a tensor) and where its bytes are.
 struct Item {
-    const uint8_t *stream;   // the container's stream section
+    const uint8_t *stream;   // the staged stream bytes
     const uint8_t *raw;      // raw bytes from the chunk's first element
     const uint8_t *gap;      // the chunk's window gaps
-    const uint8_t *cnt;      // the chunk's window code counts
+    const uint8_t *cnt;      // the chunk's window counts
     uint16_t *out;           // output from the chunk's first element
-    uint64_t b0, b1;         // the chunk's stream bits
-    uint64_t s0;             // first staged stream byte (16-byte aligned)
-    uint64_t stream_bytes;
-    uint32_t raw_left;       // raw bytes from the chunk's first element (<= 64 KiB)
-    uint32_t nc;             // elements
+    uint32_t rel0, nbits;    // the chunk's stream bits, relative to the staged bytes
     uint32_t s_len;          // staged bytes
-    uint32_t staged;         // the chunk's codes fit the LDS area
-    uint32_t lut;
+    uint32_t staged;         // the chunk's codes go through LDS
+    uint32_t nc;             // elements
+    uint32_t raw_left;       // raw bytes from the chunk's first element
+    uint32_t n_words;        // stream words from the staged first byte on
+    uint32_t lut;            // plan tensor index
 };
 
 __device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
-    uint32_t tl, chunk;
-    if (a.work) {
-        const uint32_t w = const_load(a.work + item);
-        tl = w >> kItemChunkBits;
-        chunk = w & kItemChunkMask;
-    } else {
-        tl = 0;
-        chunk = item;
-    }
+    const ChunkRec *r = a.recs + item;
     Item it;
-    const TensorDesc *d = a.desc + a.tensor_base + tl;
+    const uint32_t tensor = const_load(&r->tensor);
+    const uint32_t tl = tensor - a.tensor_base;
     const uint8_t *C = a.containers[tl];
-    const uint64_t elem0 = (uint64_t)chunk * kChunk;
-    it.stream = C + const_load(&d->off_stream);
-    it.raw = C + const_load(&d->off_raw) + elem0;
-    it.gap = C + const_load(&d->off_gap) + (uint64_t)chunk * kWindows;
-    it.cnt = C + const_load(&d->off_cnt) + (uint64_t)chunk * kWindows * 2;
-    it.out = a.outs[tl] + elem0;
-    it.nc = (uint32_t)umin64(kChunk, const_load(&d->n_elems) - elem0);
-    it.raw_left = (uint32_t)umin64(const_load(&d->raw_bytes) - elem0, 2 * kChunk);
-    it.lut = const_load(&d->lut_index);
-    const uint64_t *ci = reinterpret_cast<const uint64_t *>(C + const_load(&d->off_ci)) + 2 * (uint64_t)chunk;
-    it.b0 = const_load(ci);
-    it.b1 = umax64(const_load(ci + 2), it.b0);
-    const uint64_t sbytes = const_load(&d->stream_bytes);
-    it.stream_bytes = sbytes;
-    it.s0 = umin64((it.b0 >> 3) & ~(uint64_t)15, sbytes - 16);
-    const uint64_t s_end = umax64(umin64((((it.b1 + 127) >> 3) + 15) & ~(uint64_t)15, sbytes), it.s0 + 16);
-    it.staged = s_end <= it.s0 + kCodeCap ? 1u : 0u;
-    it.s_len = (uint32_t)umin64(s_end - it.s0, kCodeCap);
+    it.stream = C + const_load(&r->stream_off);
+    it.raw = C + const_load(&r->raw_off);
+    it.gap = C + const_load(&r->gap_off);
+    it.cnt = C + const_load(&r->cnt_off);
+    it.out = a.outs[tl] + ((uint64_t)const_load(&r->chunk) * kChunk);
+    it.rel0 = const_load(&r->rel0);
+    it.nbits = const_load(&r->nbits);
+    const uint32_t sl = const_load(&r->s_len);
+    it.s_len = sl & ~kStagedBit;
+    it.staged = sl >> 31;
+    it.nc = const_load(&r->nc);
+    it.raw_left = const_load(&r->raw_left);
+    it.n_words = const_load(&r->n_words);
+    it.lut = tensor;
     return it;
 }
 
@@ -419,7 +406,7 @@ __device__ __forceinline__ Item load_item(const DecodeArgs &a, uint32_t item) {
 // chunk's bytes the address repeats (a cache hit, no extra HBM traffic) so
 // that the load count stays fixed.
 __device__ __forceinline__ void load_codes(const Item &it, uint32_t tid, u32x4 (&cw)[kCodeLoads]) {
-    const uint8_t *stream = it.stream + it.s0;
+    const uint8_t *stream = it.stream;
 #pragma unroll
     for (int k = 0; k < kCodeLoads; ++k) {
         const uint32_t off = min(16u * kThreads * k + 16u * tid, it.s_len - 16u);
@@ -504,20 +491,21 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         }
         if (more && nx.staged) load_codes(nx, tid, cw);
 
-        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions
-        const uint64_t b0 = it.b0, b1 = it.b1, s0 = it.s0;
+        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions.
+        //      Stream positions are bit offsets from the staged first byte.
+        const uint32_t b0 = it.rel0, b1 = it.rel0 + it.nbits;
         const uint32_t nc = it.nc;
-        const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
+        const uint32_t W = (it.nbits + kWindows - 1) / kWindows;
         uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
         const uint32_t incl = wave_inclusive_sum(na + nb);
-        const uint64_t sa = b0 + (2 * tid) * W + (na ? (win.x & 0xFFu) : 0u);
-        const uint64_t sb = b0 + (2 * tid + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
+        const uint32_t sa = b0 + (2 * tid) * W + (na ? (win.x & 0xFFu) : 0u);
+        const uint32_t sb = b0 + (2 * tid + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
         // the wave's code total and first code, for the waves above it
         const uint64_t mask = __ballot(na + nb != 0);
-        const uint64_t first = na ? sa : sb;          // this lane's first code
-        const uint64_t wf = __shfl((unsigned long long)first, mask ? (int)__builtin_ctzll(mask) : 0);
+        const uint32_t first = na ? sa : sb;          // this lane's first code
+        const uint32_t wf = __shfl(first, mask ? (int)__builtin_ctzll(mask) : 0);
         if (lane == 63) L.wave_total[wave] = incl;
-        if (lane == 0) L.wave_first[wave] = mask ? (uint32_t)(wf - b0) : 0xFFFFFFFFu;
+        if (lane == 0) L.wave_first[wave] = mask ? wf : 0xFFFFFFFFu;
         __syncthreads();
 
         uint32_t base = 0;
@@ -536,31 +524,27 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint32_t mn = wave_min(min(na, nb));
         uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 1 ? (mn - 1) / kMaxPerLookup : 0u);
 
-        // Window starts as bit offsets from s0.  Peeks at p <= pmax stay
-        // inside the source; the counted loop moves a window by at most 24*T
-        // bits, so starts are kept at or below pmax - 24*T (only a container
-        // that disagrees with its index starts higher).
-        const uint64_t sbytes = it.stream_bytes;
-        const uint32_t n_words = (uint32_t)umin64((sbytes - s0) / 4, 1u << 25);
-        const uint32_t pmax = it.staged ? 32u * (kCodeWords - 1) : 32u * (n_words - 1);
+        // Peeks at p <= pmax stay inside the source; the counted loop moves a
+        // window by at most 24*T bits, so starts are kept at or below
+        // pmax - 24*T (only a container that disagrees with its index
+        // starts higher).
+        const uint32_t pmax = it.staged ? 32u * (kCodeWords - 1) : 32u * (it.n_words - 1);
         T = min(T, pmax / 48u);
-        const uint64_t plim = pmax - 24u * T;
-        const uint64_t pra = sa - 8 * s0, prb = sb - 8 * s0;   // wrap high when below s0
-        bad |= (pra > plim) | (prb > plim);
-        Chain A{(uint32_t)umin64(pra, plim) + kPosBias, qa >> 2, (qa & 3u) << 3, 0u, qa, qa + na, 0u};
-        Chain B{(uint32_t)umin64(prb, plim) + kPosBias, qb >> 2, (qb & 3u) << 3, 0u, qb, qb + nb, 0u};
+        const uint32_t plim = pmax - 24u * T;
+        bad |= (sa > plim) | (sb > plim);
+        Chain A{min(sa, plim) + kPosBias, qa >> 2, (qa & 3u) << 3, 0u, qa, qa + na, 0u};
+        Chain B{min(sb, plim) + kPosBias, qb >> 2, (qb & 3u) << 3, 0u, qb, qb + nb, 0u};
         if (it.staged) {
             // peeks read codes[k], codes[k+1] with k = P / 32 <= kCodeWords
             const LdsCodes src{L.codes, pmax + kPosBias};
             decode_pair(L, src, A, B, T, bad);
         } else {
             // peeks read words k-1 and k of the stream from s0, k < n_words
-            const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream + s0) - 1,
-                                  pmax + kPosBias};
+            const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream) - 1, pmax + kPosBias};
             decode_pair(L, src, A, B, T, bad);
         }
-        const uint64_t ea = 8 * s0 + (A.P - kPosBias);
-        const uint64_t eb = 8 * s0 + (B.P - kPosBias);
+        const uint32_t ea = A.P - kPosBias;
+        const uint32_t eb = B.P - kPosBias;
         __syncthreads();
         write_head(L, A);
         write_head(L, B);
@@ -571,15 +555,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         {
             const uint64_t above = lane == 63 ? 0 : (mask >> (lane + 1));
             const uint32_t nxt_lane = above ? lane + 1 + (uint32_t)__builtin_ctzll(above) : lane;
-            const uint64_t nxt_first = __shfl((unsigned long long)first, (int)nxt_lane);
-            uint64_t after_b = b1;
+            const uint32_t nxt_first = __shfl(first, (int)nxt_lane);
+            uint32_t after_b = b1;
             if (above) {
                 after_b = nxt_first;
             } else {
                 for (uint32_t w = wave + 1; w < (uint32_t)kWaves; ++w) {
                     const uint32_t f = L.wave_first[w];
                     if (f != 0xFFFFFFFFu) {
-                        after_b = b0 + f;
+                        after_b = f;
                         break;
                     }
                 }

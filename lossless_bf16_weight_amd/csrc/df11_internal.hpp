@@ -64,33 +64,38 @@ struct alignas(16) LutRecord {
 };
 static_assert(sizeof(LutRecord) == 5904, "LUT record size");
 
-// Per-tensor descriptor in device memory.
-struct alignas(16) TensorDesc {
-    uint64_t n_elems;
-    uint64_t off_ci;
-    uint64_t off_gap;
-    uint64_t off_cnt;
-    uint64_t off_stream;
-    uint64_t stream_bytes;
-    uint64_t off_raw;
-    uint64_t raw_bytes;
-    uint32_t n_chunks;
-    uint32_t lut_index;
-    uint32_t pad[2];
-};
-static_assert(sizeof(TensorDesc) == 80, "descriptor size");
+// Staged code bytes per chunk: chunks whose codes (plus 127 bits of slack,
+// rounded out to 16 bytes) fit go through LDS, the others are read from
+// global memory by the decode loop.
+constexpr uint32_t kCodeCap = 13 * 1024;
 
-// Work item of a batched launch: (tensor index within the launch) << 24 | chunk.
-constexpr uint32_t kItemChunkBits = 24;
-constexpr uint32_t kItemChunkMask = (1u << kItemChunkBits) - 1;
+// One chunk of one tensor, with everything the kernel needs to find its
+// bytes, computed by the plan from the validated chunk index (the kernel
+// never reads a container's chunk index).  Offsets are relative to the
+// container's first byte.
+struct alignas(16) ChunkRec {
+    uint64_t stream_off;   // first staged stream byte (16-byte aligned)
+    uint64_t raw_off;      // raw byte of the chunk's first element
+    uint64_t gap_off;      // the chunk's 512 window gaps
+    uint64_t cnt_off;      // the chunk's 512 window counts
+    uint32_t rel0;         // chunk's first stream bit - 8 * staged first byte
+    uint32_t nbits;        // the chunk's stream bits
+    uint32_t s_len;        // staged bytes (<= kCodeCap), bit 31: codes staged in LDS
+    uint32_t nc;           // elements
+    uint32_t raw_left;     // raw bytes from the chunk's first element (<= 64 KiB)
+    uint32_t n_words;      // stream words from the staged first byte on (<= 2^25)
+    uint32_t tensor;       // plan tensor index (decode tables)
+    uint32_t chunk;        // chunk index within the tensor
+};
+static_assert(sizeof(ChunkRec) == 64, "chunk record size");
+constexpr uint32_t kStagedBit = 0x80000000u;
 
 struct DecodeArgs {
-    const TensorDesc *desc;      // plan's descriptor table (indexed by global tensor)
-    const LutRecord *luts;       // plan's table records
-    const uint32_t *work;        // work items of this launch, or nullptr
+    const ChunkRec *recs;        // the launch's chunks, in order
+    const LutRecord *luts;       // plan's table records (indexed by plan tensor)
     uint32_t *status;            // plan's corruption flag
     uint32_t n_items;
-    uint32_t tensor_base;        // global index of the launch's tensor 0
+    uint32_t tensor_base;        // plan index of the launch's tensor 0
     const uint8_t *containers[DF11_MAX_BATCH];
     uint16_t *outs[DF11_MAX_BATCH];
 };

@@ -195,7 +195,7 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
                     (unsigned long long)total_bits, (unsigned long long)n);
     M.L = layout_for(n, total_bits);
     const Layout &L = M.L;
-    if (L.n_chunks > kItemChunkMask) return fail(DF11_E_UNSUPPORTED, "%llu chunks", (unsigned long long)L.n_chunks);
+    if (L.n_chunks > (1u << 24)) return fail(DF11_E_UNSUPPORTED, "%llu chunks", (unsigned long long)L.n_chunks);
     if (rd32(c + 100) != L.n_chunks) return fail(DF11_E_FORMAT, "n_chunks field");
     if (rd64(c + 112) != L.off_ci || rd64(c + 120) != L.off_gap || rd64(c + 128) != L.off_cnt ||
         rd64(c + 136) != L.off_stream || rd64(c + 144) != L.stream_bytes ||
@@ -307,12 +307,10 @@ struct df11_plan_s {
     int n_tensors = 0;
     int n_cu = 0;
     std::vector<Meta> meta;
-    std::vector<uint64_t> batch_item_offset;  // per launch group: first work item
-    std::vector<uint32_t> batch_items;        // per launch group: items
+    std::vector<uint64_t> first_rec;   // per tensor (and one past the last): first chunk record
     void *d_block = nullptr;
-    TensorDesc *d_desc = nullptr;
+    ChunkRec *d_recs = nullptr;
     LutRecord *d_luts = nullptr;
-    uint32_t *d_work = nullptr;
     uint32_t *d_status = nullptr;
 };
 
@@ -358,44 +356,48 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
             return st;
         }
     }
-    // host images of the descriptor table, the decode tables and the work list
-    std::vector<TensorDesc> desc(n_tensors);
+    // host images of the decode tables and the chunk records (plan order)
     std::vector<LutRecord> luts(n_tensors);
-    std::vector<uint32_t> work;
+    std::vector<ChunkRec> recs;
+    p->first_rec.push_back(0);
     for (int t = 0; t < n_tensors; ++t) {
         const Layout &L = p->meta[t].L;
-        TensorDesc &d = desc[t];
-        memset(&d, 0, sizeof d);
-        d.n_elems = L.n;
-        d.off_ci = L.off_ci;
-        d.off_gap = L.off_gap;
-        d.off_cnt = L.off_cnt;
-        d.off_stream = L.off_stream;
-        d.stream_bytes = L.stream_bytes;
-        d.off_raw = L.off_raw;
-        d.raw_bytes = L.raw_bytes;
-        d.n_chunks = (uint32_t)L.n_chunks;
-        d.lut_index = (uint32_t)t;
         build_lut(p->meta[t].code_len, luts[t]);
-    }
-    for (int g = 0; g * DF11_MAX_BATCH < n_tensors; ++g) {
-        p->batch_item_offset.push_back(work.size());
-        const int t_end = std::min(n_tensors, (g + 1) * DF11_MAX_BATCH);
-        for (int t = g * DF11_MAX_BATCH; t < t_end; ++t)
-            for (uint32_t ch = 0; ch < desc[t].n_chunks; ++ch)
-                work.push_back(((uint32_t)(t - g * DF11_MAX_BATCH) << kItemChunkBits) | ch);
-        p->batch_items.push_back((uint32_t)(work.size() - p->batch_item_offset.back()));
+        const uint8_t *ci = (const uint8_t *)host_meta[t] + L.off_ci;
+        for (uint64_t ch = 0; ch < L.n_chunks; ++ch) {
+            const uint64_t b0 = rd64(ci + 16 * ch), b1 = rd64(ci + 16 * (ch + 1));
+            const uint64_t elem0 = ch * kChunk;
+            const uint64_t sb = L.stream_bytes;
+            // staged bytes: the chunk's stream bytes plus 127 bits of slack,
+            // rounded out to 16 bytes, inside the stream section
+            const uint64_t s0 = std::min<uint64_t>((b0 >> 3) & ~uint64_t(15), sb - 16);
+            const uint64_t s_end = std::max<uint64_t>(std::min<uint64_t>((((b1 + 127) >> 3) + 15) & ~uint64_t(15), sb), s0 + 16);
+            ChunkRec r;
+            memset(&r, 0, sizeof r);
+            r.stream_off = L.off_stream + s0;
+            r.raw_off = L.off_raw + elem0;
+            r.gap_off = L.off_gap + ch * kWindows;
+            r.cnt_off = L.off_cnt + ch * kWindows * 2;
+            r.rel0 = (uint32_t)(b0 - 8 * s0);
+            r.nbits = (uint32_t)(b1 - b0);
+            r.s_len = (uint32_t)std::min<uint64_t>(s_end - s0, kCodeCap) | (s_end <= s0 + kCodeCap ? kStagedBit : 0u);
+            r.nc = (uint32_t)std::min<uint64_t>(kChunk, L.n - elem0);
+            r.raw_left = (uint32_t)std::min<uint64_t>(L.raw_bytes - elem0, 2 * kChunk);
+            r.n_words = (uint32_t)std::min<uint64_t>((sb - s0) / 4, uint64_t(1) << 25);
+            r.tensor = (uint32_t)t;
+            r.chunk = (uint32_t)ch;
+            recs.push_back(r);
+        }
+        p->first_rec.push_back(recs.size());
     }
 
-    const size_t off_desc = 0;
-    const size_t off_luts = up256(off_desc + sizeof(TensorDesc) * n_tensors);
-    const size_t off_work = up256(off_luts + sizeof(LutRecord) * n_tensors);
-    const size_t off_status = up256(off_work + sizeof(uint32_t) * std::max<size_t>(1, work.size()));
+    const size_t off_recs = 0;
+    const size_t off_luts = up256(off_recs + sizeof(ChunkRec) * std::max<size_t>(1, recs.size()));
+    const size_t off_status = up256(off_luts + sizeof(LutRecord) * n_tensors);
     const size_t total = off_status + 256;
     std::vector<uint8_t> image(total, 0);
-    memcpy(image.data() + off_desc, desc.data(), sizeof(TensorDesc) * n_tensors);
+    if (!recs.empty()) memcpy(image.data() + off_recs, recs.data(), sizeof(ChunkRec) * recs.size());
     memcpy(image.data() + off_luts, luts.data(), sizeof(LutRecord) * n_tensors);
-    if (!work.empty()) memcpy(image.data() + off_work, work.data(), sizeof(uint32_t) * work.size());
 
     DeviceGuard guard(hip_device);
     if (guard.err != hipSuccess) { delete p; return fail(DF11_E_HIP, "hipSetDevice(%d): %s", hip_device, hipGetErrorString(guard.err)); }
@@ -412,9 +414,8 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
         return fail(DF11_E_HIP, "hipMemcpy: %s", hipGetErrorString(e));
     }
     uint8_t *base = (uint8_t *)p->d_block;
-    p->d_desc = (TensorDesc *)(base + off_desc);
+    p->d_recs = (ChunkRec *)(base + off_recs);
     p->d_luts = (LutRecord *)(base + off_luts);
-    p->d_work = (uint32_t *)(base + off_work);
     p->d_status = (uint32_t *)(base + off_status);
     *out = p;
     return DF11_OK;
@@ -455,9 +456,8 @@ extern "C" df11_status df11_decode(df11_plan_t p, int tensor, const void *d_cont
     if (n_chunks == 0) return DF11_OK;
     DecodeArgs a;
     memset(&a, 0, sizeof a);
-    a.desc = p->d_desc;
+    a.recs = p->d_recs + p->first_rec[tensor];
     a.luts = p->d_luts;
-    a.work = nullptr;
     a.status = p->d_status;
     a.n_items = n_chunks;
     a.tensor_base = (uint32_t)tensor;
@@ -478,17 +478,17 @@ extern "C" df11_status df11_decode_batch(df11_plan_t p, const void *const *d_con
     }
     DeviceGuard guard(p->device);
     if (guard.err != hipSuccess) return fail(DF11_E_HIP, "hipSetDevice: %s", hipGetErrorString(guard.err));
-    for (size_t g = 0; g < p->batch_items.size(); ++g) {
-        if (!p->batch_items[g]) continue;
+    for (int g = 0; g * DF11_MAX_BATCH < p->n_tensors; ++g) {
+        const int t_end = std::min(p->n_tensors, (g + 1) * DF11_MAX_BATCH);
+        const uint64_t r0 = p->first_rec[g * DF11_MAX_BATCH], r1 = p->first_rec[t_end];
+        if (r1 == r0) continue;
         DecodeArgs a;
         memset(&a, 0, sizeof a);
-        a.desc = p->d_desc;
+        a.recs = p->d_recs + r0;
         a.luts = p->d_luts;
-        a.work = p->d_work + p->batch_item_offset[g];
         a.status = p->d_status;
-        a.n_items = p->batch_items[g];
+        a.n_items = (uint32_t)(r1 - r0);
         a.tensor_base = (uint32_t)(g * DF11_MAX_BATCH);
-        const int t_end = std::min(p->n_tensors, (int)(g + 1) * DF11_MAX_BATCH);
         for (int t = (int)g * DF11_MAX_BATCH; t < t_end; ++t) {
             a.containers[t - g * DF11_MAX_BATCH] = (const uint8_t *)d_containers[t];
             a.outs[t - g * DF11_MAX_BATCH] = (uint16_t *)d_outs[t];
