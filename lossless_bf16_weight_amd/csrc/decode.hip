@@ -276,17 +276,37 @@ __device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent, bool active
 
 __device__ __forceinline__ uint32_t out_pos(const Chain &c) { return (c.dw << 2) + (c.f8 >> 3); }
 
-// Bits taken by the first n codes of an entry (n <= its count).
-__device__ __forceinline__ uint32_t entry_bits(const Lds &L, uint32_t ent, uint32_t n) {
-    if (n >= ent_count(ent)) return ent_bits(ent);
-    uint32_t c = 0;
-    for (uint32_t k = 0; k < n; ++k) c += L.lut.len[(ent >> (8 * k)) & 0xFFu];
-    return c;
-}
-
 __device__ __forceinline__ void flush_tail(Lds &L, const Chain &c) {
     if (c.qe > c.q0 && (c.dw << 2) < c.qe && c.dw != (c.q0 >> 2))
         *reinterpret_cast<uint32_t *>(L.tile + tile_off(c.dw)) = c.acc;
+}
+
+template <bool kHead, class Src>
+__device__ __forceinline__ void masked_tail(Lds &L, const Src &src, Chain &A, Chain &B, int32_t &ra,
+                                            int32_t &rb, uint32_t &ea_r, uint32_t &eb_r, uint32_t &bad) {
+    uint32_t ea, eb;
+    bool any = __ballot((ra > 0) | (rb > 0)) != 0;
+    while (any) {
+        const bool aa = ra > 0, ab = rb > 0;
+        entries<true>(L, src, A.P, B.P, ea, eb, bad);
+        ea = aa ? ea : 0u;
+        eb = ab ? eb : 0u;
+        ea_r = aa ? ea : ea_r;
+        eb_r = ab ? eb : eb_r;
+        ra -= (int32_t)ent_count(ea);
+        rb -= (int32_t)ent_count(eb);
+        step<kHead, true>(L, A, ea, aa);
+        step<kHead, true>(L, B, eb, ab);
+        any = __ballot((ra > 0) | (rb > 0)) != 0;
+    }
+}
+
+// Bits taken by the last k codes of an entry (k < its count).
+__device__ __forceinline__ uint32_t trailing_bits(const Lds &L, uint32_t ent, uint32_t k) {
+    uint32_t c = 0;
+    const uint32_t n = ent_count(ent);
+    for (uint32_t j = n - k; j < n; ++j) c += L.lut.len[(ent >> (8 * j)) & 0xFFu];
+    return c;
 }
 
 // Decode both windows of this lane.  T: look-ups after which no window of
@@ -310,31 +330,18 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
         step<false>(L, A, ea);
         step<false>(L, B, eb);
     }
-    // 2. masked, without branches: a finished window stores to the dummy
-    //    dword and keeps its state; the state before each window's last
-    //    look-up is kept to find where its last code ends
+    // 2. masked, without branches: a finished window takes a zero entry
+    //    (it stores to the dummy dword and keeps its state); each window's
+    //    last entry is kept to find where its last code ends
     int32_t ra = (int32_t)(A.qe - out_pos(A)), rb = (int32_t)(B.qe - out_pos(B));
-    uint32_t pa_r = A.P, ra_r = 0, ea_r = 0, pb_r = B.P, rb_r = 0, eb_r = 0;
-    bool any = __ballot((ra > 0) | (rb > 0)) != 0;
-    while (any) {
-        const bool aa = ra > 0, ab = rb > 0;
-        entries<true>(L, src, A.P, B.P, ea, eb, bad);
-        ea = aa ? ea : 0u;
-        eb = ab ? eb : 0u;
-        pa_r = aa ? A.P : pa_r;
-        ra_r = aa ? (uint32_t)ra : ra_r;
-        ea_r = aa ? ea : ea_r;
-        pb_r = ab ? B.P : pb_r;
-        rb_r = ab ? (uint32_t)rb : rb_r;
-        eb_r = ab ? eb : eb_r;
-        ra -= (int32_t)ent_count(ea);
-        rb -= (int32_t)ent_count(eb);
-        step<true, true>(L, A, ea, aa);
-        step<true, true>(L, B, eb, ab);
-        any = __ballot((ra > 0) | (rb > 0)) != 0;
-    }
-    if (A.qe > A.q0) A.P = pa_r + entry_bits(L, ea_r, ra_r);
-    if (B.qe > B.q0) B.P = pb_r + entry_bits(L, eb_r, rb_r);
+    uint32_t ea_r = 0, eb_r = 0;
+    if (T >= 4u)
+        masked_tail<false>(L, src, A, B, ra, rb, ea_r, eb_r, bad);
+    else
+        masked_tail<true>(L, src, A, B, ra, rb, ea_r, eb_r, bad);
+    // the last entry took -r codes past the window's end
+    A.P -= trailing_bits(L, ea_r, (uint32_t)(-ra));
+    B.P -= trailing_bits(L, eb_r, (uint32_t)(-rb));
     // 3. a last look-up that crossed into a new dword left that dword's
     //    bytes in acc: store them when the window reaches into it (and it is
     //    not the window's first dword)
@@ -446,20 +453,25 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     u32x2 rw[kBlocks];
     u32x2 win;
     {
+        // (in the order the loop issues them: windows, codes, raw bytes;
+        // the compiler's wait counts assume the same order on every path)
         const Item it = load_item(a, begin);
-        if (it.staged) load_codes(it, tid, cw);
+        win = load_windows(it, tid);
+        load_codes(it, tid, cw);
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) rw[b] = load_raw(it, tid, b);
-        win = load_windows(it, tid);
     }
 
     for (uint32_t item = begin; item < end; ++item) {
         // (items are re-read from the work list, not carried over: the
         // scalar cache holds them)
         const Item it = load_item(a, item);
+        // the next item (the last one re-reads itself: the loads stay
+        // unconditional, so the compiler can count them and wait for the
+        // oldest ones only)
         const bool more = item + 1 < end;
         const Item nx = load_item(a, more ? item + 1 : item);
-        const u32x2 win_nx = more ? load_windows(nx, tid) : win;
+        const u32x2 win_nx = load_windows(nx, tid);
 
         // ---- the previous item's tile and staged words are no longer read
         __syncthreads();
@@ -489,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
                 }
             }
         }
-        if (more && nx.staged) load_codes(nx, tid, cw);
+        load_codes(nx, tid, cw);
 
         // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions.
         //      Stream positions are bit offsets from the staged first byte.
@@ -586,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
                                        *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
                 __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
             }
-            if (more) rw[b] = load_raw(nx, tid, b);
+            rw[b] = load_raw(nx, tid, b);
         }
         // ---- the ragged last block of a tensor (raw bytes fetched again)
         if (full * kBlockElems < nc) {
