@@ -11,11 +11,11 @@
  * bit.  The weights stay compressed in GPU memory and are decoded on the GPU
  * when they are needed (mlx-dfloat project page, introduction).
  *
- * Container version 2 (one tensor = one container = one code table; all
+ * Container version 3 (one tensor = one container = one code table; all
  * integers little-endian; every section starts on a 256-byte boundary):
  *
  *   header (512 bytes)
- *      0 char[8] magic "DF11HIPC"    8 u32 version = 2      12 u32 flags = 0
+ *      0 char[8] magic "DF11HIPC"    8 u32 version = 3      12 u32 flags = 0
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
  *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 0
  *     98 u16 windows = 512         100 u32 n_chunks       104 u64 total_bits
@@ -39,9 +39,10 @@
  * symbol) get consecutive values, the first is 0 (the deflate construction).
  *
  * Chunks: element j of the tensor is in chunk j / 32768.  Chunk c owns the
- * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]).  Its bits are cut in
- * 512 windows of W = ceil((b1 - b0) / 512) bits: window i is
- * [b0 + i*W, min(b0 + (i+1)*W, b1)).  cnt[c][i] counts the codes that START in
+ * stream bits [b0, b1) = [start_bit[c], start_bit[c+1]), N = b1 - b0 bits.
+ * They are cut into 512 windows as evenly as integers allow: window i is
+ * [b0 + floor(i*N/512), b0 + floor((i+1)*N/512)), so every window has
+ * floor(N/512) or ceil(N/512) bits.  cnt[c][i] counts the codes that START in
  * window i; gap[c][i] is the offset of the first of them from the window
  * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
  * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
@@ -109,7 +110,7 @@ df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info 
 /* Size bound of the container for n elements (any data). */
 uint64_t df11_container_bound(uint64_t n_elems);
 
-/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-2
+/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-3
  * container in HOST memory `out` (capacity `out_cap`, at least
  * df11_container_bound(n)).  dims[ndim] is the shape (ndim <= 8, product =
  * n; ndim = 0 means a scalar, n = 1).  `threads` = 0 uses every hardware

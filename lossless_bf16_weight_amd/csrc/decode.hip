@@ -68,9 +68,11 @@ struct Lds {
     uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
     uint8_t tile[kTilePadded + 16];
     LutRecord lut;
-    // the chunk records of the current and the next work item (slot = item
-    // parity), copied in by wave 0 one item ahead
+    // the chunk records of the current and the next work item (slot =
+    // iteration parity), copied in by wave 0 one item ahead, and their item
+    // numbers (n_items or more: no item; the record is then item n_items-1's)
     uint32_t rec[2][16];
+    uint32_t rec_id[2];
     // per wave: bit offset from the chunk start of the first code of its
     // first non-empty window (~0: all its windows are empty), and the number
     // of codes its windows hold
@@ -270,7 +272,7 @@ __device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent, bool active
     }
     if (kMasked) addr = active ? addr : kDummy;
     *reinterpret_cast<uint32_t *>(L.tile + addr) = lo;
-    const uint32_t f8n = c.f8 + (ent_count(ent) << 3);
+    const uint32_t f8n = (__builtin_amdgcn_ubfe(ent, kEntCountShift, 3) << 3) + c.f8;
     const bool crossed = f8n >= 32u;
     c.acc = crossed ? (uint32_t)(x >> 32) : lo;
     c.dw += crossed ? 1u : 0u;
@@ -313,6 +315,47 @@ __device__ __forceinline__ uint32_t trailing_bits(const Lds &L, uint32_t ent, ui
     return c;
 }
 
+// The code words a chain's peeks read, in registers: w0, w1 = staged words
+// k, k+1 with k = P / 32.  Each look-up also reads word k+2, with its table
+// entry, and shifts it in when the look-up moves the chain into the next
+// word; so a look-up waits on one LDS round trip (the table entry and that
+// word together) instead of two in a row.
+struct Window {
+    uint32_t w0, w1;
+};
+
+__device__ __forceinline__ Window window_at(const uint32_t *w, uint32_t P) {
+    const uint32_t k = P >> 5;
+    return Window{w[k], w[k + 1]};
+}
+
+// One counted look-up of both chains from their register windows.
+template <bool kHead>
+__device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &wa, Window &wb,
+                                            uint32_t &bad) {
+    const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
+    const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
+    const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
+    uint32_t ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
+    uint32_t eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
+    const uint32_t na = L.codes[(A.P >> 5) + 2];
+    const uint32_t nb = L.codes[(B.P >> 5) + 2];
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
+        if (ea == 0) ea = long_entry(L.lut, ta, bad);
+        if (eb == 0) eb = long_entry(L.lut, tb, bad);
+    }
+    // a look-up takes fewer than 32 bits, so it moves a chain at most one word
+    const bool ca = (A.P | 31u) < A.P + ent_bits(ea);
+    const bool cb = (B.P | 31u) < B.P + ent_bits(eb);
+    wa.w0 = ca ? wa.w1 : wa.w0;
+    wa.w1 = ca ? na : wa.w1;
+    wb.w0 = cb ? wb.w1 : wb.w0;
+    wb.w1 = cb ? nb : wb.w1;
+    step<kHead>(L, A, ea);
+    step<kHead>(L, B, eb);
+}
+
 // Decode both windows of this lane.  T: look-ups after which no window of
 // the wave has run out of codes.  On return A.P / B.P hold the stream
 // positions (plus kPosBias) where the windows' last codes end.
@@ -324,15 +367,23 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
     //    source's end, so these peeks need no clamp); a chain leaves its
     //    window's first dword within four look-ups
     uint32_t t = 0;
-    for (; t < T && t < 4u; ++t) {
-        entries<false>(L, src, A.P, B.P, ea, eb, bad);
-        step<true>(L, A, ea);
-        step<true>(L, B, eb);
-    }
-    for (; t < T; ++t) {
-        entries<false>(L, src, A.P, B.P, ea, eb, bad);
-        step<false>(L, A, ea);
-        step<false>(L, B, eb);
+    if constexpr (Src::kLds) {
+        Window wa = window_at(src.w, A.P), wb = window_at(src.w, B.P);
+        // (the loop then starts with no LDS read in flight)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        for (; t < T && t < 4u; ++t) window_step<true>(L, A, B, wa, wb, bad);
+        for (; t < T; ++t) window_step<false>(L, A, B, wa, wb, bad);
+    } else {
+        for (; t < T && t < 4u; ++t) {
+            entries<false>(L, src, A.P, B.P, ea, eb, bad);
+            step<true>(L, A, ea);
+            step<true>(L, B, eb);
+        }
+        for (; t < T; ++t) {
+            entries<false>(L, src, A.P, B.P, ea, eb, bad);
+            step<false>(L, A, ea);
+            step<false>(L, B, eb);
+        }
     }
     // 2. masked, without branches: a finished window takes a zero entry
     //    (it stores to the dummy dword and keeps its state); each window's
@@ -432,8 +483,33 @@ __device__ __forceinline__ u32x4 fetch_rec(const DecodeArgs &a, uint32_t item, u
     return reinterpret_cast<const u32x4 *>(a.recs + item)[lane & 3u];
 }
 // ... and later puts it in its LDS slot.
-__device__ __forceinline__ void put_rec(Lds &L, uint32_t slot, u32x4 v, uint32_t lane) {
+__device__ __forceinline__ void put_rec(Lds &L, uint32_t slot, u32x4 v, uint32_t id, uint32_t lane) {
     if (lane < 4u) reinterpret_cast<u32x4 *>(L.rec[slot])[lane] = v;
+    if (lane == 0) L.rec_id[slot] = id;
+}
+
+// Wave 0: the next ticket of the launch (lane 0 takes it, every lane gets
+// it).  Tickets count on from gridDim.x: workgroup w's first item is w.
+__device__ __forceinline__ uint32_t take_ticket(const DecodeArgs &a, uint32_t lane) {
+    uint32_t t = 0;
+    if (lane == 0) t = atomicAdd(a.work, 1u);
+    return gridDim.x + __builtin_amdgcn_readfirstlane(t);
+}
+
+// The decode tables of a tensor, 16 bytes per lane per 4 KiB.
+constexpr int kLutLoads = (int)((sizeof(LutRecord) / 16 + kThreads - 1) / kThreads);
+static_assert(sizeof(LutRecord) % 16 == 0, "table record size");
+__device__ __forceinline__ void load_lut(const DecodeArgs &a, uint32_t lut, uint32_t tid, u32x4 (&lr)[kLutLoads]) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + lut);
+#pragma unroll
+    for (int k = 0; k < kLutLoads; ++k)
+        lr[k] = src[min(kThreads * k + tid, (uint32_t)(sizeof(LutRecord) / 16 - 1))];
+}
+__device__ __forceinline__ void put_lut(Lds &L, uint32_t tid, const u32x4 (&lr)[kLutLoads]) {
+    u32x4 *dst = reinterpret_cast<u32x4 *>(&L.lut);
+#pragma unroll
+    for (int k = 0; k < kLutLoads; ++k)
+        if (kThreads * k + tid < sizeof(LutRecord) / 16) dst[kThreads * k + tid] = lr[k];
 }
 
 // The staged code bytes of an item: 16 bytes per lane per 4 KiB.  Past the
@@ -468,54 +544,50 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     __shared__ Lds L;
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u, wave = tid >> 6;
-    const uint32_t begin = (uint32_t)((uint64_t)a.n_items * blockIdx.x / gridDim.x);
-    const uint32_t end = (uint32_t)((uint64_t)a.n_items * (blockIdx.x + 1) / gridDim.x);
-    uint32_t cur_lut = 0xFFFFFFFFu;
+    const uint32_t n = a.n_items;   // >= gridDim.x
     uint32_t bad_any = 0;
-    if (begin >= end) return;
 
     // Software pipeline over the workgroup's items: while item i is
-    // assembled, the code bytes of item i+1 are in flight, and its raw bytes
-    // are requested block by block as item i's assembly frees the registers.
+    // assembled, the code bytes and decode tables of item i+1 are in flight,
+    // and its raw bytes are requested block by block as item i's assembly
+    // frees the registers.  Items come from the launch's ticket counter, two
+    // ahead, so that workgroups that run faster take more of them.
     u32x4 cw[kCodeLoads];
     u32x2 rw[kBlocks];
+    u32x4 lr[kLutLoads];
     u32x2 win;
     if (wave == 0) {
-        const u32x4 r0 = fetch_rec(a, begin, lane);
-        const u32x4 r1 = fetch_rec(a, min(begin + 1, end - 1), lane);
-        put_rec(L, begin & 1u, r0, lane);
-        put_rec(L, (begin + 1) & 1u, r1, lane);
+        const uint32_t i0 = blockIdx.x;
+        const u32x4 r0 = fetch_rec(a, min(i0, n - 1), lane);
+        put_rec(L, 0, r0, i0, lane);
     }
     __syncthreads();
     {
-        // (in the order the loop issues them: windows, codes, raw bytes;
-        // the compiler's wait counts assume the same order on every path)
-        const Item it = item_at(a, L, begin & 1u);
+        // (in the order the loop issues them: windows, codes, tables, raw
+        // bytes; the compiler's wait counts assume the same order on every
+        // path)
+        const Item it = item_at(a, L, 0);
         win = load_windows(it, tid);
         load_codes(it, tid, cw);
+        load_lut(a, it.lut, tid, lr);
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) rw[b] = load_raw(it, tid, b);
+        put_lut(L, tid, lr);
     }
 
-    for (uint32_t item = begin; item < end; ++item) {
+    for (uint32_t k = 0;; ++k) {
         // ---- the previous item's tile and staged words are no longer
-        //      read; this item's and the next one's records are in LDS
+        //      read; this item's and the next one's records and this
+        //      item's tables are in LDS
         __syncthreads();
-        const Item it = item_at(a, L, item & 1u);
-        // the next item (the last one re-reads itself: the loads stay
-        // unconditional, so the compiler can count them and wait for the
-        // oldest ones only)
-        const Item nx = item_at(a, L, (item + 1) & 1u);
-        const u32x2 win_nx = load_windows(nx, tid);
-
-        // ---- decode tables of this tensor -> LDS
-        const uint32_t lut = it.lut;
-        if (lut != cur_lut) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + lut);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(&L.lut);
-            for (uint32_t i = tid; i < sizeof(LutRecord) / 16; i += kThreads) dst[i] = src[i];
-            cur_lut = lut;
-        }
+        const uint32_t sl = k & 1u;
+        if (__builtin_amdgcn_readfirstlane(L.rec_id[sl]) >= n) break;
+        const Item it = item_at(a, L, sl);
+        // the next item (with none, item n-1 is loaded again: the loads
+        // stay unconditional, so the compiler can count them and wait for
+        // the oldest ones only)
+        uint32_t t1 = n;
+        if (wave == 0) t1 = take_ticket(a, lane);
 
         // ---- the staged words to LDS (every tile byte of the chunk gets
         //      written by the decode, so the tile needs no clearing)
@@ -537,11 +609,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         //      Stream positions are bit offsets from the staged first byte.
         const uint32_t b0 = it.rel0, b1 = it.rel0 + it.nbits;
         const uint32_t nc = it.nc;
-        const uint32_t W = (it.nbits + kWindows - 1) / kWindows;
         uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
         const uint32_t incl = wave_inclusive_sum(na + nb);
-        const uint32_t sa = b0 + (2 * tid) * W + (na ? (win.x & 0xFFu) : 0u);
-        const uint32_t sb = b0 + (2 * tid + 1) * W + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
+        const uint32_t sa = b0 + window_edge(it.nbits, 2 * tid) + (na ? (win.x & 0xFFu) : 0u);
+        const uint32_t sb = b0 + window_edge(it.nbits, 2 * tid + 1) + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
         // the wave's code total and first code, for the waves above it
         const uint64_t mask = __ballot(na + nb != 0);
         const uint32_t first = na ? sa : sb;          // this lane's first code
@@ -550,6 +621,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         if (lane == 0) L.wave_first[wave] = mask ? wf : 0xFFFFFFFFu;
         __syncthreads();
 
+        u32x4 r1;
+        if (wave == 0) r1 = fetch_rec(a, min(t1, n - 1), lane);
         uint32_t base = 0;
         for (uint32_t w = 0; w < wave; ++w) base += L.wave_total[w];
         const uint32_t qa = base + incl - na - nb;
@@ -587,6 +660,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         }
         const uint32_t ea = A.P - kPosBias;
         const uint32_t eb = B.P - kPosBias;
+        if (wave == 0) put_rec(L, sl ^ 1u, r1, t1, lane);
         __syncthreads();
         write_head(L, A);
         write_head(L, B);
@@ -620,9 +694,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         //      Wave 0 fetches the record after next meanwhile.
         //      The next item's code bytes are requested first: they are
         //      needed first.
+        const Item nx = item_at(a, L, sl ^ 1u);
+        const u32x2 win_nx = load_windows(nx, tid);
         load_codes(nx, tid, cw);
-        u32x4 r2;
-        if (wave == 0) r2 = fetch_rec(a, min(item + 2, end - 1), lane);
+        load_lut(a, nx.lut, tid, lr);
         uint16_t *o = it.out;
         const uint32_t full = nc / kBlockElems;
 #pragma unroll
@@ -655,10 +730,17 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
                 }
             }
         }
-        if (wave == 0) put_rec(L, item & 1u, r2, lane);
+        // the next item's tables (nothing reads them during the assembly)
+        put_lut(L, tid, lr);
         win = win_nx;
     }
     if (__ballot(bad_any) && lane == 0) atomicOr(a.status, 1u);
+    // The last workgroup to finish (every ticket of the launch has been
+    // taken by then) clears the counter for the slot's next launch.
+    if (tid == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
+        atomicExch(a.work, 0u);
+        atomicExch(a.work + 1, 0u);
+    }
 }
 
 hipError_t launch_decode(const DecodeArgs &args, int grid, hipStream_t stream) {

@@ -6,8 +6,8 @@
 
 namespace df11 {
 
-// Container version 2 constants (layout documented in include/df11.h).
-constexpr uint32_t kVersion = 2;
+// Container version 3 constants (layout documented in include/df11.h).
+constexpr uint32_t kVersion = 3;
 constexpr uint32_t kHeader = DF11_HEADER_BYTES;
 constexpr uint32_t kChunk = DF11_CHUNK_ELEMS;
 constexpr int kWindows = DF11_WINDOWS;
@@ -25,6 +25,13 @@ constexpr int kMaxLen = DF11_MAX_CODE_LEN;
 #endif
 DF11_HD constexpr uint8_t rot_exp(unsigned e) {
     return (uint8_t)(((e >> 1) | (e << 7)) & 0xFFu);
+}
+
+// First bit of window i (0 <= i <= kWindows) of a chunk of nbits bits,
+// counted from the chunk's first bit: the windows split the chunk's bits as
+// evenly as integers allow.  (nbits <= 24 * kChunk, so i * nbits < 2^32.)
+DF11_HD constexpr uint32_t window_edge(uint32_t nbits, uint32_t i) {
+    return (i * nbits) / (uint32_t)kWindows;
 }
 
 // First-level decode table: indexed by the next kL1Bits bits of the stream,
@@ -90,10 +97,20 @@ struct alignas(16) ChunkRec {
 static_assert(sizeof(ChunkRec) == 64, "chunk record size");
 constexpr uint32_t kStagedBit = 0x80000000u;
 
+// Work tickets.  A launch's workgroups take its chunks in order from a
+// ticket counter: work[0] = tickets handed out past the first gridDim.x,
+// work[1] = workgroups finished; the last workgroup to finish puts both back
+// to zero.  A plan holds kWorkSlots counters, 64 bytes apart, and gives them
+// to its launches in turn, so launches of one plan overlap safely while
+// fewer than kWorkSlots launches of it are issued in between.
+constexpr uint32_t kWorkSlots = 64;
+constexpr uint32_t kWorkStride = 16;   // uint32 per counter slot
+
 struct DecodeArgs {
     const ChunkRec *recs;        // the launch's chunks, in order
     const LutRecord *luts;       // plan's table records (indexed by plan tensor)
     uint32_t *status;            // plan's corruption flag
+    uint32_t *work;              // this launch's ticket counter slot
     uint32_t n_items;
     uint32_t tensor_base;        // plan index of the launch's tensor 0
     const uint8_t *containers[DF11_MAX_BATCH];

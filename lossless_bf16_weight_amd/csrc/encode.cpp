@@ -1,4 +1,4 @@
-// libdf11 encoder: BF16 words -> version-2 container (layout in include/df11.h),
+// libdf11 encoder: BF16 words -> version-3 container (layout in include/df11.h),
 // multi-threaded on the host.
 //
 // Method: mlx-dfloat project page, introduction and 16-bit weight diagram --
@@ -207,7 +207,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         thread_local std::vector<uint8_t> buf;
         const uint64_t lo = c * kChunk, hi = std::min<uint64_t>(n, lo + kChunk);
         const uint64_t b0 = start[c], b1 = start[c + 1];
-        const uint64_t W = (b1 - b0 + kWindows - 1) / kWindows;
+        const uint32_t nbits = (uint32_t)(b1 - b0);
         const unsigned head = (unsigned)(b0 & 7);
         const uint64_t nbytes = (head + (b1 - b0) + 7) / 8;
         buf.assign(nbytes + 8, 0);
@@ -217,10 +217,11 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         uint64_t acc = 0;   // pending bits, right-aligned
         unsigned nacc = head;
         uint64_t at = 0, pos = 0;   // output byte, chunk-relative bit position
+        unsigned win = 0;           // the window holding bit pos
         for (uint64_t j = lo; j < hi; ++j) {
             const unsigned e = (w[j] >> 7) & 0xFF;
-            const unsigned win = (unsigned)(pos / W);
-            if (cnt[win]++ == 0) gap[win] = (uint8_t)(pos - win * W);
+            while (win + 1 < (unsigned)kWindows && window_edge(nbits, win + 1) <= pos) ++win;
+            if (cnt[win]++ == 0) gap[win] = (uint8_t)(pos - window_edge(nbits, win));
             acc = (acc << len[e]) | code[e];
             nacc += len[e];
             pos += len[e];

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -242,13 +243,13 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
         const uint64_t elems = std::min<uint64_t>(kChunk, n - ch * kChunk);
         if (sb > b1 || b1 - sb < elems || b1 - sb > elems * kMaxLen)
             return fail(DF11_E_FORMAT, "chunk %llu bit range", (unsigned long long)ch);
-        const uint64_t W = (b1 - sb + kWindows - 1) / kWindows;
+        const uint32_t nbits = (uint32_t)(b1 - sb);   // <= 24 * kChunk, checked above
         uint64_t sum = 0;
         for (int i = 0; i < kWindows; ++i) {
             const unsigned gap = c[L.off_gap + ch * kWindows + i];
             const unsigned cnt = rd16(c + L.off_cnt + ch * kWindows * 2 + 2 * i);
             sum += cnt;
-            const uint64_t ws = sb + i * W, we = std::min<uint64_t>(sb + (i + 1) * W, b1);
+            const uint64_t ws = sb + window_edge(nbits, i), we = sb + window_edge(nbits, i + 1);
             if (cnt == 0) {
                 if (gap != 0xFF) return fail(DF11_E_FORMAT, "chunk %llu window %d: gap without codes", (unsigned long long)ch, i);
                 continue;
@@ -312,6 +313,8 @@ struct df11_plan_s {
     ChunkRec *d_recs = nullptr;
     LutRecord *d_luts = nullptr;
     uint32_t *d_status = nullptr;
+    uint32_t *d_work = nullptr;              // kWorkSlots ticket counters
+    std::atomic<uint32_t> launches{0};       // picks each launch's counter slot
 };
 
 namespace {
@@ -328,6 +331,11 @@ struct DeviceGuard {
         if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
     }
 };
+
+uint32_t *next_work_slot(df11_plan_s *p) {
+    const uint32_t k = p->launches.fetch_add(1, std::memory_order_relaxed) % kWorkSlots;
+    return p->d_work + kWorkStride * k;
+}
 
 int grid_for(const df11_plan_s *p, uint64_t items) {
     const uint64_t resident = (uint64_t)p->n_cu * (uint64_t)decode_wgs_per_cu();
@@ -394,7 +402,8 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
     const size_t off_recs = 0;
     const size_t off_luts = up256(off_recs + sizeof(ChunkRec) * std::max<size_t>(1, recs.size()));
     const size_t off_status = up256(off_luts + sizeof(LutRecord) * n_tensors);
-    const size_t total = off_status + 256;
+    const size_t off_work = off_status + 256;
+    const size_t total = off_work + sizeof(uint32_t) * kWorkStride * kWorkSlots;
     std::vector<uint8_t> image(total, 0);
     if (!recs.empty()) memcpy(image.data() + off_recs, recs.data(), sizeof(ChunkRec) * recs.size());
     memcpy(image.data() + off_luts, luts.data(), sizeof(LutRecord) * n_tensors);
@@ -417,6 +426,7 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
     p->d_recs = (ChunkRec *)(base + off_recs);
     p->d_luts = (LutRecord *)(base + off_luts);
     p->d_status = (uint32_t *)(base + off_status);
+    p->d_work = (uint32_t *)(base + off_work);
     *out = p;
     return DF11_OK;
 }
@@ -459,6 +469,7 @@ extern "C" df11_status df11_decode(df11_plan_t p, int tensor, const void *d_cont
     a.recs = p->d_recs + p->first_rec[tensor];
     a.luts = p->d_luts;
     a.status = p->d_status;
+    a.work = next_work_slot(p);
     a.n_items = n_chunks;
     a.tensor_base = (uint32_t)tensor;
     a.containers[0] = (const uint8_t *)d_container;
@@ -487,6 +498,7 @@ extern "C" df11_status df11_decode_batch(df11_plan_t p, const void *const *d_con
         a.recs = p->d_recs + r0;
         a.luts = p->d_luts;
         a.status = p->d_status;
+        a.work = next_work_slot(p);
         a.n_items = (uint32_t)(r1 - r0);
         a.tensor_base = (uint32_t)(g * DF11_MAX_BATCH);
         for (int t = (int)g * DF11_MAX_BATCH; t < t_end; ++t) {

@@ -117,7 +117,7 @@ def canonical_codes(lengths) -> np.ndarray:
 
 
 def encode(words: np.ndarray, shape=None) -> np.ndarray:
-    """Encode a uint16 array (BF16 bit patterns) into a version-2 container."""
+    """Encode a uint16 array (BF16 bit patterns) into a version-3 container."""
     w = np.ascontiguousarray(words, dtype=np.uint16).reshape(-1)
     shape = tuple(words.shape) if shape is None else tuple(shape)
     dims = np.array(shape if shape else (0,), dtype=np.uint64)
@@ -171,7 +171,7 @@ def check(container: np.ndarray) -> int:
     return int(lib().oracle_check(_p(c, ctypes.c_uint8), c.size))
 
 
-# ---- header fields of a version-2 container (layout in df11_oracle.c) ----
+# ---- header fields of a version-3 container (layout in df11_oracle.c) ----
 
 def header(container: np.ndarray) -> dict:
     c = np.ascontiguousarray(container, dtype=np.uint8)

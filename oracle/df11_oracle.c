@@ -29,11 +29,13 @@
  *    0 is the first bit;
  *  - raw byte: (sign << 7) | fraction, i.e. ((w >> 8) & 0x80) | (w & 0x7F);
  *  - chunks of 32768 elements (64 KiB of BF16 output), each with its start
- *    bit; 512 equal-bit windows per chunk with (gap, cnt) per window.
+ *    bit; the N bits of a chunk are cut into 512 windows as evenly as
+ *    integers allow (window i starts floor(i * N / 512) bits after the
+ *    chunk's first bit), with (gap, cnt) per window.
  *
- * Container version 2 (all integers little-endian, sections 256-byte aligned):
+ * Container version 3 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
- *     0  char[8] magic "DF11HIPC"     8  u32 version (2)   12 u32 flags (0)
+ *     0  char[8] magic "DF11HIPC"     8  u32 version (3)   12 u32 flags (0)
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
  *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 reserved
  *    98  u16 windows                100  u32 n_chunks     104 u64 total_bits
@@ -57,7 +59,7 @@
 #define CAP 24
 #define CHUNK 32768u
 #define WINDOWS 512
-#define VERSION 2
+#define VERSION 3
 #define HDR 512u
 
 /* ------------------------------------------------------------------ */
@@ -214,6 +216,11 @@ uint64_t oracle_container_bound(uint64_t n) {
     return L.total;
 }
 
+/* First bit of window i (0 <= i <= 512) of a chunk of N bits, counted from
+ * the chunk's first bit: the windows split the N bits as evenly as integers
+ * allow (every window has floor(N/512) or ceil(N/512) bits). */
+static uint64_t window_edge(uint64_t N, uint64_t i) { return i * N / WINDOWS; }
+
 static void put_bit(uint8_t *stream, uint64_t pos, unsigned bit) {
     if (bit) stream[pos / 8] |= (uint8_t)(0x80u >> (pos % 8));
 }
@@ -286,23 +293,24 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u64(out + L.off_ci + L.n_chunks * 16, total_bits);
     put_u64(out + L.off_ci + L.n_chunks * 16 + 8, n);
 
-    /* 5. window index: 512 windows of W = ceil(chunk bits / 512) bits; per
-     *    window the offset of its first code start and the number of code
-     *    starts */
+    /* 5. window index: the chunk's bits cut into 512 windows (window_edge);
+     *    per window the offset of its first code start from the window's
+     *    first bit and the number of code starts */
     for (uint64_t c = 0; c < L.n_chunks; c++) {
         uint64_t b0 = get_u64(out + L.off_ci + c * 16);
         uint64_t b1 = get_u64(out + L.off_ci + (c + 1) * 16);
-        uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
         uint8_t *gap = out + L.off_gap + c * WINDOWS;
         uint8_t *cntp = out + L.off_cnt + c * WINDOWS * 2;
         unsigned cnt[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
         for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
         uint64_t p = b0;
+        int win = 0;
         uint64_t j_end = (c + 1) * CHUNK < n ? (c + 1) * CHUNK : n;
         for (uint64_t j = c * CHUNK; j < j_end; j++) {
-            uint64_t win = (p - b0) / W;
-            if (cnt[win] == 0) gap[win] = (uint8_t)(p - (b0 + win * W));
+            /* the window holding bit p: the last one that starts at or before it */
+            while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= p) win++;
+            if (cnt[win] == 0) gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)));
             cnt[win]++;
             p += len[exponent_of(words[j])];
         }
@@ -419,7 +427,7 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
     const uint8_t *stream = c + P.L.off_stream;
     uint64_t b0 = get_u64(c + P.L.off_ci + chunk * 16);
     uint64_t b1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16);
-    uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
+    uint64_t ws = b0 + window_edge(b1 - b0, (uint64_t)win);
     unsigned gap = c[P.L.off_gap + chunk * WINDOWS + win];
     unsigned cnt = get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * win);
     /* output position of this window's first code: codes of earlier windows */
@@ -427,8 +435,8 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
     for (int i = 0; i < win; i++) before += get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * i);
     uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8) + before;
     *n_out = cnt;
-    if (cnt == 0) { *end_bit = b0 + win * W; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
-    uint64_t pos = b0 + win * W + gap;
+    if (cnt == 0) { *end_bit = ws; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
+    uint64_t pos = ws + gap;
     for (unsigned k = 0; k < cnt; k++) {
         int e = read_code(&P, stream, &pos);
         if (e < 0) return -e;
@@ -471,17 +479,16 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
         uint64_t b0 = pos;
         uint64_t b1 = get_u64(ent + 16);
         if (b1 < b0 || b1 > L->total_bits) return ORACLE_E_FORMAT;
-        uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;
         unsigned cnt[WINDOWS];
         int gap[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
         for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
+        int win = 0;
         uint64_t j_end = (ch + 1) * CHUNK < L->n ? (ch + 1) * CHUNK : L->n;
         for (uint64_t j = ch * CHUNK; j < j_end; j++) {
-            if (W == 0) return ORACLE_E_FORMAT;
-            uint64_t win = (pos - b0) / W;
-            if (win >= WINDOWS) return ORACLE_E_FORMAT;
-            if (cnt[win] == 0) gap[win] = (int)(pos - (b0 + win * W));
+            if (pos >= b1) return ORACLE_E_FORMAT;
+            while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= pos) win++;
+            if (cnt[win] == 0) gap[win] = (int)(pos - (b0 + window_edge(b1 - b0, win)));
             cnt[win]++;
             int e = read_code(&P, stream, &pos);
             if (e < 0) return -e;

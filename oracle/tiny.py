@@ -11,7 +11,7 @@ routines that the tests hold the oracle against:
   lightest weights); its cost is the optimum without a length cap.
 * `canonical_code_strings`: canonical code values by the counting
   construction of RFC 1951 section 3.2.2 (bl_count / next_code), as strings.
-* `decode_with_strings`: decodes a version-2 container by matching code
+* `decode_with_strings`: decodes a version-3 container by matching code
   strings against the bit string of the stream, ignoring every index.
 """
 from __future__ import annotations
@@ -93,7 +93,7 @@ def _u64(b, o):
 
 
 def decode_with_strings(container: bytes):
-    """Decode a version-2 container through its code strings only."""
+    """Decode a version-3 container through its code strings only."""
     b = bytes(container)
     assert b[:8] == b"DF11HIPC"
     n = _u64(b, 16)

@@ -162,6 +162,38 @@ def test_non_default_stream_and_repeats():
         assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
+def test_ticket_counters_across_many_launches_and_streams():
+    """Every launch takes its chunks from one of the plan's ticket counters,
+    which its last workgroup clears.  160 launches (single and batched, on
+    two streams that may run side by side) go round every counter slot more
+    than twice; every output must be exact."""
+    torch = _torch()
+    log("ticket counters: 160 launches on two streams")
+    sizes = [3 * 32768 + 5, 900001, 40000]
+    ws = [W.normal_bf16((n,), seed=60 + i) for i, n in enumerate(sizes)]
+    cs = oracle_encode_many(ws)
+    plan = df11.Plan(cs)
+    dcs = [to_device_u8(c) for c in cs]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for r in range(40):
+        o = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+        ob = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+        with torch.cuda.stream(s1):
+            df11.decode(plan, 0, dcs[0], o[0], stream=s1)
+            df11.decode(plan, 2, dcs[2], o[2], stream=s1)
+        with torch.cuda.stream(s2):
+            df11.decode(plan, 1, dcs[1], o[1], stream=s2)
+            df11.decode_batch(plan, dcs, ob, stream=s2)
+        outs += [o, ob]
+    df11.check(plan, stream=s1)
+    df11.check(plan, stream=s2)
+    torch.cuda.synchronize()
+    for o in outs:
+        for w, t in zip(ws, o):
+            assert (t.cpu().numpy().view(np.uint16) == w).all()
+
+
 def test_corrupted_stream_sets_the_flag():
     """A flipped bit in the device copy of the stream: the kernel keeps every
     access in bounds, and df11_check reports the inconsistency (or the words

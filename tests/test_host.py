@@ -100,8 +100,8 @@ def test_validate_rejects_broken_containers():
 
     assert _status(c) == 0
     assert bad(lambda x: x.__setitem__(0, ord("X"))) == E_FORMAT                  # magic
-    assert bad(lambda x: x.__setitem__(8, 3)) == E_UNSUPPORTED                   # version
-    assert bad(lambda x: x.__setitem__(8, 1)) == E_UNSUPPORTED                   # version
+    assert bad(lambda x: x.__setitem__(8, 4)) == E_UNSUPPORTED                   # version
+    assert bad(lambda x: x.__setitem__(8, 2)) == E_UNSUPPORTED                   # an older version
     assert bad(lambda x: x.__setitem__(99, 1)) == E_UNSUPPORTED                  # windows
     assert bad(lambda x: x.__setitem__(97, 1)) == E_FORMAT                       # reserved
     assert bad(lambda x: x.__setitem__(96, 25)) == E_UNSUPPORTED                 # max length

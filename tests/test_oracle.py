@@ -263,15 +263,16 @@ def test_chunk_and_window_index_reproduce_the_source(n):
         NW = oracle.WINDOWS
         parts, ends = [], []
         b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
-        Wb = (b1 - b0 + NW - 1) // NW
+        # window i starts floor(i * N / 512) bits into the chunk's N bits
+        edges = b0 + (np.arange(NW + 1) * (b1 - b0)) // NW
         for win in range(NW):
             words, end = oracle.decode_window(c, ch, win)
             parts.append(words)
             if len(words):
                 ends.append((win, end))
                 # the window's last code starts inside it and may run past it
-                assert b0 + (win + 1) * Wb <= end or end == b1
-                assert end - min(b1, b0 + (win + 1) * Wb) < 24
+                assert edges[win + 1] <= end <= b1
+                assert end - edges[win + 1] < 24
         assert (np.concatenate(parts) == w[lo:hi]).all()
         assert ends[-1][1] == b1
         gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
@@ -281,7 +282,7 @@ def test_chunk_and_window_index_reproduce_the_source(n):
         # the number of starts inside it, its gap the first one's offset
         ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
         starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
-        edges = b0 + Wb * np.arange(NW)
+        edges = edges[:NW]
         before = np.searchsorted(starts, edges, side="left")
         want_cnt = np.diff(np.append(before, hi - lo))
         cnt = c[h["off_win_cnt"] + 2 * NW * ch:h["off_win_cnt"] + 2 * NW * (ch + 1)].view(np.uint16)

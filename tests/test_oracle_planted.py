@@ -38,14 +38,16 @@ MUTATIONS = [
     ("both bit writer and reader least significant bit first",
      None, None, 0),
     ("window gap off by one",
-     "gap[win] = (uint8_t)(p - (b0 + win * W));",
-     "gap[win] = (uint8_t)(p - (b0 + win * W) + 1);", 0),
+     "gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)));",
+     "gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)) + 1);", 0),
     ("window count misses a code that starts on the window's first bit",
      "            cnt[win]++;",
-     "            cnt[win] += (p != b0 + win * W);", 0),
-    ("window width rounds down",
-     "uint64_t W = (b1 - b0 + WINDOWS - 1) / WINDOWS;",
-     "uint64_t W = (b1 - b0) / WINDOWS + 1;", 0),
+     "            cnt[win] += (p != b0 + window_edge(b1 - b0, win));", 0),
+    ("window edges round up",
+     "return i * N / WINDOWS;", "return (i * N + WINDOWS - 1) / WINDOWS;", 0),
+    ("window search stops one window early",
+     "while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= p) win++;",
+     "while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) < p) win++;", 0),
     ("chunk start bit recorded after the first code",
      "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos);",
      "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos + 1);", 0),
@@ -105,6 +107,22 @@ def _pins_pass() -> bool:
                 return False
             parts = [oracle.decode_window(c, ch, win)[0] for win in range(oracle.WINDOWS)]
             if not (np.concatenate(parts) == w[lo:hi]).all():
+                return False
+            # the index from first principles: code starts from the source
+            # and the header's code lengths, windows at floor(i * N / 512)
+            h = oracle.header(c)
+            ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 16 * (h["n_chunks"] + 1)].view(np.uint64)
+            b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
+            ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
+            starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
+            NW = oracle.WINDOWS
+            edges = b0 + (np.arange(NW) * (b1 - b0)) // NW
+            before = np.searchsorted(starts, edges, side="left")
+            want_cnt = np.diff(np.append(before, hi - lo))
+            cnt = c[h["off_win_cnt"] + 2 * NW * ch:h["off_win_cnt"] + 2 * NW * (ch + 1)].view(np.uint16)
+            gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
+            want_gap = np.where(want_cnt > 0, starts[np.minimum(before, hi - lo - 1)] - edges, 0xFF)
+            if not ((cnt == want_cnt).all() and (gap == want_gap).all()):
                 return False
         return True
     except Exception:
