@@ -82,7 +82,6 @@ struct Lds {
 static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0 && offsetof(Lds, rec) % 16 == 0,
               "LDS alignment");
 static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
-constexpr uint32_t kDummy = kTilePadded;   // a tile dword nobody reads
 
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
@@ -231,63 +230,45 @@ __device__ __forceinline__ void entries(const Lds &L, const Src &src, uint32_t p
     }
 }
 
-// One window's decoder.  Output bytes are gathered per tile dword: `acc`
-// holds the bytes of the current dword below the next position (the higher
-// bytes are zero), and every look-up stores that dword whole.  A dword that
-// holds the end of one window and the start of the next is stored by both
-// windows' chains, each with zeros in the other's bytes; so no chain stores
-// its window's first dword during the decode: it keeps it in `head`, and
-// after a barrier every chain writes its first-dword bytes one by one.  The
-// last dword a chain stores (after its last look-up, from acc when that
-// look-up crossed into it) may hold bytes past its window's end (decoded
-// codes of the next window: the right values, or zeros), which the next
-// window's first-dword bytes overwrite.
+// One window's decoder.  The tile is cleared before the decode, and every
+// look-up ORs its exponent bytes into the tile dword at the chain's next
+// output position and the dword after it.  So chains never overwrite each
+// other's bytes: where a window's last look-up decodes codes of the next
+// window (its last entry can run up to two codes past the window's end), it
+// ORs in the same values that the next window's chain writes there.
 struct Chain {
     uint32_t P;      // stream position of the next code, plus kPosBias
-    uint32_t dw;     // tile dword of the next output position
-    uint32_t f8;     // 8 x the next output position's byte in that dword
-    uint32_t acc;    // that dword's bytes below the next position
-    uint32_t q0, qe; // the window's first output position and its end
-    uint32_t head;   // the window's first tile dword (its bytes from q0 & 3 on)
+    uint32_t p8;     // 8 x the next output position (chunk-relative)
+    uint32_t qe;     // the window's end (output position)
 };
 
 // Byte offset in the tile of dword dw: 4 pad bytes after every 128, so that
 // the dwords lanes store at the same time (their windows' outputs start
-// about 64 positions apart) spread over the banks.
+// about 64 positions apart) spread over the banks.  The bytes a look-up
+// spills past dword 32g+31 land in the pad after it, and the assembly ORs
+// them into dword 32g+32.
 __device__ __forceinline__ uint32_t tile_off(uint32_t dw) { return (dw + (dw >> 5)) << 2; }
 
-// Chain c takes look-up entry ent (its bytes go to the tile dword at the
-// next output position); kHead: the chain may still be in its window's
-// first dword.  kMasked: an inactive chain (ent = 0 then) stores to the
-// dummy dword and keeps its state.
-template <bool kHead, bool kMasked = false>
-__device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent, bool active = true) {
-    const uint64_t x = (uint64_t)(ent & 0xFFFFFFu) << c.f8;   // the entry's bytes from f8 on
-    const uint32_t lo = c.acc | (uint32_t)x;
-    uint32_t addr = tile_off(c.dw);
-    if (kHead) {
-        const bool in_head = c.dw == (c.q0 >> 2);
-        c.head = in_head ? lo : c.head;
-        addr = in_head ? kDummy : addr;
-    }
-    if (kMasked) addr = active ? addr : kDummy;
-    *reinterpret_cast<uint32_t *>(L.tile + addr) = lo;
-    const uint32_t f8n = (__builtin_amdgcn_ubfe(ent, kEntCountShift, 3) << 3) + c.f8;
-    const bool crossed = f8n >= 32u;
-    c.acc = crossed ? (uint32_t)(x >> 32) : lo;
-    c.dw += crossed ? 1u : 0u;
-    c.f8 = f8n & 31u;
+__device__ __forceinline__ void tile_or(Lds &L, uint32_t off, uint32_t v) {
+    uint32_t *d = static_cast<uint32_t *>(__builtin_assume_aligned(L.tile + off, 4));   // off % 4 == 0
+    __hip_atomic_fetch_or(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Chain c takes look-up entry ent (0 for a finished chain in the masked
+// phase: it then ORs zeros and keeps its state).
+__device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent) {
+    // the entry's bytes from the position's byte in its dword on
+    const uint64_t x = (uint64_t)(ent & 0xFFFFFFu) << (c.p8 & 24u);
+    const uint32_t off = tile_off(c.p8 >> 5);
+    tile_or(L, off, (uint32_t)x);
+    tile_or(L, off + 4, (uint32_t)(x >> 32));
+    c.p8 += ent_count(ent) << 3;
     c.P += ent_bits(ent);
 }
 
-__device__ __forceinline__ uint32_t out_pos(const Chain &c) { return (c.dw << 2) + (c.f8 >> 3); }
+__device__ __forceinline__ uint32_t out_pos(const Chain &c) { return c.p8 >> 3; }
 
-__device__ __forceinline__ void flush_tail(Lds &L, const Chain &c) {
-    if (c.qe > c.q0 && (c.dw << 2) < c.qe && c.dw != (c.q0 >> 2))
-        *reinterpret_cast<uint32_t *>(L.tile + tile_off(c.dw)) = c.acc;
-}
-
-template <bool kHead, class Src>
+template <class Src>
 __device__ __forceinline__ void masked_tail(Lds &L, const Src &src, Chain &A, Chain &B, int32_t &ra,
                                             int32_t &rb, uint32_t &ea_r, uint32_t &eb_r, uint32_t &bad) {
     uint32_t ea, eb;
@@ -301,8 +282,8 @@ __device__ __forceinline__ void masked_tail(Lds &L, const Src &src, Chain &A, Ch
         eb_r = ab ? eb : eb_r;
         ra -= (int32_t)ent_count(ea);
         rb -= (int32_t)ent_count(eb);
-        step<kHead, true>(L, A, ea, aa);
-        step<kHead, true>(L, B, eb, ab);
+        step(L, A, ea);
+        step(L, B, eb);
         any = __ballot((ra > 0) | (rb > 0)) != 0;
     }
 }
@@ -330,7 +311,6 @@ __device__ __forceinline__ Window window_at(const uint32_t *w, uint32_t P) {
 }
 
 // One counted look-up of both chains from their register windows.
-template <bool kHead>
 __device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &wa, Window &wb,
                                             uint32_t &bad) {
     const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
@@ -352,8 +332,48 @@ __device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &
     wa.w1 = ca ? na : wa.w1;
     wb.w0 = cb ? wb.w1 : wb.w0;
     wb.w1 = cb ? nb : wb.w1;
-    step<kHead>(L, A, ea);
-    step<kHead>(L, B, eb);
+    step(L, A, ea);
+    step(L, B, eb);
+}
+
+// The masked phase from register windows: as window_step, for the chains
+// whose windows still have codes (the others take a zero entry and keep
+// their state).  The next-word reads are clamped to the staged words, so a
+// container whose index disagrees with its stream reads inside them.
+__device__ __forceinline__ void masked_window_tail(Lds &L, uint32_t kmax, Chain &A, Chain &B, Window &wa,
+                                                   Window &wb, int32_t &ra, int32_t &rb, uint32_t &ea_r,
+                                                   uint32_t &eb_r, uint32_t &bad) {
+    const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
+    bool any = __ballot((ra > 0) | (rb > 0)) != 0;
+    while (any) {
+        const bool aa = ra > 0, ab = rb > 0;
+        const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
+        const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
+        uint32_t ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
+        uint32_t eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
+        const uint32_t na = L.codes[min(A.P >> 5, kmax) + 2];
+        const uint32_t nb = L.codes[min(B.P >> 5, kmax) + 2];
+        __builtin_amdgcn_sched_barrier(0);
+        if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
+            if (ea == 0) ea = long_entry(L.lut, ta, bad);
+            if (eb == 0) eb = long_entry(L.lut, tb, bad);
+        }
+        ea = aa ? ea : 0u;
+        eb = ab ? eb : 0u;
+        ea_r = aa ? ea : ea_r;
+        eb_r = ab ? eb : eb_r;
+        ra -= (int32_t)ent_count(ea);
+        rb -= (int32_t)ent_count(eb);
+        const bool ca = (A.P | 31u) < A.P + ent_bits(ea);
+        const bool cb = (B.P | 31u) < B.P + ent_bits(eb);
+        wa.w0 = ca ? wa.w1 : wa.w0;
+        wa.w1 = ca ? na : wa.w1;
+        wb.w0 = cb ? wb.w1 : wb.w0;
+        wb.w1 = cb ? nb : wb.w1;
+        step(L, A, ea);
+        step(L, B, eb);
+        any = __ballot((ra > 0) | (rb > 0)) != 0;
+    }
 }
 
 // Decode both windows of this lane.  T: look-ups after which no window of
@@ -363,66 +383,45 @@ template <class Src>
 __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Chain &B, uint32_t T,
                                             uint32_t &bad) {
     uint32_t ea, eb;
+    int32_t ra, rb;
+    uint32_t ea_r = 0, eb_r = 0;
     // 1. counted (the caller keeps the starts at least 24*T bits below the
-    //    source's end, so these peeks need no clamp); a chain leaves its
-    //    window's first dword within four look-ups
-    uint32_t t = 0;
+    //    source's end, so these peeks need no clamp); 2. masked, without
+    //    branches: a finished window takes a zero entry; each window's last
+    //    entry is kept to find where its last code ends
     if constexpr (Src::kLds) {
         Window wa = window_at(src.w, A.P), wb = window_at(src.w, B.P);
         // (the loop then starts with no LDS read in flight)
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        for (; t < T && t < 4u; ++t) window_step<true>(L, A, B, wa, wb, bad);
-        for (; t < T; ++t) window_step<false>(L, A, B, wa, wb, bad);
+        for (uint32_t t = 0; t < T; ++t) window_step(L, A, B, wa, wb, bad);
+        ra = (int32_t)(A.qe - out_pos(A));
+        rb = (int32_t)(B.qe - out_pos(B));
+        masked_window_tail(L, src.pmax >> 5, A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
     } else {
-        for (; t < T && t < 4u; ++t) {
+        for (uint32_t t = 0; t < T; ++t) {
             entries<false>(L, src, A.P, B.P, ea, eb, bad);
-            step<true>(L, A, ea);
-            step<true>(L, B, eb);
+            step(L, A, ea);
+            step(L, B, eb);
         }
-        for (; t < T; ++t) {
-            entries<false>(L, src, A.P, B.P, ea, eb, bad);
-            step<false>(L, A, ea);
-            step<false>(L, B, eb);
-        }
+        ra = (int32_t)(A.qe - out_pos(A));
+        rb = (int32_t)(B.qe - out_pos(B));
+        masked_tail(L, src, A, B, ra, rb, ea_r, eb_r, bad);
     }
-    // 2. masked, without branches: a finished window takes a zero entry
-    //    (it stores to the dummy dword and keeps its state); each window's
-    //    last entry is kept to find where its last code ends
-    int32_t ra = (int32_t)(A.qe - out_pos(A)), rb = (int32_t)(B.qe - out_pos(B));
-    uint32_t ea_r = 0, eb_r = 0;
-    if (T >= 4u)
-        masked_tail<false>(L, src, A, B, ra, rb, ea_r, eb_r, bad);
-    else
-        masked_tail<true>(L, src, A, B, ra, rb, ea_r, eb_r, bad);
     // the last entry took -r codes past the window's end
     A.P -= trailing_bits(L, ea_r, (uint32_t)(-ra));
     B.P -= trailing_bits(L, eb_r, (uint32_t)(-rb));
-    // 3. a last look-up that crossed into a new dword left that dword's
-    //    bytes in acc: store them when the window reaches into it (and it is
-    //    not the window's first dword)
-    flush_tail(L, A);
-    flush_tail(L, B);
 }
 
-// After every chain's dword stores (and a barrier): the window's bytes in
-// its first tile dword, one by one.
-__device__ __forceinline__ void write_head(Lds &L, const Chain &c) {
-    const uint32_t n = c.qe - c.q0;
-    const uint32_t f = c.q0 & 3u;
-    const uint32_t m = n < 4u - f ? n : 4u - f;
-    const uint32_t a = tile_off(c.q0 >> 2) + f;
-#pragma unroll
-    for (uint32_t k = 0; k < 4; ++k)
-        if (k < m) L.tile[a + k] = (uint8_t)(c.head >> (8 * (f + k)));
-}
-
-// Loads of data that no thread writes during the kernel (work list,
-// descriptors, chunk index) through the constant address space: with a
-// uniform address they become scalar loads, which wait on their own counter
-// instead of behind the vector loads and stores in flight.
-template <class T>
-__device__ __forceinline__ T const_load(const T *p) {
-    return *(const __attribute__((address_space(4))) T *)p;
+// Tile dwords dw and dw+1 (dw even) for the assembly.  When dw opens a
+// 32-dword group, the pad before it holds the bytes that look-ups at the
+// group's last dword spilled into it: pad_mask (all ones for such lanes) ORs
+// them in.  (Dword 0 ORs itself.)
+__device__ __forceinline__ u32x2 tile_pair(const Lds &L, uint32_t dw, uint32_t pad_mask) {
+    const uint32_t ta = tile_off(dw);
+    const uint32_t tp = ta ? ta - 4u : 0u;
+    const uint32_t pad = *reinterpret_cast<const uint32_t *>(L.tile + tp) & pad_mask;
+    return u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta) | pad,
+                 *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
 }
 
 // One work item (a chunk of a tensor) and where its bytes are.
@@ -589,8 +588,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         uint32_t t1 = n;
         if (wave == 0) t1 = take_ticket(a, lane);
 
-        // ---- the staged words to LDS (every tile byte of the chunk gets
-        //      written by the decode, so the tile needs no clearing)
+        // ---- the tile cleared (the decode ORs its bytes in), and the staged
+        //      words to LDS
+#pragma unroll
+        for (uint32_t i = 0; i < sizeof(L.tile) / 16; i += kThreads)
+            if (i + tid < sizeof(L.tile) / 16) reinterpret_cast<u32x4 *>(L.tile)[i + tid] = u32x4{0u, 0u, 0u, 0u};
         if (it.staged) {
 #pragma unroll
             for (int k = 0; k < kCodeLoads; ++k) {
@@ -647,8 +649,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         T = min(T, pmax / 48u);
         const uint32_t plim = pmax - 24u * T;
         bad |= (sa > plim) | (sb > plim);
-        Chain A{min(sa, plim) + kPosBias, qa >> 2, (qa & 3u) << 3, 0u, qa, qa + na, 0u};
-        Chain B{min(sb, plim) + kPosBias, qb >> 2, (qb & 3u) << 3, 0u, qb, qb + nb, 0u};
+        Chain A{min(sa, plim) + kPosBias, qa << 3, qa + na};
+        Chain B{min(sb, plim) + kPosBias, qb << 3, qb + nb};
         if (it.staged) {
             // peeks read codes[k], codes[k+1] with k = P / 32 <= kCodeWords
             const LdsCodes src{L.codes, pmax + kPosBias};
@@ -661,9 +663,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint32_t ea = A.P - kPosBias;
         const uint32_t eb = B.P - kPosBias;
         if (wave == 0) put_rec(L, sl ^ 1u, r1, t1, lane);
-        __syncthreads();
-        write_head(L, A);
-        write_head(L, B);
         __syncthreads();
 
         // ---- every non-empty window ends where the next non-empty window's
@@ -700,13 +699,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         load_lut(a, nx.lut, tid, lr);
         uint16_t *o = it.out;
         const uint32_t full = nc / kBlockElems;
+        // lanes whose first dword opens a 32-dword group (tid % 16 == 0) OR
+        // in the pad before it
+        const uint32_t pad_mask = (tid & 15u) ? 0u : ~0u;
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
                 const uint32_t j = kBlockElems * b + 8 * tid;
-                const uint32_t ta = tile_off(j >> 2);
-                const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
-                                       *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
+                const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
                 __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
             }
             rw[b] = load_raw(nx, tid, b);
@@ -716,9 +716,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
                 const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
-                const uint32_t ta = tile_off(j >> 2);
-                const u32x2 t8 = u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta),
-                                       *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
+                const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
                 const u32x4 v = join8(t8, r8);
                 if (j + 8 <= nc) {
                     *reinterpret_cast<u32x4 *>(o + j) = v;
