@@ -21,6 +21,7 @@ Inputs are synthetic: seeded N(0, 0.02) weights rounded to BF16.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -33,13 +34,24 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0
 METRIC = "decoded BF16 GB/s and % of HBM roofline (Llama-8B block), bit-exact"
 WORKLOAD = "llama8b_block"
-KERNEL_SRC = os.path.join(ROOT, "lossless_bf16_weight_amd", "csrc", "decode.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "lossless_bf16_weight_amd", "csrc", f)
+               for f in ("decode.hip", "df11_internal.hpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_llama8b_block_counters.txt")
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the decode kernel's sources
+    (decode.hip, then df11_internal.hpp) with comments and whitespace removed:
+    a counter summary stays valid across comment edits, not across code
+    changes."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -6,37 +6,42 @@
 // one bitstream; output words are bit-identical to the originals.
 //
 // One workgroup = four wave64s (256 lanes) decodes whole chunks of 32768
-// elements (64 KiB of BF16 output), one after the other, over a contiguous
-// range of the launch's work items (tensor, chunk).  Per chunk:
+// elements (64 KiB of BF16 output), one after the other; a launch's
+// workgroups take its chunks from a ticket counter, one chunk ahead.  Per
+// chunk:
 //
-//   1. stage: coalesced 16-byte loads of the chunk's code bytes, byte-swapped
-//      into big-endian 32-bit words in LDS; the chunk's raw bytes wait in
-//      registers (8 bytes per lane per 2048 elements) until step 5.  Both are
-//      requested while the previous chunk decodes;
-//   2. index: the chunk's bits form 512 equal windows; lane i takes windows
-//      2i and 2i+1.  A DPP prefix sum over each wave's lane totals of the
-//      window code counts, plus the totals of the waves below (through LDS),
-//      gives each window the chunk position of its first code;
-//   3. decode: each lane walks its two windows side by side (two independent
-//      dependency chains; 512 chains per workgroup).  A look-up peeks 32 bits
-//      with one ds_read2_b32 and a funnel shift, then one LDS first-level
-//      table entry resolves up to three codes of <= 10 bits; codes of 11..16
-//      bits use a second-level table, longer ones the canonical limits.
-//      Exponent bytes (rotated, see rot_exp) go to a 32 KiB LDS tile at their
-//      chunk positions.  A counted loop with no per-lane control flow runs
-//      while no window of the wave can run out (each look-up takes at most
-//      three codes); a masked loop and an exact per-window loop finish;
+//   1. stage: the tile is cleared; the chunk's code bytes, requested with
+//      coalesced 16-byte loads while the previous chunk was assembled, go
+//      to LDS as 32-bit words with the stream's first bit lowest; the
+//      chunk's raw bytes wait in registers (8 bytes per lane per 2048
+//      elements) until step 4;
+//   2. index: the chunk's N bits form 512 windows (window i starts
+//      floor(i*N/512) bits in); lane i takes windows 2i and 2i+1.  A DPP
+//      prefix sum over each wave's lane totals of the window code counts,
+//      plus the totals of the waves below (through LDS), gives each window
+//      the chunk position of its first code;
+//   3. decode: each lane walks its two windows side by side (two
+//      independent dependency chains; 512 chains per workgroup).  A chain
+//      keeps the two code words around its position in registers; a
+//      look-up funnel-shifts them, reads one first-level table entry (up to
+//      three codes of <= 10 bits; codes of 11..16 bits use a second-level
+//      table, longer ones the canonical limits) together with the next code
+//      word, and ORs the exponent bytes (rotated, see rot_exp) into a 32 KiB
+//      LDS tile at their chunk positions.  A counted loop with no per-lane
+//      control flow runs while no window of the wave can run out (each
+//      look-up takes at most three codes); a masked loop finishes;
 //   4. check: a window must end exactly where the next non-empty window's
 //      first code starts (or at the chunk end); otherwise the plan's flag is
 //      set;
 //   5. assemble: per 2048 elements, each lane joins 8 tile bytes with 8 raw
 //      bytes into BF16 words (two byte permutes and one bitfield insert per
 //      two words) and writes them with one 16-byte store, contiguous across
-//      the wave (1 KiB per store instruction).
+//      the wave (1 KiB per store instruction); the next chunk's code bytes,
+//      tables and raw bytes are requested meanwhile.
 //
 // There is no matrix arithmetic here: the path is bound by HBM traffic
-// (about 1.33 bytes read and 2 bytes written per element), with integer
-// ALU and LDS issue as the secondary limit.
+// (about 1.37 bytes read and 2 bytes written per element), with the look-up
+// chains' latency and integer ALU as the secondary limit.
 #include <hip/hip_runtime.h>
 
 #include "df11_internal.hpp"
@@ -47,9 +52,9 @@ constexpr int kThreads = 256;                      // lanes per workgroup
 constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = kChunk;                 // one exponent byte per element
 constexpr uint32_t kTilePadded = kTileBytes + kTileBytes / 32;   // 4 pad bytes per 128
-// LDS per workgroup: 13 KiB staged codes + 33 KiB tile + 5.8 KiB tables =
-// 51.8 KiB, so that three workgroups fit in a compute unit's 160 KiB (the
-// allocation is rounded up, and 52.8 KiB would leave room for only two).
+// LDS per workgroup: 13 KiB staged codes + 33 KiB tile + 5.8 KiB tables +
+// 160 bytes of records and wave totals = 52 KiB, so that three workgroups
+// fit in a compute unit's 160 KiB.
 constexpr int kCodeWords = kCodeCap / 4;
 constexpr int kCodeLoads = (kCodeCap + 16 * kThreads - 1) / (16 * kThreads);
 constexpr int kBlockElems = 8 * kThreads;          // elements per store block
@@ -59,10 +64,10 @@ static_assert(2 * kThreads == kWindows, "two windows per lane");
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// LDS of one wave.  Staged code word k (big-endian) sits in codes[k + 1],
-// with codes[1] 16-byte aligned; the 12 bytes in front keep codes[0] (read
-// only for positions that are multiples of 32) inside the struct.  The
-// tile's and the tables' bases fold into the instructions' 16-bit offsets.
+// LDS of one workgroup.  Staged code word k (first stream bit lowest) sits
+// in codes[k + 1], with codes[1] 16-byte aligned; the 12 bytes in front keep
+// codes[0] inside the struct.  The tile's and the tables' bases fold into
+// the instructions' 16-bit offsets.
 struct Lds {
     uint32_t pad[3];
     uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
@@ -519,6 +524,7 @@ __device__ __forceinline__ void load_codes(const Item &it, uint32_t tid, u32x4 (
 #pragma unroll
     for (int k = 0; k < kCodeLoads; ++k) {
         const uint32_t off = min(16u * kThreads * k + 16u * tid, it.s_len - 16u);
+        // (non-temporal: plain loads measured about 6% slower overall)
         cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + off));
     }
 }
@@ -534,9 +540,10 @@ __device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t tid, int b) {
 
 // The index entries of this lane's windows 2 tid and 2 tid + 1: x = both
 // gaps (low byte: window 2 tid), y = both code counts (low half: window
-// 2 tid).
+// 2 tid).  (Non-temporal, as the code bytes: about 1% faster here.)
 __device__ __forceinline__ u32x2 load_windows(const Item &it, uint32_t tid) {
-    return u32x2{reinterpret_cast<const uint16_t *>(it.gap)[tid], reinterpret_cast<const uint32_t *>(it.cnt)[tid]};
+    return u32x2{__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(it.gap) + tid),
+                 __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(it.cnt) + tid)};
 }
 
 __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
