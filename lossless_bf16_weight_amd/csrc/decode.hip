@@ -676,12 +676,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint32_t ea = A.P - kPosBias;
         const uint32_t eb = B.P - kPosBias;
         if (wave == 0 && !late) put_rec(L, sl ^ 1u, r1, t1, lane);
+        // (the ticket's round trip overlaps the wait for the other waves)
+        if (wave == 0 && late) t1 = take_ticket(a, lane);
         __syncthreads();
         if (late) {
-            if (wave == 0) {
-                t1 = take_ticket(a, lane);
-                put_rec(L, sl ^ 1u, fetch_rec(a, min(t1, n - 1), lane), t1, lane);
-            }
+            if (wave == 0) put_rec(L, sl ^ 1u, fetch_rec(a, min(t1, n - 1), lane), t1, lane);
             __syncthreads();
         }
 
