@@ -122,6 +122,69 @@ def cpu_baseline(containers, infos, min_wall_s: float = 1.5, max_wall_s: float =
                       f"bit-serial oracle decode on {threads} threads, {dt:.1f} s wall"}
 
 
+def jit_overlap(n_layers: int, token_counts, reps: int):
+    """The just-in-time layer loop with a consumer: per layer, the consumer
+    computes x @ W^T for the layer's seven tensors (BF16 products by the
+    vendor library), and the next layer decodes on its own stream meanwhile.
+    Per token count: ms per layer for the consumer alone (weights already
+    decoded), the decode alone, and the overlapped loop; the overhead is the
+    loop's time over the consumer's, minus one (the quantity the mlx-dfloat
+    page reports per denoising step)."""
+    import numpy as np
+    import torch
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+    from lossless_bf16_weight_amd.jit import LayerLoop
+
+    F = torch.nn.functional
+    plans, dconts = [], []
+    for l in range(n_layers):
+        specs = W.llama8b_block(l)
+        cs = [df11.encode(s.make().reshape(-1), shape=s.shape) for s in specs]
+        plans.append(df11.Plan(cs))
+        dconts.append([torch.from_numpy(c).to("cuda") for c in cs])
+    loop = LayerLoop(plans, dconts)
+    stream = torch.cuda.current_stream()
+    loop.decode_into(0, 0, stream)
+    torch.cuda.synchronize()
+    resident = loop.weights(0, 0)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps / n_layers
+
+    rows = []
+    for T in token_counts:
+        gen = torch.Generator(device="cuda").manual_seed(T)
+        x = (torch.randn(T, 4096, device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+        x2 = (torch.randn(T, 14336, device="cuda", generator=gen) * 0.5).to(torch.bfloat16)
+
+        def consume(l, ws):
+            for w in ws:
+                F.linear(x2 if w.shape[1] == x2.shape[1] else x, w)
+
+        consumer_ms = timed(lambda: [consume(l, resident) for l in range(n_layers)])
+        decode_ms = timed(lambda: [loop.decode_into(l, l & 1, stream) for l in range(n_layers)])
+        loop_ms = timed(lambda: loop.run(consume))
+        flops = 2.0 * T * sum(w.numel() for w in resident)
+        rows.append({"tokens": T, "consumer_ms_per_layer": round(consumer_ms, 4),
+                     "decode_ms_per_layer": round(decode_ms, 4), "jit_loop_ms_per_layer": round(loop_ms, 4),
+                     "overhead": round(loop_ms / consumer_ms - 1.0, 4),
+                     "decode_hidden": round((consumer_ms + decode_ms - loop_ms) / decode_ms, 4),
+                     "consumer_tflops": round(flops / (consumer_ms * 1e-3) / 1e12, 1)})
+    print(json.dumps({"metric": "just-in-time layer loop: overhead of decoding one layer ahead of a BF16 consumer",
+                      "config": {"workload": "llama8b_block layers", "layers": n_layers,
+                                 "consumer": "x @ W^T for the 7 tensors of each layer (torch.nn.functional.linear)"},
+                      "results": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +194,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (the reference "
                          "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--jit-overlap", action="store_true",
+                    help="only measure the just-in-time layer loop against its consumer")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this decoder runs on one GPU "
@@ -139,6 +204,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.jit_overlap:
+        jit_overlap(n_layers=8, token_counts=(1, 256, 2048, 8192), reps=5)
+        return
 
     if args.copy_calibration:
         a = torch.ones(256 << 20, dtype=torch.int16, device="cuda:0")
