@@ -13,6 +13,8 @@ routines that the tests hold the oracle against:
   construction of RFC 1951 section 3.2.2 (bl_count / next_code), as strings.
 * `decode_with_strings`: decodes a version-3 container by matching code
   strings against the bit string of the stream, ignoring every index.
+* `nf12_encode_tiny`: an NF12 container built a second way (field values by
+  slicing the 16-bit pattern as a string, each group as one 96-bit integer).
 """
 from __future__ import annotations
 
@@ -117,3 +119,43 @@ def decode_with_strings(container: bytes):
         r = b[off_raw + j]
         words.append(((r & 0x80) << 8) | (e << 7) | (r & 0x7F))
     return words
+
+
+def nf12_encode_tiny(words):
+    """Byte string of the NF12 container of `words` (a list of ints)."""
+    n = len(words)
+    padded = list(words) + [0x3800] * (-n % 8)
+    groups = [padded[i:i + 8] for i in range(0, len(padded), 8)]
+    G = len(groups)
+    n_words = (G + 63) // 64
+
+    def fits(w):
+        return format(w, "016b")[1:5] == "0111"
+
+    def code(w):
+        s = format(w, "016b")
+        return int(s[0] + s[5:9] + s[9:16], 2)
+
+    esc = [g for g in range(G) if not all(fits(w) for w in groups[g])]
+    align = lambda x: (x + 255) // 256 * 256
+    off_slots = 256
+    off_flags = align(off_slots + 12 * G)
+    off_prefix = align(off_flags + 8 * n_words)
+    off_escape = align(off_prefix + 4 * n_words)
+    total = align(off_escape + 16 * len(esc))
+    out = bytearray(total)
+    out[0:8] = b"NF12HIPC"
+    struct.pack_into("<II", out, 8, 1, 0)
+    struct.pack_into("<QQQQQQQQ", out, 16, n, G, len(esc), off_slots, off_flags, off_prefix, off_escape, total)
+    for g in range(G):
+        if g in esc:
+            continue
+        v = sum(code(w) << (12 * i) for i, w in enumerate(groups[g]))
+        out[off_slots + 12 * g:off_slots + 12 * g + 12] = v.to_bytes(12, "little")
+    for w in range(n_words):
+        flags = sum(1 << (g - 64 * w) for g in esc if 64 * w <= g < 64 * (w + 1))
+        struct.pack_into("<Q", out, off_flags + 8 * w, flags)
+        struct.pack_into("<I", out, off_prefix + 4 * w, sum(1 for g in esc if g < 64 * w))
+    for k, g in enumerate(esc):
+        struct.pack_into("<8H", out, off_escape + 16 * k, *groups[g])
+    return bytes(out)
