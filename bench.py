@@ -185,6 +185,67 @@ def jit_overlap(n_layers: int, token_counts, reps: int):
                       "results": rows}), flush=True)
 
 
+def nf12_compare(reps: int = 100, warmup: int = 200):
+    """NF12 (fixed-rate 12-bit groups with an escape buffer) next to DF11 on
+    the workloads that fit one decode: container size relative to BF16 and
+    decode rate (BF16 GB/s and HBM GB/s of the bytes each decode moves)."""
+    import numpy as np
+    import torch
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    rows = []
+    for name in ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
+        specs = W.WORKLOADS[name]()
+        words = [s.make().reshape(-1) for s in specs]
+        n = sum(w.size for w in words)
+        outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in words]
+        # DF11
+        dc = [df11.encode(w, shape=s.shape, threads=16) for w, s in zip(words, specs)]
+        plan = df11.Plan(dc)
+        d_dc = [torch.from_numpy(c).to("cuda") for c in dc]
+        df_ms = timed(lambda: df11.decode_batch(plan, d_dc, outs, stream=stream))
+        df11.check(plan, stream=stream)
+        df_ok = all(torch.equal(torch.from_numpy(w.view(np.int16)).to("cuda"), o) for w, o in zip(words, outs))
+        df_bytes = sum(i["bytes_read_per_decode"] for i in plan.infos) + 2 * n
+        df_size = sum(c.size for c in dc)
+        # NF12
+        nc = [df11.nf12_encode(w, threads=16) for w in words]
+        d_nc = [torch.from_numpy(c).to("cuda") for c in nc]
+        hdrs = [c[:256].copy() for c in nc]
+        nf_ms = timed(lambda: [df11.nf12_decode(h, d, o, stream=stream) for h, d, o in zip(hdrs, d_nc, outs)])
+        nf_ok = all(torch.equal(torch.from_numpy(w.view(np.int16)).to("cuda"), o) for w, o in zip(words, outs))
+        nf_size = sum(c.size for c in nc)
+        esc = sum(int(c[32:40].view(np.uint64)[0]) for c in nc)
+        groups = sum((w.size + 7) // 8 for w in words)
+        nf_bytes = sum(12 * ((w.size + 7) // 8) for w in words) + 16 * esc + groups // 8 + groups // 16 + 2 * n
+        rows.append({"workload": name, "elements": n, "tensors": len(words),
+                     "df11": {"ratio": round(df_size / (2 * n), 4), "ms": round(df_ms, 5),
+                              "bf16_GBs": round(2 * n / df_ms / 1e6, 1), "hbm_GBs": round(df_bytes / df_ms / 1e6, 1),
+                              "launches": 1 + (len(words) - 1) // 64, "bit_exact": bool(df_ok)},
+                     "nf12": {"ratio": round(nf_size / (2 * n), 4), "ms": round(nf_ms, 5),
+                              "bf16_GBs": round(2 * n / nf_ms / 1e6, 1), "hbm_GBs": round(nf_bytes / nf_ms / 1e6, 1),
+                              "outlier_groups": round(esc / groups, 5), "launches": len(words),
+                              "bit_exact": bool(nf_ok)}})
+        del d_dc, d_nc, outs
+    print(json.dumps({"metric": "NF12 next to DF11: size relative to BF16 and decode rate", "results": rows}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -194,6 +255,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device-to-device copy (the reference "
                          "dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--nf12", action="store_true",
+                    help="only compare the NF12 format with DF11 on the workloads")
     ap.add_argument("--jit-overlap", action="store_true",
                     help="only measure the just-in-time layer loop against its consumer")
     args = ap.parse_args()
@@ -204,6 +267,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.nf12:
+        nf12_compare()
+        return
 
     if args.jit_overlap:
         jit_overlap(n_layers=8, token_counts=(1, 256, 2048, 8192), reps=5)

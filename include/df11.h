@@ -183,6 +183,58 @@ df11_status df11_check(df11_plan_t plan, hipStream_t stream);
 df11_status df11_bw_control(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
                             int hip_device, hipStream_t stream);
 
+/* ------------------------------------------------------------------- NF12 */
+
+/* NF12: a second, fixed-rate lossless format (nf12 news page, "Developer
+ * open-sources nf12: lossless 12-bit compression for BF16 models", "How it
+ * works" and "Implementation details").  Weights go in groups of 8.  When the
+ * top four exponent bits of all 8 are 0111, the group is stored in 12 bytes:
+ * code i = (sign << 11) | (low four exponent bits << 7) | fraction occupies
+ * bits 12i .. 12i+11 (bit b = bit b % 8 of byte b / 8).  Any other group is
+ * an outlier: its 12-byte slot is zero, a bitmap flags it, and its 8 words
+ * are kept whole in an escape buffer (28 bytes per outlier group in all).
+ * A partial last group is completed with the word 0x3800, which fits.
+ *
+ * Container (little-endian; sections start on 256-byte boundaries):
+ *   header (256 bytes)
+ *      0 char[8] magic "NF12HIPC"   8 u32 version = 1     12 u32 flags = 0
+ *     16 u64 n_elems               24 u64 n_groups        32 u64 n_escaped
+ *     40 u64 off_slots             48 u64 off_flags       56 u64 off_prefix
+ *     64 u64 off_escape            72 u64 total_bytes     80 u8[176] 0
+ *   slots   n_groups x 12 bytes
+ *   flags   ceil(n_groups / 64) x u64: bit g % 64 of word g / 64 = group g
+ *           is an outlier
+ *   prefix  ceil(n_groups / 64) x u32: outlier groups before each flag word
+ *   escape  n_escaped x 16 bytes: the outlier groups' words, in group order
+ *   Bytes not named above are zero. */
+
+/* Bytes an NF12 container of n elements can take at most. */
+uint64_t df11_nf12_bound(uint64_t n_elems);
+
+/* Encode n BF16 words (HOST, uint16 bit patterns) into an NF12 container in
+ * HOST memory out (out_cap bytes, df11_nf12_bound(n) always suffices).
+ * threads <= 0: all hardware threads.  The bytes do not depend on threads.
+ * Returns DF11_OK or DF11_E_ARG. */
+df11_status df11_nf12_encode(const uint16_t *words, uint64_t n, void *out, uint64_t out_cap,
+                             uint64_t *out_bytes, int threads);
+
+/* Validate an NF12 container in HOST memory.  With bytes >= its total size
+ * every section is checked (flags, prefix counts, zero outlier slots and
+ * padding); with fewer (at least the 256-byte header) only the header and
+ * the layout.  *n_elems (if not NULL) receives the element count.
+ * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
+df11_status df11_nf12_validate(const void *container, size_t bytes, uint64_t *n_elems);
+
+/* Decode an NF12 container: host_header = HOST copy of its first 256 bytes
+ * (validated here); d_container = DEVICE pointer to the whole container;
+ * d_out = DEVICE pointer to n_elems * 2 bytes.  Both 16-byte aligned, not
+ * overlapping.  Enqueues on `stream`; never allocates or synchronizes.
+ * Memory safety does not depend on the device bytes (an outlier's escape
+ * entry is clamped into the escape buffer).
+ * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT, DF11_E_UNSUPPORTED or DF11_E_HIP. */
+df11_status df11_nf12_decode(const void *host_header, const void *d_container, void *d_out,
+                             int hip_device, hipStream_t stream);
+
 /* ------------------------------------------------------------------- misc */
 
 /* Text of the last non-OK status on this thread (never NULL). */

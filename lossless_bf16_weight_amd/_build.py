@@ -21,6 +21,8 @@ SOURCES = [
     ("encode.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("decode.hip", DEVICE),
     ("control.hip", DEVICE),
+    ("nf12.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
+    ("nf12.hip", DEVICE),
 ]
 
 

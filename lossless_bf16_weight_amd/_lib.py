@@ -54,6 +54,7 @@ EXPORTS = [
     "df11_validate", "df11_container_bound", "df11_encode", "df11_plan", "df11_plan_destroy",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
+    "df11_nf12_bound", "df11_nf12_encode", "df11_nf12_validate", "df11_nf12_decode",
 ]
 
 
@@ -95,6 +96,14 @@ def lib():
     L.df11_abi_version.restype = ctypes.c_int
     L.df11_bw_control.argtypes = [vp, u64, vp, u64, ctypes.c_int, vp]
     L.df11_bw_control.restype = ctypes.c_int
+    L.df11_nf12_bound.argtypes = [u64]
+    L.df11_nf12_bound.restype = u64
+    L.df11_nf12_encode.argtypes = [vp, u64, vp, u64, ctypes.POINTER(u64), ctypes.c_int]
+    L.df11_nf12_encode.restype = ctypes.c_int
+    L.df11_nf12_validate.argtypes = [vp, sz, ctypes.POINTER(u64)]
+    L.df11_nf12_validate.restype = ctypes.c_int
+    L.df11_nf12_decode.argtypes = [vp, vp, vp, ctypes.c_int, vp]
+    L.df11_nf12_decode.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -218,3 +227,37 @@ def check(plan: Plan, stream=None):
     """Synchronize the stream and raise DF11Error(E_CORRUPT) if a decode found
     a stream inconsistent with its index."""
     _raise(lib().df11_check(plan.handle, _stream_handle(stream)))
+
+
+# ---- NF12: the fixed-rate 12-bit format (layout in include/df11.h) --------
+
+NF12_HEADER = 256
+
+
+def nf12_encode(words, threads: int = 0) -> np.ndarray:
+    """NF12 container (uint8 numpy array, host) of BF16 bit patterns."""
+    w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
+    cap = int(lib().df11_nf12_bound(w.size))
+    out = np.empty(max(cap, 1), np.uint8)
+    nbytes = ctypes.c_uint64(0)
+    _raise(lib().df11_nf12_encode(w.ctypes.data, w.size, out.ctypes.data, cap, ctypes.byref(nbytes), threads))
+    return out[: nbytes.value]
+
+
+def nf12_validate(container) -> int:
+    """Element count of a valid NF12 container (host); raises DF11Error."""
+    c = _host_u8(container)
+    n = ctypes.c_uint64(0)
+    _raise(lib().df11_nf12_validate(c.ctypes.data, c.size, ctypes.byref(n)))
+    return int(n.value)
+
+
+def nf12_decode(host_header, container, out, device: int = 0, stream=None):
+    """Enqueue the decode of an NF12 container: host_header = host copy of
+    (at least) its first 256 bytes, container = the device copy (uint8),
+    out = device tensor of n_elems 16-bit words."""
+    h = _host_u8(host_header)
+    if h.size < NF12_HEADER:
+        raise ValueError("the NF12 header is 256 bytes")
+    _raise(lib().df11_nf12_decode(h.ctypes.data, container.data_ptr(), out.data_ptr(), device,
+                                  _stream_handle(stream)))

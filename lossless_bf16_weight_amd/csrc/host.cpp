@@ -26,7 +26,7 @@ using namespace df11;
 
 static thread_local std::string g_error = "no error";
 
-static df11_status fail(df11_status st, const char *fmt, ...) {
+df11_status df11::report_error(df11_status st, const char *fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -34,6 +34,11 @@ static df11_status fail(df11_status st, const char *fmt, ...) {
     va_end(ap);
     g_error = std::string(df11_status_str(st)) + ": " + buf;
     return st;
+}
+
+template <class... A>
+static df11_status fail(df11_status st, const char *fmt, A... args) {
+    return report_error(st, fmt, args...);
 }
 
 #define HIP_TRY(expr)                                                              \
