@@ -235,6 +235,13 @@ df11_status df11_nf12_validate(const void *container, size_t bytes, uint64_t *n_
 df11_status df11_nf12_decode(const void *host_header, const void *d_container, void *d_out,
                              int hip_device, hipStream_t stream);
 
+/* Decode n_tensors NF12 containers in as few launches as possible (up to 24
+ * tensors per launch): host_headers[t], d_containers[t] and d_outs[t] as in
+ * df11_nf12_decode (the three arrays are HOST arrays).  Every header is
+ * validated before anything is enqueued. */
+df11_status df11_nf12_decode_batch(const void *const *host_headers, const void *const *d_containers,
+                                   void *const *d_outs, int n_tensors, int hip_device, hipStream_t stream);
+
 /* ------------------------------------------------------------------- misc */
 
 /* Text of the last non-OK status on this thread (never NULL). */

@@ -55,6 +55,7 @@ EXPORTS = [
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
     "df11_nf12_bound", "df11_nf12_encode", "df11_nf12_validate", "df11_nf12_decode",
+    "df11_nf12_decode_batch",
 ]
 
 
@@ -104,6 +105,9 @@ def lib():
     L.df11_nf12_validate.restype = ctypes.c_int
     L.df11_nf12_decode.argtypes = [vp, vp, vp, ctypes.c_int, vp]
     L.df11_nf12_decode.restype = ctypes.c_int
+    L.df11_nf12_decode_batch.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                         ctypes.c_int, ctypes.c_int, vp]
+    L.df11_nf12_decode_batch.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -261,3 +265,18 @@ def nf12_decode(host_header, container, out, device: int = 0, stream=None):
         raise ValueError("the NF12 header is 256 bytes")
     _raise(lib().df11_nf12_decode(h.ctypes.data, container.data_ptr(), out.data_ptr(), device,
                                   _stream_handle(stream)))
+
+
+def nf12_decode_batch(host_headers: List, containers: List, outs: List, device: int = 0, stream=None):
+    """Enqueue the decode of several NF12 containers (host header copies,
+    device containers, device outputs), in as few launches as possible."""
+    n = len(host_headers)
+    if len(containers) != n or len(outs) != n:
+        raise ValueError("one header, one container and one output per tensor")
+    hs = [_host_u8(h) for h in host_headers]
+    if any(h.size < NF12_HEADER for h in hs):
+        raise ValueError("the NF12 header is 256 bytes")
+    hp = (ctypes.c_void_p * n)(*[h.ctypes.data for h in hs])
+    cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in containers])
+    op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
+    _raise(lib().df11_nf12_decode_batch(hp, cp, op, n, device, _stream_handle(stream)))

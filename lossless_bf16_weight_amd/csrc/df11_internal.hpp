@@ -158,13 +158,24 @@ inline Nf12Layout nf12_layout(uint64_t n, uint64_t n_escaped) {
     return L;
 }
 
-struct Nf12Args {
+// One tensor of an NF12 launch.
+struct Nf12Tensor {
     const uint8_t *slots;      // n_groups x 12 bytes
-    const uint64_t *flags;     // n_words outlier bitmaps
-    const uint32_t *prefix;    // n_words outlier counts before each bitmap word
+    const uint64_t *flags;     // outlier bitmaps, 64 groups per word
+    const uint32_t *prefix;    // outlier counts before each bitmap word
     const uint8_t *escape;     // n_escaped x 16 bytes
     uint16_t *out;             // n words
     uint64_t n, n_groups, n_escaped;
+    uint64_t word_base;        // the launch's bitmap words before this tensor's
+};
+
+// Tensors per NF12 launch (the kernel arguments hold their descriptors).
+constexpr int kNf12MaxBatch = 24;
+
+struct Nf12Args {
+    Nf12Tensor t[kNf12MaxBatch];
+    uint32_t n_tensors;
+    uint64_t n_words;          // bitmap words (64-group units) over all tensors
 };
 
 // Launches the NF12 decode kernel (nf12.hip) with at most max_grid

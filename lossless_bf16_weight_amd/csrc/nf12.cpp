@@ -196,37 +196,58 @@ extern "C" df11_status df11_nf12_validate(const void *container, size_t bytes, u
     return DF11_OK;
 }
 
-extern "C" df11_status df11_nf12_decode(const void *host_header, const void *d_container, void *d_out,
-                                        int hip_device, hipStream_t stream) {
-    Nf12Layout L;
-    df11_status st = check_header((const uint8_t *)host_header, kNf12Header, L);
-    if (st) return st;
-    if (L.n == 0) return DF11_OK;
-    if (!d_container || !d_out) return report_error(DF11_E_ARG, "NULL device pointer");
-    if (((uintptr_t)d_container & 15) || ((uintptr_t)d_out & 15))
-        return report_error(DF11_E_ARG, "device pointers must be 16-byte aligned");
-    const uintptr_t c0 = (uintptr_t)d_container, o0 = (uintptr_t)d_out;
-    if (c0 < o0 + 2 * L.n && o0 < c0 + L.total) return report_error(DF11_E_ARG, "output overlaps the container");
+extern "C" df11_status df11_nf12_decode_batch(const void *const *host_headers, const void *const *d_containers,
+                                              void *const *d_outs, int n_tensors, int hip_device,
+                                              hipStream_t stream) {
+    if (n_tensors < 0 || (n_tensors > 0 && (!host_headers || !d_containers || !d_outs)))
+        return report_error(DF11_E_ARG, "nf12_decode_batch arguments");
+    std::vector<Nf12Layout> lay(n_tensors);
+    for (int t = 0; t < n_tensors; ++t) {
+        df11_status st = check_header((const uint8_t *)host_headers[t], kNf12Header, lay[t]);
+        if (st) return st;
+        if (lay[t].n == 0) continue;
+        if (!d_containers[t] || !d_outs[t]) return report_error(DF11_E_ARG, "tensor %d: NULL device pointer", t);
+        const uintptr_t c0 = (uintptr_t)d_containers[t], o0 = (uintptr_t)d_outs[t];
+        if ((c0 & 15) || (o0 & 15)) return report_error(DF11_E_ARG, "tensor %d: device pointers must be 16-byte aligned", t);
+        if (c0 < o0 + 2 * lay[t].n && o0 < c0 + lay[t].total)
+            return report_error(DF11_E_ARG, "tensor %d: output overlaps the container", t);
+    }
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess) prev = -1;
     if (prev != hip_device && hipSetDevice(hip_device) != hipSuccess)
         return report_error(DF11_E_HIP, "hipSetDevice(%d) failed", hip_device);
     int n_cu = 0;
     hipError_t e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device);
-    if (e == hipSuccess) {
-        const uint8_t *c = (const uint8_t *)d_container;
-        Nf12Args a;
-        a.slots = c + L.off_slots;
-        a.flags = (const uint64_t *)(c + L.off_flags);
-        a.prefix = (const uint32_t *)(c + L.off_prefix);
-        a.escape = c + L.off_escape;
-        a.out = (uint16_t *)d_out;
-        a.n = L.n;
-        a.n_groups = L.n_groups;
-        a.n_escaped = L.n_escaped;
-        e = launch_nf12_decode(a, std::max(n_cu, 1) * 32, stream);
+    Nf12Args a;
+    memset(&a, 0, sizeof a);
+    auto flush = [&]() {
+        if (a.n_tensors && e == hipSuccess) e = launch_nf12_decode(a, std::max(n_cu, 1) * 32, stream);
+        memset(&a, 0, sizeof a);
+    };
+    for (int t = 0; t < n_tensors && e == hipSuccess; ++t) {
+        const Nf12Layout &L = lay[t];
+        if (L.n == 0) continue;
+        if (a.n_tensors == (uint32_t)kNf12MaxBatch) flush();
+        const uint8_t *c = (const uint8_t *)d_containers[t];
+        Nf12Tensor &T = a.t[a.n_tensors++];
+        T.slots = c + L.off_slots;
+        T.flags = (const uint64_t *)(c + L.off_flags);
+        T.prefix = (const uint32_t *)(c + L.off_prefix);
+        T.escape = c + L.off_escape;
+        T.out = (uint16_t *)d_outs[t];
+        T.n = L.n;
+        T.n_groups = L.n_groups;
+        T.n_escaped = L.n_escaped;
+        T.word_base = a.n_words;
+        a.n_words += L.n_words;
     }
+    flush();
     if (prev >= 0 && prev != hip_device) (void)hipSetDevice(prev);
     if (e != hipSuccess) return report_error(DF11_E_HIP, "NF12 decode launch: %s", hipGetErrorString(e));
     return DF11_OK;
+}
+
+extern "C" df11_status df11_nf12_decode(const void *host_header, const void *d_container, void *d_out,
+                                        int hip_device, hipStream_t stream) {
+    return df11_nf12_decode_batch(&host_header, &d_container, &d_out, 1, hip_device, stream);
 }

@@ -7,13 +7,14 @@
 // bits << 7) | fraction at bits 12i .. 12i+11; every other group is flagged
 // in a bitmap and its 8 words sit whole in an escape buffer, in group order.
 //
-// One lane per group: a wave takes 64 consecutive groups (768 bytes in, 1 KiB
-// out, both contiguous), which are exactly the 64 bits of one bitmap word, so
-// an outlier finds its escape entry from the word's prefix count plus the
-// flags below its lane (one mbcnt).  Workgroups sweep the groups
-// block-cyclically with four groups per lane in flight, like the bandwidth
-// control, since the path is bound by HBM traffic: 12 bytes read and 16
-// written per 8 weights (plus 16 escape bytes for an outlier group).
+// One lane per group: a wave takes the 64 groups of one bitmap word (768
+// bytes in, 1 KiB out, both contiguous), so an outlier finds its escape entry
+// from the word's prefix count plus a popcount of the flags below its lane.
+// A launch decodes up to kNf12MaxBatch tensors: their bitmap words form one
+// range, which workgroups sweep block-cyclically with four words per wave in
+// flight, like the bandwidth control, since the path is bound by HBM
+// traffic: 12 bytes read and 16 written per 8 weights (plus 16 escape bytes
+// for an outlier group).
 #include <hip/hip_runtime.h>
 
 #include "df11_internal.hpp"
@@ -45,44 +46,68 @@ __device__ __forceinline__ v4u expand(v3u d) {
                pair(d.z >> 8, d.z >> 20)};
 }
 
+// Moves t to the tensor of the launch that bitmap word w belongs to.  A
+// wave meets its words in increasing order, so the scan resumes where it
+// stopped (uniform per wave, in scalar registers).
+__device__ __forceinline__ void advance_to(const Nf12Args &a, uint64_t w, uint32_t &t) {
+    while (t + 1 < a.n_tensors && a.t[t + 1].word_base <= w) ++t;
+}
+
 __global__ __launch_bounds__(kNfThreads) void nf12_decode_kernel(Nf12Args a) {
     const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t below = (uint64_t(1) << lane) - 1u;
-    const uint64_t step = (uint64_t)gridDim.x * kNfThreads * kNfUnroll;
-    for (uint64_t base = (uint64_t)blockIdx.x * kNfThreads * kNfUnroll; base < a.n_groups; base += step) {
+    constexpr uint32_t kWaves = kNfThreads / 64;
+    const uint64_t step = (uint64_t)gridDim.x * kWaves * kNfUnroll;
+    uint32_t cur = 0;   // the tensor of the wave's last word
+    // workgroup-iteration i covers bitmap words [i*16, i*16+16): wave v takes
+    // words 4k + v, k < kNfUnroll, one group per lane
+    for (uint64_t base = (uint64_t)blockIdx.x * kWaves * kNfUnroll; base < a.n_words; base += step) {
         v3u slot[kNfUnroll];
         uint64_t flags[kNfUnroll];
-        uint32_t prefix[kNfUnroll];
+        uint32_t prefix[kNfUnroll], tens[kNfUnroll];
+        uint64_t group[kNfUnroll];
 #pragma unroll
         for (int k = 0; k < kNfUnroll; ++k) {
-            const uint64_t g = base + (uint64_t)kNfThreads * k + threadIdx.x;
-            if (g < a.n_groups) {
-                slot[k] = __builtin_nontemporal_load(reinterpret_cast<const v3u *>(a.slots + 12 * g));
+            const uint64_t w = base + kWaves * k + wave;
+            tens[k] = 0;
+            group[k] = ~uint64_t(0);
+            if (w < a.n_words) {
+                advance_to(a, w, cur);
+                const uint32_t t = cur;
+                const Nf12Tensor &T = a.t[t];
+                const uint64_t wl = w - T.word_base;
+                const uint64_t g = 64 * wl + lane;
+                tens[k] = t;
                 // (the wave's 64 groups share one bitmap word: scalar loads)
-                const uint32_t wd = __builtin_amdgcn_readfirstlane((uint32_t)(g >> 6));
-                flags[k] = *(const __attribute__((address_space(4))) uint64_t *)(a.flags + wd);
-                prefix[k] = *(const __attribute__((address_space(4))) uint32_t *)(a.prefix + wd);
+                flags[k] = *(const __attribute__((address_space(4))) uint64_t *)(T.flags + wl);
+                prefix[k] = *(const __attribute__((address_space(4))) uint32_t *)(T.prefix + wl);
+                if (g < T.n_groups) {
+                    group[k] = g;
+                    slot[k] = __builtin_nontemporal_load(reinterpret_cast<const v3u *>(T.slots + 12 * g));
+                }
             }
         }
 #pragma unroll
         for (int k = 0; k < kNfUnroll; ++k) {
-            const uint64_t g = base + (uint64_t)kNfThreads * k + threadIdx.x;
-            if (g >= a.n_groups) continue;
+            const uint64_t g = group[k];
+            if (g == ~uint64_t(0)) continue;
+            const Nf12Tensor &T = a.t[tens[k]];
             v4u v = expand(slot[k]);
-            if (((flags[k] >> lane) & 1u) && a.n_escaped) {
+            if (((flags[k] >> lane) & 1u) && T.n_escaped) {
                 // the escape entry of this outlier, kept inside the buffer
                 // whatever the device bytes say
                 uint64_t r = prefix[k] + (uint64_t)__builtin_popcountll(flags[k] & below);
-                r = r < a.n_escaped ? r : a.n_escaped - 1;
-                v = *reinterpret_cast<const v4u *>(a.escape + 16 * r);
+                r = r < T.n_escaped ? r : T.n_escaped - 1;
+                v = *reinterpret_cast<const v4u *>(T.escape + 16 * r);
             }
             const uint64_t j = 8 * g;
-            if (j + 8 <= a.n) {
-                __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(a.out + j));
+            if (j + 8 <= T.n) {
+                __builtin_nontemporal_store(v, reinterpret_cast<v4u *>(T.out + j));
             } else {
-                for (uint32_t i = 0; j + i < a.n; ++i) {
-                    const uint32_t w = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
-                    a.out[j + i] = (uint16_t)(w >> (16 * (i & 1u)));
+                for (uint32_t i = 0; j + i < T.n; ++i) {
+                    const uint32_t wd = i < 2 ? v.x : i < 4 ? v.y : i < 6 ? v.z : v.w;
+                    T.out[j + i] = (uint16_t)(wd >> (16 * (i & 1u)));
                 }
             }
         }
@@ -92,8 +117,8 @@ __global__ __launch_bounds__(kNfThreads) void nf12_decode_kernel(Nf12Args a) {
 }  // namespace
 
 hipError_t launch_nf12_decode(const Nf12Args &args, int max_grid, hipStream_t stream) {
-    const uint64_t per_wg = (uint64_t)kNfThreads * kNfUnroll;
-    const uint64_t need = (args.n_groups + per_wg - 1) / per_wg;
+    const uint64_t per_wg = (uint64_t)(kNfThreads / 64) * kNfUnroll;   // bitmap words per step
+    const uint64_t need = (args.n_words + per_wg - 1) / per_wg;
     const int grid = (int)(need < (uint64_t)max_grid ? need : (uint64_t)max_grid);
     if (grid == 0) return hipSuccess;
     hipLaunchKernelGGL(nf12_decode_kernel, dim3(grid), dim3(kNfThreads), 0, stream, args);

@@ -122,3 +122,26 @@ def test_bad_arguments_are_rejected():
         df11.nf12_decode(c[:256], dc, out[1:])          # misaligned output
     with pytest.raises(ValueError):
         df11.nf12_decode(c[:100], dc, out)
+
+
+def test_batch_of_mixed_sizes_split_over_launches():
+    """30 tensors (more than one launch holds), mixed sizes including empty
+    and partial groups, guard words around every output."""
+    import torch
+    log("nf12 batch of 30")
+    sizes = [0, 1, 9, 4096, 65536 + 7, 513, 8, 100003] + [3000 + 131 * i for i in range(22)]
+    ws = []
+    for i, n in enumerate(sizes):
+        w = W.normal_bf16((n,), seed=100 + i)
+        if n:
+            w[::(17 + i)] = 0
+        ws.append(w)
+    cs = [df11.nf12_encode(w) for w in ws]
+    bufs = [empty_words(max(n, 1), guard=32) for n in sizes]
+    dcs = [to_device_u8(np.pad(c, (0, 16))) for c in cs]
+    df11.nf12_decode_batch([c[:256] for c in cs], dcs, [o for _, o in bufs])
+    torch.cuda.synchronize()
+    for w, (buf, _), n in zip(ws, bufs, sizes):
+        host = buf.cpu().numpy().view(np.uint16)
+        assert (host[32:32 + n] == w).all()
+        assert (host[:32] == 0x5A5A).all() and (host[32 + max(n, 1):] == 0x5A5A).all()
