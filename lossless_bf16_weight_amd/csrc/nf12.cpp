@@ -15,7 +15,7 @@
 #include <thread>
 #include <vector>
 
-#include "df11_internal.hpp"
+#include "nf12_internal.hpp"
 
 using namespace df11;
 

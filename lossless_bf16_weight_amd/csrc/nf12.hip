@@ -17,7 +17,7 @@
 // for an outlier group).
 #include <hip/hip_runtime.h>
 
-#include "df11_internal.hpp"
+#include "nf12_internal.hpp"
 
 namespace df11 {
 
