@@ -303,3 +303,37 @@ def test_bw_control_moves_every_byte():
         df11.bw_control(src[:15], dst)                # size not a multiple of 16
     with pytest.raises(df11.DF11Error):
         df11.bw_control(src, src)                     # overlapping regions
+
+
+def test_decode_batch_replays_from_a_hip_graph():
+    """decode_batch captured into a HIP graph (three launches, each with its
+    own ticket counter slot), replayed five times with eager work and
+    synchronization in between; every replay must give exact words, so every
+    launch's last workgroup must have cleared its counter."""
+    torch = _torch()
+    log("hip graph replays")
+    sizes = [32768 * 3 + 11, 250000, 4096]
+    ws = [W.normal_bf16((n,), seed=200 + i) for i, n in enumerate(sizes)]
+    cs = oracle_encode_many(ws)
+    plan = df11.Plan(cs)
+    dcs = [to_device_u8(c) for c in cs]
+    outs = [[torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes] for _ in range(3)]
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        df11.decode_batch(plan, dcs, outs[0], stream=s)      # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for o in outs:
+            df11.decode_batch(plan, dcs, o, stream=s)
+    for rep in range(5):
+        for o in outs:
+            for t in o:
+                t.fill_(rep + 1)                               # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o in outs:
+            for w, t in zip(ws, o):
+                assert (t.cpu().numpy().view(np.uint16) == w).all(), rep
+    df11.check(plan)
