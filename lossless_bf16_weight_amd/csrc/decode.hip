@@ -88,9 +88,6 @@ static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0 && o
               "LDS alignment");
 static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
 
-__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) {
     return __builtin_amdgcn_perm(0u, x, 0x00010203u);
 }
@@ -151,10 +148,6 @@ struct LdsCodes {
     static constexpr bool kLds = true;
     const uint32_t *w;   // w[k] = staged word k-1, least significant bit first
     uint32_t pmax;       // largest P whose words are inside
-    __device__ __forceinline__ uint32_t peek(uint32_t P) const {
-        const uint32_t k = P >> 5;
-        return __builtin_amdgcn_alignbit(w[k + 1], w[k], P);
-    }
 };
 
 struct GlobalCodes {
@@ -198,37 +191,21 @@ __device__ __forceinline__ uint32_t long_entry(const LutRecord &T, uint32_t top,
 __device__ __forceinline__ uint32_t ent_count(uint32_t ent) { return ent >> kEntCountShift; }
 __device__ __forceinline__ uint32_t ent_bits(uint32_t ent) { return (ent >> kEntLenShift) & 31u; }
 
-// Both chains' look-up entries, their LDS round trips overlapped (the fences
-// keep the scheduler from serializing them: addresses | both code reads |
-// funnel shifts and table offsets | both table reads).  kClamp: clamp the
-// positions to the source.
-template <bool kClamp, class Src>
-__device__ __forceinline__ void entries(const Lds &L, const Src &src, uint32_t pa, uint32_t pb,
+// Both chains' look-up entries with the code words read from the stream in
+// global memory (chunks whose codes are not staged in LDS).  kClamp: clamp
+// the positions to the source.
+template <bool kClamp>
+__device__ __forceinline__ void entries(const Lds &L, const GlobalCodes &src, uint32_t pa, uint32_t pb,
                                         uint32_t &ea, uint32_t &eb, uint32_t &bad) {
     if (kClamp) {
         pa = min(pa, src.pmax);
         pb = min(pb, src.pmax);
     }
-    uint32_t ta, tb;
     const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
-    if constexpr (Src::kLds) {
-        const uint32_t ka = pa >> 5, kb = pb >> 5;
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t a0 = src.w[ka], a1 = src.w[ka + 1];
-        const uint32_t b0 = src.w[kb], b1 = src.w[kb + 1];
-        __builtin_amdgcn_sched_barrier(0);
-        ta = __builtin_amdgcn_alignbit(a1, a0, pa);
-        tb = __builtin_amdgcn_alignbit(b1, b0, pb);
-        const uint32_t oa = ta & ((kL1Size - 1) << 2), ob = tb & ((kL1Size - 1) << 2);
-        __builtin_amdgcn_sched_barrier(0);
-        ea = *reinterpret_cast<const uint32_t *>(l1 + oa);
-        eb = *reinterpret_cast<const uint32_t *>(l1 + ob);
-    } else {
-        ta = src.peek(pa);
-        tb = src.peek(pb);
-        ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
-        eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
-    }
+    const uint32_t ta = src.peek(pa);
+    const uint32_t tb = src.peek(pb);
+    ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
+    eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
     if (__builtin_expect((ea == 0) | (eb == 0), 0)) {
         if (ea == 0) ea = long_entry(L.lut, ta, bad);
         if (eb == 0) eb = long_entry(L.lut, tb, bad);
@@ -273,8 +250,8 @@ __device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent) {
 
 __device__ __forceinline__ uint32_t out_pos(const Chain &c) { return c.p8 >> 3; }
 
-template <class Src>
-__device__ __forceinline__ void masked_tail(Lds &L, const Src &src, Chain &A, Chain &B, int32_t &ra,
+// The masked phase for a source in global memory (see masked_window_tail).
+__device__ __forceinline__ void masked_tail(Lds &L, const GlobalCodes &src, Chain &A, Chain &B, int32_t &ra,
                                             int32_t &rb, uint32_t &ea_r, uint32_t &eb_r, uint32_t &bad) {
     uint32_t ea, eb;
     bool any = __ballot((ra > 0) | (rb > 0)) != 0;
@@ -583,8 +560,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
 
     for (uint32_t k = 0;; ++k) {
         // ---- the previous item's tile and staged words are no longer
-        //      read; this item's and the next one's records and this
-        //      item's tables are in LDS
+        //      read; this item's record and tables are in LDS
         __syncthreads();
         const uint32_t sl = k & 1u;
         if (__builtin_amdgcn_readfirstlane(L.rec_id[sl]) >= n) break;
@@ -595,9 +571,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // when every workgroup would otherwise wait for it at once.
         const bool late = k != 0;
         const Item it = item_at(a, L, sl);
-        // the next item (with none, item n-1 is loaded again: the loads
-        // stay unconditional, so the compiler can count them and wait for
-        // the oldest ones only)
+        // the next item's ticket (n and above: none; its record is then item
+        // n-1's, so that the next item's loads stay unconditional and the
+        // compiler can count them and wait for the oldest ones only)
         uint32_t t1 = n;
         if (wave == 0 && !late) t1 = take_ticket(a, lane);
 
@@ -608,14 +584,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             if (i + tid < sizeof(L.tile) / 16) reinterpret_cast<u32x4 *>(L.tile)[i + tid] = u32x4{0u, 0u, 0u, 0u};
         if (it.staged) {
 #pragma unroll
-            for (int k = 0; k < kCodeLoads; ++k) {
-                if (16u * kThreads * k + 16u * tid < (uint32_t)kCodeCap) {
-                    u32x4 v = cw[k];
+            for (int q = 0; q < kCodeLoads; ++q) {
+                if (16u * kThreads * q + 16u * tid < (uint32_t)kCodeCap) {
+                    u32x4 v = cw[q];
                     v.x = lsb_first(v.x);
                     v.y = lsb_first(v.y);
                     v.z = lsb_first(v.z);
                     v.w = lsb_first(v.w);
-                    reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * k + tid] = v;
+                    reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * q + tid] = v;
                 }
             }
         }
@@ -665,7 +641,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         Chain A{min(sa, plim) + kPosBias, qa << 3, qa + na};
         Chain B{min(sb, plim) + kPosBias, qb << 3, qb + nb};
         if (it.staged) {
-            // peeks read codes[k], codes[k+1] with k = P / 32 <= kCodeWords
+            // code-word reads: codes[k .. k+2] with k = P / 32 <= kCodeWords - 1
             const LdsCodes src{L.codes, pmax + kPosBias};
             decode_pair(L, src, A, B, T, bad);
         } else {
@@ -709,9 +685,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
 
         // ---- assemble and store the whole 2048-element blocks; each block's
         //      raw registers take the next item's bytes right after use.
-        //      Wave 0 fetches the record after next meanwhile.
-        //      The next item's code bytes are requested first: they are
-        //      needed first.
+        //      The next item's window entries, code bytes and tables are
+        //      requested first: they are needed first.
         const Item nx = item_at(a, L, sl ^ 1u);
         const u32x2 win_nx = load_windows(nx, tid);
         load_codes(nx, tid, cw);
