@@ -10,7 +10,7 @@ Prints one JSON line:
   roofline       HBM roofline of the decode kernel: algorithmic bytes per
                  launch (index + code stream + raw bytes read, BF16 written)
                  over the kernel's average duration (HIP events on the launch
-                 stream), against the MI355X peak of 8 TB/s; `traffic` holds
+                 stream around the timed steps), against the MI355X peak of 8 TB/s; `traffic` holds
                  the HBM bytes per launch measured with rocprofv3 counters
                  when they were taken on the current kernel source, else null
   bw_control     the same read and write byte counts moved by a kernel that
@@ -185,6 +185,126 @@ def jit_overlap(n_layers: int, token_counts, reps: int):
                       "results": rows}), flush=True)
 
 
+def stack_loop(passes: int, warmup: int):
+    """The just-in-time layer loop with no consumer, over the whole stack: 32
+    Llama-3-8B-shaped blocks plus the 128256x4096 embedding (7.5 G weights),
+    every container resident in HBM; one pass decodes each group in turn with
+    one batched call into a reused BF16 buffer.  Reports the sustained rate
+    over the timed passes and, from HIP events around every launch of one
+    more pass, the mean duration of a block's launch and of the embedding's.
+    With two streams, consecutive groups alternate between two streams and
+    two buffers, so that a launch's first workgroups start on the compute
+    units its predecessor's last workgroups leave free.  Every group's output
+    is compared with its source words through a SHA-256 of both."""
+    import numpy as np
+    import torch
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    groups = W.llama8b_stack_layers(32)
+    plans, dconts, counts, shas = [], [], [], []
+    read_bytes = 0
+    for g in groups:
+        ws = [s.make(threads=threads).reshape(-1) for s in g]
+        cs = [df11.encode(w, shape=s.shape, threads=threads) for w, s in zip(ws, g)]
+        shas.append([hashlib.sha256(w.view(np.uint8)).hexdigest() for w in ws])
+        counts.append([w.size for w in ws])
+        plans.append(df11.Plan(cs))
+        read_bytes += sum(i["bytes_read_per_decode"] for i in plans[-1].infos)
+        dconts.append([torch.from_numpy(c).to(dev) for c in cs])
+        del ws, cs
+    n_total = sum(sum(c) for c in counts)
+    resident = sum(int(c.numel()) for dc in dconts for c in dc)
+    words = max(sum(((n + 7) // 8) * 8 for n in c) for c in counts)
+    bufs = [torch.empty(words, dtype=torch.int16, device=dev) for _ in range(2)]
+
+    def views(buf, ci):
+        out, off = [], 0
+        for n in ci:
+            out.append(buf[off:off + n])
+            off += (n + 7) // 8 * 8
+        return out
+
+    outs = [[views(b, c) for c in counts] for b in bufs]
+    side = torch.cuda.Stream()
+    streams = [stream, side]
+    algo = read_bytes + 2 * n_total
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    joined = torch.cuda.Event()
+
+    def one_pass(n_streams):
+        # group g on stream g % n_streams, into that stream's buffer; a
+        # stream's next launch follows its own previous one, so a buffer is
+        # rewritten only after the launch before has written it
+        for g, (plan, dc) in enumerate(zip(plans, dconts)):
+            j = g % n_streams
+            df11.decode_batch(plan, dc, outs[j][g], stream=streams[j])
+
+    def timed(n_streams):
+        for _ in range(warmup):
+            one_pass(n_streams)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        side.wait_event(e0)
+        for _ in range(passes):
+            one_pass(n_streams)
+        joined.record(side)
+        stream.wait_event(joined)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        pass_ms = e0.elapsed_time(e1) / passes
+        return {"streams": n_streams, "pass_ms": round(pass_ms, 4),
+                "wall_ms_per_pass": round(wall * 1e3 / passes, 4),
+                "value": round(2 * n_total / (pass_ms * 1e-3) / 1e9, 1),
+                "hbm_GBs": round(algo / (pass_ms * 1e-3) / 1e9, 1),
+                "roofline_frac": round(algo / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+    rows = [timed(1), timed(2)]
+    # one more single-stream pass with events around every launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+    for g, ((a, b), plan, dc) in enumerate(zip(ev, plans, dconts)):
+        a.record(stream)
+        df11.decode_batch(plan, dc, outs[0][g], stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    # bit-exactness: a two-stream pass, each group checked after its launch
+    # (the stream's next launch waits for the copy)
+    exact = True
+    host = torch.empty(words, dtype=torch.int16, pin_memory=True)
+    for g, (plan, dc, ci, sh) in enumerate(zip(plans, dconts, counts, shas)):
+        j = g % 2
+        df11.decode_batch(plan, dc, outs[j][g], stream=streams[j])
+        streams[j].synchronize()
+        df11.check(plan, stream=streams[j])
+        host.copy_(bufs[j])
+        h = host.numpy().view(np.uint8)
+        off = 0
+        for n, want in zip(ci, sh):
+            exact &= hashlib.sha256(h[2 * off:2 * (off + n)]).hexdigest() == want
+            off += (n + 7) // 8 * 8
+    best = max(rows, key=lambda r: r["value"])
+    print(json.dumps({
+        "metric": "just-in-time layer loop over the resident 32-layer stack: sustained decode rate",
+        "value": best["value"], "unit": "GB/s of BF16 output", "streams": best["streams"],
+        "passes": passes, "warmup": warmup, "by_streams": rows,
+        "launches_per_pass": len(groups),
+        "block_launch_ms_mean": round(sum(launch_ms[:-1]) / (len(groups) - 1), 5),
+        "embedding_launch_ms": round(launch_ms[-1], 5),
+        "bit_exact": bool(exact),
+        "config": {"workload": "llama8b_stack", "layers": 32, "elements": n_total,
+                   "bf16_bytes": 2 * n_total, "resident_container_bytes": resident,
+                   "algorithmic_bytes_per_pass": algo},
+    }), flush=True)
+    if not exact:
+        sys.exit(1)
+
+
 def nf12_compare(reps: int = 100, warmup: int = 200):
     """NF12 (fixed-rate 12-bit groups with an escape buffer) next to DF11 on
     the workloads that fit one decode: container size relative to BF16 and
@@ -259,6 +379,8 @@ def main():
                     help="only compare the NF12 format with DF11 on the workloads")
     ap.add_argument("--jit-overlap", action="store_true",
                     help="only measure the just-in-time layer loop against its consumer")
+    ap.add_argument("--stack", action="store_true",
+                    help="only measure the layer loop over the resident 32-layer stack")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this decoder runs on one GPU "
@@ -274,6 +396,10 @@ def main():
 
     if args.jit_overlap:
         jit_overlap(n_layers=8, token_counts=(1, 256, 2048, 8192), reps=5)
+        return
+
+    if args.stack:
+        stack_loop(passes=20, warmup=10)
         return
 
     if args.copy_calibration:
@@ -311,15 +437,22 @@ def main():
         df11.decode_batch(plan, d_conts, outs, stream=stream)
     torch.cuda.synchronize()
 
-    # whole-job throughput: K back-to-back steps
+    # whole-job throughput: K back-to-back steps.  HIP events on the launch
+    # stream bracket the same steps: their interval over K is the kernel's
+    # average duration, back-to-back gaps included
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         df11.decode_batch(plan, d_conts, outs, stream=stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    avg_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # kernel duration: HIP events around each launch on the launch stream
+    # the spread of single launches: events around each of 100 more launches
+    # (each interval also holds the events' own latency)
     n_ev = min(args.steps, 100)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -329,24 +462,79 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     durs_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    avg_ms = sum(durs_ms) / len(durs_ms)
 
-    # bandwidth control: the same read and write sizes, no decoding
+    # bandwidth control: the same read and write sizes, no decoding, timed
+    # the same way (events around back-to-back launches)
     ctl_src = torch.empty((bytes_read + 15) // 16 * 16, dtype=torch.uint8, device=dev)
     ctl_src.fill_(1)
     ctl_dst = torch.empty(bytes_written, dtype=torch.uint8, device=dev)
-    for _ in range(3):
+    n_ctl = max(n_ev, 10)
+    for _ in range(n_ctl):
         df11.bw_control(ctl_src, ctl_dst, stream=stream)
-    c_starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    c_ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    for i in range(n_ev):
-        c_starts[i].record(stream)
+    ev0.record(stream)
+    for _ in range(n_ctl):
         df11.bw_control(ctl_src, ctl_dst, stream=stream)
-        c_ends[i].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
-    ctl_ms = sum(s.elapsed_time(e) for s, e in zip(c_starts, c_ends)) / n_ev
-    ctl_gbs = (ctl_src.numel() + ctl_dst.numel()) / (ctl_ms * 1e-3) / 1e9
-    del ctl_src, ctl_dst
+    ctl_ms = ev0.elapsed_time(ev1) / n_ctl
+    ctl_bytes = ctl_src.numel() + ctl_dst.numel()
+    ctl_gbs = ctl_bytes / (ctl_ms * 1e-3) / 1e9
+
+    # ablation: the same steps with the reads never in the last-level cache.
+    # Eight copies of the inputs (2.4 GB of containers, 2.4 GB of control
+    # source) are used in turn, so the bytes a step reads were last touched
+    # 7 steps (5 GB of traffic) earlier, as in a pass over distinct layers
+    n_copy = 8
+    cold_conts = [[c.clone() for c in d_conts] for _ in range(n_copy)]
+    cold_src = [ctl_src.clone() for _ in range(n_copy)]
+    n_cold = max(n_ev, 10) // n_copy * n_copy
+
+    def cold_rate(fn):
+        for i in range(n_cold):
+            fn(i % n_copy)
+        ev0.record(stream)
+        for i in range(n_cold):
+            fn(i % n_copy)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_cold
+
+    cold_ms = cold_rate(lambda k: df11.decode_batch(plan, cold_conts[k], outs, stream=stream))
+    cold_ctl_ms = cold_rate(lambda k: df11.bw_control(cold_src[k], ctl_dst, stream=stream))
+    df11.check(plan, stream=stream)
+    cold_exact = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) for w, o in zip(words, outs))
+    del cold_conts, cold_src, ctl_src, ctl_dst
+
+    # the same steps on two streams in turn, each with its own outputs: a
+    # launch's first workgroups start while its predecessor's last ones
+    # finish (what a pass over many layers can do)
+    side = torch.cuda.Stream()
+    outs2 = [torch.empty_like(o) for o in outs]
+    n_two = max(n_ev, 10) // 2 * 2
+
+    def two_streams():
+        for i in range(n_two):
+            if i & 1:
+                df11.decode_batch(plan, d_conts, outs2, stream=side)
+            else:
+                df11.decode_batch(plan, d_conts, outs, stream=stream)
+
+    for _ in range(2):
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        side.wait_event(ev0)
+        two_streams()
+        joined = torch.cuda.Event()
+        joined.record(side)
+        stream.wait_event(joined)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+    two_ms = ev0.elapsed_time(ev1) / n_two
+    df11.check(plan, stream=stream)
+    two_exact = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) and
+                    torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o2)
+                    for w, o, o2 in zip(words, outs, outs2))
+    del outs2
 
     # bit-exact against the source words
     df11.check(plan, stream=stream)
@@ -388,7 +576,8 @@ def main():
             "traffic": traffic,
             "kernel": "df11::decode_kernel",
             "kernel_ms_avg": round(avg_ms, 5),
-            "kernel_ms_min": round(durs_ms[0], 5),
+            "kernel_ms_single_launch_median": round(durs_ms[len(durs_ms) // 2], 5),
+            "kernel_ms_single_launch_min": round(durs_ms[0], 5),
         },
         # the same bytes moved with no decoding (df11_bw_control): the HBM
         # rate this access pattern reaches on this GPU
@@ -399,6 +588,27 @@ def main():
             "frac_of_peak": round(ctl_gbs / PEAK_HBM_GBS, 4),
             "decode_over_control": round(achieved / ctl_gbs, 4),
         },
+        # ablation: inputs rotated over 8 copies, none in the last-level cache
+        "cold_inputs": {
+            "copies": n_copy,
+            "kernel_ms_avg": round(cold_ms, 5),
+            "value": round(bytes_written / (cold_ms * 1e-3) / 1e9, 1),
+            "hbm_GBs": round(algo_bytes / (cold_ms * 1e-3) / 1e9, 1),
+            "frac": round(algo_bytes / (cold_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bw_control_ms": round(cold_ctl_ms, 5),
+            "bw_control_GBs": round(ctl_bytes / (cold_ctl_ms * 1e-3) / 1e9, 1),
+            "decode_over_control": round(algo_bytes / cold_ms / (ctl_bytes / cold_ctl_ms), 4),
+            "bit_exact": bool(cold_exact),
+        },
+        # ablation: consecutive steps alternate between two streams and two
+        # output sets, so that launches overlap at their ends
+        "two_streams": {
+            "ms_per_step": round(two_ms, 5),
+            "value": round(bytes_written / (two_ms * 1e-3) / 1e9, 1),
+            "hbm_GBs": round(algo_bytes / (two_ms * 1e-3) / 1e9, 1),
+            "frac": round(algo_bytes / (two_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bit_exact": bool(two_exact),
+        },
     }
     # the host encoder (a multi-threaded C++ pass, byte-identical to the
     # oracle's containers), on the same tensors: context, not the metric
@@ -407,7 +617,7 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(conts, infos)
     print(json.dumps(result), flush=True)
-    if not exact:
+    if not (exact and cold_exact and two_exact):
         sys.exit(1)
 
 
