@@ -189,13 +189,14 @@ def stack_loop(passes: int, warmup: int):
     """The just-in-time layer loop with no consumer, over the whole stack: 32
     Llama-3-8B-shaped blocks plus the 128256x4096 embedding (7.5 G weights),
     every container resident in HBM; one pass decodes each group in turn with
-    one batched call into a reused BF16 buffer.  Reports the sustained rate
-    over the timed passes and, from HIP events around every launch of one
-    more pass, the mean duration of a block's launch and of the embedding's.
-    With two streams, consecutive groups alternate between two streams and
-    two buffers, so that a launch's first workgroups start on the compute
-    units its predecessor's last workgroups leave free.  Every group's output
-    is compared with its source words through a SHA-256 of both."""
+    one batched call into a reused BF16 buffer.  Both formats: DF11 and the
+    fixed-rate NF12.  Reports the sustained rate over the timed passes and,
+    from HIP events around every launch of one more pass, the mean duration
+    of a block's launch and of the embedding's.  With two streams,
+    consecutive groups alternate between two streams and two buffers, so
+    that a launch's first workgroups start on the compute units its
+    predecessor's last workgroups leave free.  Every group's output is
+    compared with its source words through a SHA-256 of both."""
     import numpy as np
     import torch
     import lossless_bf16_weight_amd as df11
@@ -205,19 +206,28 @@ def stack_loop(passes: int, warmup: int):
     stream = torch.cuda.current_stream()
     threads = max(1, min(16, os.cpu_count() or 1))
     groups = W.llama8b_stack_layers(32)
-    plans, dconts, counts, shas = [], [], [], []
-    read_bytes = 0
+    plans, dconts, hdrs, nconts, counts, shas = [], [], [], [], [], []
+    read = {"df11": 0, "nf12": 0}
+    stored = {"df11": 0, "nf12": 0}
     for g in groups:
         ws = [s.make(threads=threads).reshape(-1) for s in g]
         cs = [df11.encode(w, shape=s.shape, threads=threads) for w, s in zip(ws, g)]
+        ns = [df11.nf12_encode(w, threads=threads) for w in ws]
         shas.append([hashlib.sha256(w.view(np.uint8)).hexdigest() for w in ws])
         counts.append([w.size for w in ws])
         plans.append(df11.Plan(cs))
-        read_bytes += sum(i["bytes_read_per_decode"] for i in plans[-1].infos)
+        read["df11"] += sum(i["bytes_read_per_decode"] for i in plans[-1].infos)
+        stored["df11"] += sum(c.size for c in cs)
+        for c, w in zip(ns, ws):
+            n_groups = (w.size + 7) // 8
+            n_esc = int(c[32:40].view(np.uint64)[0])
+            read["nf12"] += 12 * n_groups + 16 * n_esc + 12 * ((n_groups + 63) // 64)
+            stored["nf12"] += c.size
         dconts.append([torch.from_numpy(c).to(dev) for c in cs])
-        del ws, cs
+        hdrs.append([c[:256].copy() for c in ns])
+        nconts.append([torch.from_numpy(c).to(dev) for c in ns])
+        del ws, cs, ns
     n_total = sum(sum(c) for c in counts)
-    resident = sum(int(c.numel()) for dc in dconts for c in dc)
     words = max(sum(((n + 7) // 8) * 8 for n in c) for c in counts)
     bufs = [torch.empty(words, dtype=torch.int16, device=dev) for _ in range(2)]
 
@@ -231,27 +241,33 @@ def stack_loop(passes: int, warmup: int):
     outs = [[views(b, c) for c in counts] for b in bufs]
     side = torch.cuda.Stream()
     streams = [stream, side]
-    algo = read_bytes + 2 * n_total
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     joined = torch.cuda.Event()
 
-    def one_pass(n_streams):
+    def launch(fmt, g, j, st):
+        if fmt == "df11":
+            df11.decode_batch(plans[g], dconts[g], outs[j][g], stream=st)
+        else:
+            df11.nf12_decode_batch(hdrs[g], nconts[g], outs[j][g], stream=st)
+
+    def one_pass(fmt, n_streams):
         # group g on stream g % n_streams, into that stream's buffer; a
         # stream's next launch follows its own previous one, so a buffer is
         # rewritten only after the launch before has written it
-        for g, (plan, dc) in enumerate(zip(plans, dconts)):
+        for g in range(len(groups)):
             j = g % n_streams
-            df11.decode_batch(plan, dc, outs[j][g], stream=streams[j])
+            launch(fmt, g, j, streams[j])
 
-    def timed(n_streams):
+    def timed(fmt, n_streams):
+        algo = read[fmt] + 2 * n_total
         for _ in range(warmup):
-            one_pass(n_streams)
+            one_pass(fmt, n_streams)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         e0.record(stream)
         side.wait_event(e0)
         for _ in range(passes):
-            one_pass(n_streams)
+            one_pass(fmt, n_streams)
         joined.record(side)
         stream.wait_event(joined)
         e1.record(stream)
@@ -264,44 +280,52 @@ def stack_loop(passes: int, warmup: int):
                 "hbm_GBs": round(algo / (pass_ms * 1e-3) / 1e9, 1),
                 "roofline_frac": round(algo / (pass_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
-    rows = [timed(1), timed(2)]
-    # one more single-stream pass with events around every launch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
-    for g, ((a, b), plan, dc) in enumerate(zip(ev, plans, dconts)):
-        a.record(stream)
-        df11.decode_batch(plan, dc, outs[0][g], stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    # bit-exactness: a two-stream pass, each group checked after its launch
-    # (the stream's next launch waits for the copy)
-    exact = True
-    host = torch.empty(words, dtype=torch.int16, pin_memory=True)
-    for g, (plan, dc, ci, sh) in enumerate(zip(plans, dconts, counts, shas)):
-        j = g % 2
-        df11.decode_batch(plan, dc, outs[j][g], stream=streams[j])
-        streams[j].synchronize()
-        df11.check(plan, stream=streams[j])
-        host.copy_(bufs[j])
-        h = host.numpy().view(np.uint8)
-        off = 0
-        for n, want in zip(ci, sh):
-            exact &= hashlib.sha256(h[2 * off:2 * (off + n)]).hexdigest() == want
-            off += (n + 7) // 8 * 8
-    best = max(rows, key=lambda r: r["value"])
+    def per_launch(fmt):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
+        for g, (a, b) in enumerate(ev):
+            a.record(stream)
+            launch(fmt, g, 0, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return round(sum(ms[:-1]) / (len(ms) - 1), 5), round(ms[-1], 5)
+
+    def exact(fmt):
+        # a two-stream pass, each group checked after its launch (the
+        # stream's next launch is enqueued after the copy)
+        ok = True
+        host = torch.empty(words, dtype=torch.int16, pin_memory=True)
+        for g in range(len(groups)):
+            j = g % 2
+            launch(fmt, g, j, streams[j])
+            streams[j].synchronize()
+            if fmt == "df11":
+                df11.check(plans[g], stream=streams[j])
+            host.copy_(bufs[j])
+            h = host.numpy().view(np.uint8)
+            off = 0
+            for n, want in zip(counts[g], shas[g]):
+                ok &= hashlib.sha256(h[2 * off:2 * (off + n)]).hexdigest() == want
+                off += (n + 7) // 8 * 8
+        return bool(ok)
+
+    res = {}
+    for fmt in ("df11", "nf12"):
+        rows = [timed(fmt, 1), timed(fmt, 2)]
+        blk, emb = per_launch(fmt)
+        res[fmt] = {"size_vs_bf16": round(stored[fmt] / (2 * n_total), 4),
+                    "resident_bytes": stored[fmt], "algorithmic_bytes_per_pass": read[fmt] + 2 * n_total,
+                    "by_streams": rows, "block_launch_ms_mean": blk, "embedding_launch_ms": emb,
+                    "bit_exact": exact(fmt)}
+    best = max(res["df11"]["by_streams"], key=lambda r: r["value"])
     print(json.dumps({
         "metric": "just-in-time layer loop over the resident 32-layer stack: sustained decode rate",
         "value": best["value"], "unit": "GB/s of BF16 output", "streams": best["streams"],
-        "passes": passes, "warmup": warmup, "by_streams": rows,
-        "launches_per_pass": len(groups),
-        "block_launch_ms_mean": round(sum(launch_ms[:-1]) / (len(groups) - 1), 5),
-        "embedding_launch_ms": round(launch_ms[-1], 5),
-        "bit_exact": bool(exact),
-        "config": {"workload": "llama8b_stack", "layers": 32, "elements": n_total,
-                   "bf16_bytes": 2 * n_total, "resident_container_bytes": resident,
-                   "algorithmic_bytes_per_pass": algo},
+        "passes": passes, "warmup": warmup, "launches_per_pass": len(groups),
+        "config": {"workload": "llama8b_stack", "layers": 32, "elements": n_total, "bf16_bytes": 2 * n_total},
+        "df11": res["df11"], "nf12": res["nf12"],
     }), flush=True)
-    if not exact:
+    if not (res["df11"]["bit_exact"] and res["nf12"]["bit_exact"]):
         sys.exit(1)
 
 
