@@ -329,6 +329,94 @@ def stack_loop(passes: int, warmup: int):
         sys.exit(1)
 
 
+def workload_table(rounds: int = 3):
+    """DF11 decode time of every single-decode workload: one batched call
+    over the workload's tensors per rep.  "warm": back-to-back reps between
+    two events, per round (after 400 warm-up reps, as the part runs slower
+    for its first few hundred back-to-back launches); "flushed": each rep
+    alone between its own events, after a pass that reads 1 GiB of other
+    data (the bandwidth control with a 16-byte output), so that the
+    containers come from HBM and the last-level cache holds only clean
+    lines; "write_flushed": the same after 1 GiB of writes instead, whose
+    dirty lines the decode's own traffic then writes back.  Medians over
+    rounds (warm) or reps, with min and max; every output compared with the
+    source words."""
+    import numpy as np
+    import torch
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+    flush.fill_(1)
+    sink = torch.empty(16, dtype=torch.uint8, device=dev)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    rows = []
+    for name in ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
+        specs = W.WORKLOADS[name]()
+        words = [s.make(threads=threads).reshape(-1) for s in specs]
+        n = sum(w.size for w in words)
+        conts = [df11.encode(w, shape=s.shape, threads=threads) for w, s in zip(words, specs)]
+        plan = df11.Plan(conts)
+        algo = sum(i["bytes_read_per_decode"] for i in plan.infos) + 2 * n
+        dc = [torch.from_numpy(c).to(dev) for c in conts]
+        outs = [torch.empty(w.size, dtype=torch.int16, device=dev) for w in words]
+
+        def run():
+            df11.decode_batch(plan, dc, outs, stream=stream)
+
+        reps = 200 if n <= (1 << 22) else 20
+        for _ in range(400):
+            run()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm = []
+        for _ in range(rounds):
+            a.record(stream)
+            for _ in range(reps):
+                run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            warm.append(a.elapsed_time(b) / reps)
+        cold, wcold = [], []
+        for _ in range(5 * rounds):
+            df11.bw_control(flush, sink, stream=stream)
+            a.record(stream)
+            run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        for _ in range(5 * rounds):
+            flush.fill_(1)
+            a.record(stream)
+            run()
+            b.record(stream)
+            torch.cuda.synchronize()
+            wcold.append(a.elapsed_time(b))
+        df11.check(plan, stream=stream)
+        ok = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) for w, o in zip(words, outs))
+
+        def stats(v):
+            v = sorted(v)
+            med = v[len(v) // 2]
+            return {"ms_median": round(med, 5), "ms_min": round(v[0], 5), "ms_max": round(v[-1], 5),
+                    "bf16_GBs": round(2 * n / (med * 1e-3) / 1e9, 1),
+                    "hbm_GBs": round(algo / (med * 1e-3) / 1e9, 1),
+                    "frac": round(algo / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+        rows.append({"workload": name, "tensors": len(words), "elements": n,
+                     "chunks": sum((i["n_elems"] + 32767) // 32768 for i in plan.infos),
+                     "ratio": round(sum(c.size for c in conts) / (2 * n), 4),
+                     "algorithmic_bytes": algo, "warm": stats(warm), "flushed": stats(cold),
+                     "write_flushed": stats(wcold),
+                     "bit_exact": bool(ok)})
+        del dc, outs, plan
+    print(json.dumps({"metric": "DF11 decode of each workload: one batched call, warm and with the "
+                                "last-level cache flushed", "results": rows}), flush=True)
+    if not all(r["bit_exact"] for r in rows):
+        sys.exit(1)
+
+
 def nf12_compare(reps: int = 100, warmup: int = 200):
     """NF12 (fixed-rate 12-bit groups with an escape buffer) next to DF11 on
     the workloads that fit one decode: container size relative to BF16 and
@@ -403,6 +491,8 @@ def main():
                     help="only compare the NF12 format with DF11 on the workloads")
     ap.add_argument("--jit-overlap", action="store_true",
                     help="only measure the just-in-time layer loop against its consumer")
+    ap.add_argument("--workloads", action="store_true",
+                    help="only time the DF11 decode of every single-decode workload, warm and flushed")
     ap.add_argument("--stack", action="store_true",
                     help="only measure the layer loop over the resident 32-layer stack")
     args = ap.parse_args()
@@ -424,6 +514,10 @@ def main():
 
     if args.stack:
         stack_loop(passes=20, warmup=10)
+        return
+
+    if args.workloads:
+        workload_table()
         return
 
     if args.copy_calibration:
