@@ -11,22 +11,21 @@
  * bit.  The weights stay compressed in GPU memory and are decoded on the GPU
  * when they are needed (mlx-dfloat project page, introduction).
  *
- * Container version 3 (one tensor = one container = one code table; all
+ * Container version 4 (one tensor = one container = one code table; all
  * integers little-endian; every section starts on a 256-byte boundary):
  *
  *   header (512 bytes)
- *      0 char[8] magic "DF11HIPC"    8 u32 version = 3      12 u32 flags = 0
+ *      0 char[8] magic "DF11HIPC"    8 u32 version = 4      12 u32 flags = 0
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
  *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 0
  *     98 u16 windows = 512         100 u32 n_chunks       104 u64 total_bits
- *    112 u64 off_chunk_index       120 u64 off_win_gap    128 u64 off_win_cnt
+ *    112 u64 off_chunk_index       120 u64 off_windows    128 u64 0
  *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
  *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
  *    208 u8 code_len[256]          464 u8[48] 0
  *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
  *                entry is { total_bits, n_elems }
- *   window gap   n_chunks x 512 x u8
- *   window cnt   n_chunks x 512 x u16
+ *   windows      n_chunks x 512 x u16: cnt | (gap << 11)
  *   stream       the exponent codes, concatenated, most significant bit first
  *                (bit 7 of byte 0 is the first bit); ceil(total_bits/8) bytes
  *                rounded up to 16, plus 16 zero bytes
@@ -43,8 +42,11 @@
  * They are cut into 512 windows as evenly as integers allow: window i is
  * [b0 + floor(i*N/512), b0 + floor((i+1)*N/512)), so every window has
  * floor(N/512) or ceil(N/512) bits.  cnt[c][i] counts the codes that START in
- * window i; gap[c][i] is the offset of the first of them from the window
- * start (always < 24), or 0xFF when cnt is 0.  The first code of window i is
+ * window i (at most 1536, a window's largest bit count, so 11 bits); gap[c][i]
+ * is the offset of the first of them from the window start (always < 24, 5
+ * bits), and 0 when cnt is 0.  One 16-bit entry per window holds both: a
+ * smaller block index in the spirit of the df11pack page's experimental 8-bit
+ * index ("Beyond the official format").  The first code of window i is
  * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
  * the windows.  The decoder gives one 256-lane workgroup to a chunk and two
  * neighbouring windows to each lane, and forms the prefix sum with one
@@ -102,7 +104,7 @@ typedef struct {
  * window count, code lengths <= 24, Kraft sum (exactly 1, or 1/2 for a single
  * symbol), section offsets and sizes, start bits monotone with out_elem =
  * 32768*c, per chunk: sum of cnt = chunk size, gap < 24 when cnt > 0, gap =
- * 0xFF when cnt = 0, and a window's codes fit its share of the stream.
+ * 0 when cnt = 0, and a window's codes fit its share of the stream.
  * `info` may be NULL.  Reads only; allocates nothing on the device.
  * Returns DF11_OK, DF11_E_ARG, DF11_E_FORMAT or DF11_E_UNSUPPORTED. */
 df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info);
@@ -110,7 +112,7 @@ df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info 
 /* Size bound of the container for n elements (any data). */
 uint64_t df11_container_bound(uint64_t n_elems);
 
-/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-3
+/* Encode n BF16 words (HOST memory, uint16 bit patterns) into a version-4
  * container in HOST memory `out` (capacity `out_cap`, at least
  * df11_container_bound(n)).  dims[ndim] is the shape (ndim <= 8, product =
  * n; ndim = 0 means a scalar, n = 1).  `threads` = 0 uses every hardware

@@ -132,7 +132,7 @@ def container_bound(n: int) -> int:
 
 def encode(words, shape=None, threads: int = 0) -> np.ndarray:
     """Encode BF16 bit patterns (uint16/int16 numpy array, host) into a
-    version-3 container (uint8 numpy array)."""
+    version-4 container (uint8 numpy array)."""
     w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
     shape = tuple(np.asarray(words).shape) if shape is None else tuple(shape)
     dims = (ctypes.c_uint64 * max(1, len(shape)))(*shape)

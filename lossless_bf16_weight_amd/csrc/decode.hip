@@ -64,6 +64,16 @@ static_assert(2 * kThreads == kWindows, "two windows per lane");
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Global memory, named as such: loads and stores through these pointers are
+// global instructions, never flat ones (a flat store also counts against the
+// LDS wait counter, so every LDS wait after it would wait for the store too),
+// whatever the compiler can infer about where a pointer points.
+#define GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ GLOBAL T *global(T *p) {
+    return (GLOBAL T *)p;
+}
+
 // LDS of one workgroup.  Staged code word k (first stream bit lowest) sits
 // in codes[k + 1], with codes[1] 16-byte aligned; the 12 bytes in front keep
 // codes[0] inside the struct.  The tile's and the tables' bases fold into
@@ -152,7 +162,7 @@ struct LdsCodes {
 
 struct GlobalCodes {
     static constexpr bool kLds = false;
-    const uint32_t *w;   // w[k] = stream word k-1, as stored
+    const GLOBAL uint32_t *w;   // w[k] = stream word k-1, as stored
     uint32_t pmax;
     __device__ __forceinline__ uint32_t peek(uint32_t P) const {
         const uint32_t k = P >> 5;
@@ -422,11 +432,10 @@ __device__ __forceinline__ u32x2 tile_pair(const Lds &L, uint32_t dw, uint32_t p
 
 // One work item (a chunk of a tensor) and where its bytes are.
 struct Item {
-    const uint8_t *stream;   // the staged stream bytes
-    const uint8_t *raw;      // raw bytes from the chunk's first element
-    const uint8_t *gap;      // the chunk's window gaps
-    const uint8_t *cnt;      // the chunk's window counts
-    uint16_t *out;           // output from the chunk's first element
+    const GLOBAL uint8_t *stream;   // the staged stream bytes
+    const GLOBAL uint8_t *raw;      // raw bytes from the chunk's first element
+    const GLOBAL uint8_t *win;      // the chunk's window entries
+    GLOBAL uint16_t *out;           // output from the chunk's first element
     uint32_t rel0, nbits;    // the chunk's stream bits, relative to the staged bytes
     uint32_t s_len;          // staged bytes
     uint32_t staged;         // the chunk's codes go through LDS
@@ -451,16 +460,15 @@ __device__ __forceinline__ Item item_at(const DecodeArgs &a, const Lds &L, uint3
     }
     // fields in ChunkRec order
     const uint64_t stream_off = f[0] | (uint64_t)f[1] << 32, raw_off = f[2] | (uint64_t)f[3] << 32;
-    const uint64_t gap_off = f[4] | (uint64_t)f[5] << 32, cnt_off = f[6] | (uint64_t)f[7] << 32;
+    const uint64_t win_off = f[4] | (uint64_t)f[5] << 32;
     const uint32_t tensor = f[14], chunk = f[15];
     const uint32_t tl = tensor - a.tensor_base;
-    const uint8_t *C = a.containers[tl];
+    const GLOBAL uint8_t *C = global(a.containers[tl]);
     Item it;
     it.stream = C + stream_off;
     it.raw = C + raw_off;
-    it.gap = C + gap_off;
-    it.cnt = C + cnt_off;
-    it.out = a.outs[tl] + (uint64_t)chunk * kChunk;
+    it.win = C + win_off;
+    it.out = global(a.outs[tl]) + (uint64_t)chunk * kChunk;
     it.rel0 = f[8];
     it.nbits = f[9];
     it.s_len = f[10] & ~kStagedBit;
@@ -475,7 +483,7 @@ static_assert(offsetof(ChunkRec, rel0) == 32 && offsetof(ChunkRec, tensor) == 56
 
 // Wave 0 fetches a chunk record (lanes 0..3: 16 bytes each) ...
 __device__ __forceinline__ u32x4 fetch_rec(const DecodeArgs &a, uint32_t item, uint32_t lane) {
-    return reinterpret_cast<const u32x4 *>(a.recs + item)[lane & 3u];
+    return reinterpret_cast<const GLOBAL u32x4 *>(global(a.recs) + item)[lane & 3u];
 }
 // ... and later puts it in its LDS slot.
 __device__ __forceinline__ void put_rec(Lds &L, uint32_t slot, u32x4 v, uint32_t id, uint32_t lane) {
@@ -495,7 +503,7 @@ __device__ __forceinline__ uint32_t take_ticket(const DecodeArgs &a, uint32_t la
 constexpr int kLutLoads = (int)((sizeof(LutRecord) / 16 + kThreads - 1) / kThreads);
 static_assert(sizeof(LutRecord) % 16 == 0, "table record size");
 __device__ __forceinline__ void load_lut(const DecodeArgs &a, uint32_t lut, uint32_t tid, u32x4 (&lr)[kLutLoads]) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.luts + lut);
+    const GLOBAL u32x4 *src = reinterpret_cast<const GLOBAL u32x4 *>(global(a.luts) + lut);
 #pragma unroll
     for (int k = 0; k < kLutLoads; ++k)
         lr[k] = src[min(kThreads * k + tid, (uint32_t)(sizeof(LutRecord) / 16 - 1))];
@@ -511,12 +519,12 @@ __device__ __forceinline__ void put_lut(Lds &L, uint32_t tid, const u32x4 (&lr)[
 // chunk's bytes the address repeats (a cache hit, no extra HBM traffic) so
 // that the load count stays fixed.
 __device__ __forceinline__ void load_codes(const Item &it, uint32_t tid, u32x4 (&cw)[kCodeLoads]) {
-    const uint8_t *stream = it.stream;
+    const GLOBAL uint8_t *stream = it.stream;
 #pragma unroll
     for (int k = 0; k < kCodeLoads; ++k) {
         const uint32_t off = min(16u * kThreads * k + 16u * tid, it.s_len - 16u);
         // (non-temporal: plain loads measured about 6% slower overall)
-        cw[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(stream + off));
+        cw[k] = __builtin_nontemporal_load(reinterpret_cast<const GLOBAL u32x4 *>(stream + off));
     }
 }
 
@@ -526,15 +534,14 @@ __device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t tid, int b) {
     uint32_t j = kBlockElems * b + 8u * tid;
     if (it.nc != (uint32_t)kChunk) j = min(j, (it.raw_left - 8u) & ~7u);
     // (a plain load: the non-temporal hint measured about 8% slower here)
-    return *reinterpret_cast<const u32x2 *>(it.raw + j);
+    return *reinterpret_cast<const GLOBAL u32x2 *>(it.raw + j);
 }
 
-// The index entries of this lane's windows 2 tid and 2 tid + 1: x = both
-// gaps (low byte: window 2 tid), y = both code counts (low half: window
-// 2 tid).  (Non-temporal, as the code bytes: about 1% faster here.)
-__device__ __forceinline__ u32x2 load_windows(const Item &it, uint32_t tid) {
-    return u32x2{__builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(it.gap) + tid),
-                 __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(it.cnt) + tid)};
+// The index entries of this lane's windows 2 tid (low half) and 2 tid + 1
+// (high half), each count | gap << kWinGapShift.  (Non-temporal, as the
+// code bytes: about 1% faster here.)
+__device__ __forceinline__ uint32_t load_windows(const Item &it, uint32_t tid) {
+    return __builtin_nontemporal_load(reinterpret_cast<const GLOBAL uint32_t *>(it.win) + tid);
 }
 
 __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
@@ -552,7 +559,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     u32x4 cw[kCodeLoads];
     u32x2 rw[kBlocks];
     u32x4 lr[kLutLoads];
-    u32x2 win;
+    uint32_t win;
+    // the second item's ticket, taken at once (its round trip overlaps the
+    // first record's): at the end of the first decode every workgroup would
+    // otherwise wait for the ticket counter at the same time
     if (wave == 0) {
         const uint32_t i0 = blockIdx.x;
         const u32x4 r0 = fetch_rec(a, min(i0, n - 1), lane);
@@ -582,12 +592,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // that at the end of the launch no workgroup holds a chunk in reserve
         // while others have run out (about 3% faster than taking it one chunk
         // ahead); only a workgroup's first chunk takes it before decoding,
-        // when every workgroup would otherwise wait for it at once.
+        // when every workgroup would otherwise wait for it at once.  (A
+        // ticket of n or above: no item; its record is then item n-1's, so
+        // that the next item's loads stay unconditional and the compiler can
+        // count them and wait for the oldest ones only.)
         const bool late = k != 0;
         const Item it = item_at(a, L, sl);
-        // the next item's ticket (n and above: none; its record is then item
-        // n-1's, so that the next item's loads stay unconditional and the
-        // compiler can count them and wait for the oldest ones only)
         uint32_t t1 = n;
         if (wave == 0 && !late) t1 = take_ticket(a, lane);
 
@@ -614,10 +624,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         //      Stream positions are bit offsets from the staged first byte.
         const uint32_t b0 = it.rel0, b1 = it.rel0 + it.nbits;
         const uint32_t nc = it.nc;
-        uint32_t na = win.y & 0xFFFFu, nb = win.y >> 16;
+        uint32_t na = win & kWinCntMask, nb = (win >> 16) & kWinCntMask;
         const uint32_t incl = wave_inclusive_sum(na + nb);
-        const uint32_t sa = b0 + window_edge(it.nbits, 2 * tid) + (na ? (win.x & 0xFFu) : 0u);
-        const uint32_t sb = b0 + window_edge(it.nbits, 2 * tid + 1) + (nb ? ((win.x >> 8) & 0xFFu) : 0u);
+        const uint32_t sa = b0 + window_edge(it.nbits, 2 * tid) + ((win >> kWinGapShift) & 31u);
+        const uint32_t sb = b0 + window_edge(it.nbits, 2 * tid + 1) + (win >> (16 + kWinGapShift));
         // the wave's code total and first code, for the waves above it
         const uint64_t mask = __ballot(na + nb != 0);
         const uint32_t first = na ? sa : sb;          // this lane's first code
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             decode_pair(L, l2, src, A, B, T, bad);
         } else {
             // peeks read words k-1 and k of the stream from s0, k < n_words
-            const GlobalCodes src{reinterpret_cast<const uint32_t *>(it.stream) - 1, pmax + kPosBias};
+            const GlobalCodes src{reinterpret_cast<const GLOBAL uint32_t *>(it.stream) - 1, pmax + kPosBias};
             decode_pair(L, l2, src, A, B, T, bad);
         }
         const uint32_t ea = A.P - kPosBias;
@@ -704,10 +714,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         //      The next item's window entries, code bytes and tables are
         //      requested first: they are needed first.
         const Item nx = item_at(a, L, sl ^ 1u);
-        const u32x2 win_nx = load_windows(nx, tid);
+        const uint32_t win_nx = load_windows(nx, tid);
         load_codes(nx, tid, cw);
         load_lut(a, nx.lut, tid, lr);
-        uint16_t *o = it.out;
+        GLOBAL uint16_t *o = it.out;
         const uint32_t full = nc / kBlockElems;
         // lanes whose first dword opens a 32-dword group (tid % 16 == 0) OR
         // in the pad before it
@@ -717,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             if ((uint32_t)b < full) {
                 const uint32_t j = kBlockElems * b + 8 * tid;
                 const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
-                __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<u32x4 *>(o + j));
+                __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<GLOBAL u32x4 *>(o + j));
             }
             rw[b] = load_raw(nx, tid, b);
         }
@@ -725,11 +735,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         if (full * kBlockElems < nc) {
             const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
-                const u32x2 r8 = *reinterpret_cast<const u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
+                const u32x2 r8 = *reinterpret_cast<const GLOBAL u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
                 const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
                 const u32x4 v = join8(t8, r8);
                 if (j + 8 <= nc) {
-                    *reinterpret_cast<u32x4 *>(o + j) = v;
+                    *reinterpret_cast<GLOBAL u32x4 *>(o + j) = v;
                 } else {
                     for (uint32_t k = 0; j + k < nc; ++k) {
                         const uint32_t wd = k < 2 ? v.x : k < 4 ? v.y : k < 6 ? v.z : v.w;

@@ -6,12 +6,19 @@
 
 namespace df11 {
 
-// Container version 3 constants (layout documented in include/df11.h).
-constexpr uint32_t kVersion = 3;
+// Container version 4 constants (layout documented in include/df11.h).
+constexpr uint32_t kVersion = 4;
 constexpr uint32_t kHeader = DF11_HEADER_BYTES;
 constexpr uint32_t kChunk = DF11_CHUNK_ELEMS;
 constexpr int kWindows = DF11_WINDOWS;
 constexpr int kMaxLen = DF11_MAX_CODE_LEN;
+// A window's 16-bit index entry: the number of codes that start in it (at
+// most 1536: a window has at most ceil(24 * kChunk / kWindows) bits) in the
+// low 11 bits, the offset of the first of them from the window's first bit
+// (under 24) in the top 5; 0 for a window with no code start.
+constexpr unsigned kWinGapShift = 11;
+constexpr unsigned kWinCntMask = (1u << kWinGapShift) - 1u;
+static_assert((24u * kChunk + kWindows - 1) / kWindows <= kWinCntMask, "window counts fit 11 bits");
 
 // Exponent bytes are handled rotated right by one bit inside the decoder,
 // rot(e) = (e >> 1) | (e & 1) << 7, so that a BF16 word splits into the two
@@ -83,8 +90,8 @@ constexpr uint32_t kCodeCap = 13 * 1024;
 struct alignas(16) ChunkRec {
     uint64_t stream_off;   // first staged stream byte (16-byte aligned)
     uint64_t raw_off;      // raw byte of the chunk's first element
-    uint64_t gap_off;      // the chunk's 512 window gaps
-    uint64_t cnt_off;      // the chunk's 512 window counts
+    uint64_t win_off;      // the chunk's 512 window entries
+    uint64_t reserved;
     uint32_t rel0;         // chunk's first stream bit - 8 * staged first byte
     uint32_t nbits;        // the chunk's stream bits
     uint32_t s_len;        // staged bytes (<= kCodeCap), bit 31: codes staged in LDS

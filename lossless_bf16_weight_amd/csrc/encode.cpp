@@ -1,4 +1,4 @@
-// libdf11 encoder: BF16 words -> version-3 container (layout in include/df11.h),
+// libdf11 encoder: BF16 words -> version-4 container (layout in include/df11.h),
 // multi-threaded on the host.
 //
 // Method: mlx-dfloat project page, introduction and 16-bit weight diagram --
@@ -161,9 +161,8 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
 
     // layout
     const uint64_t off_ci = kHeader;
-    const uint64_t off_gap = up256(off_ci + (n_chunks + 1) * 16);
-    const uint64_t off_cnt = up256(off_gap + n_chunks * kWindows);
-    const uint64_t off_stream = up256(off_cnt + n_chunks * kWindows * 2);
+    const uint64_t off_win = up256(off_ci + (n_chunks + 1) * 16);
+    const uint64_t off_stream = up256(off_win + n_chunks * kWindows * 2);
     const uint64_t stream_bytes = up16((total_bits + 7) / 8) + 16;
     const uint64_t off_raw = up256(off_stream + stream_bytes);
     const uint64_t raw_bytes = up16(n);
@@ -188,8 +187,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
     wr32(out + 100, (uint32_t)n_chunks);
     wr64(out + 104, total_bits);
     wr64(out + 112, off_ci);
-    wr64(out + 120, off_gap);
-    wr64(out + 128, off_cnt);
+    wr64(out + 120, off_win);
     wr64(out + 136, off_stream);
     wr64(out + 144, stream_bytes);
     wr64(out + 152, off_raw);
@@ -212,8 +210,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         const uint64_t nbytes = (head + (b1 - b0) + 7) / 8;
         buf.assign(nbytes + 8, 0);
         unsigned cnt[kWindows] = {};
-        uint8_t gap[kWindows];
-        memset(gap, 0xFF, sizeof gap);
+        unsigned gap[kWindows] = {};
         uint64_t acc = 0;   // pending bits, right-aligned
         unsigned nacc = head;
         uint64_t at = 0, pos = 0;   // output byte, chunk-relative bit position
@@ -221,7 +218,7 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         for (uint64_t j = lo; j < hi; ++j) {
             const unsigned e = (w[j] >> 7) & 0xFF;
             while (win + 1 < (unsigned)kWindows && window_edge(nbits, win + 1) <= pos) ++win;
-            if (cnt[win]++ == 0) gap[win] = (uint8_t)(pos - window_edge(nbits, win));
+            if (cnt[win]++ == 0) gap[win] = (unsigned)(pos - window_edge(nbits, win));
             acc = (acc << len[e]) | code[e];
             nacc += len[e];
             pos += len[e];
@@ -238,8 +235,9 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
             if (shared) __atomic_fetch_or(&stream[first + i], buf[i], __ATOMIC_RELAXED);
             else stream[first + i] = buf[i];
         }
-        memcpy(out + off_gap + c * kWindows, gap, kWindows);
-        for (int i = 0; i < kWindows; ++i) wr16(out + off_cnt + c * kWindows * 2 + 2 * i, (uint16_t)cnt[i]);
+        // (a window has at most 1536 bits, so cnt fits 11 bits; gap < 24)
+        for (int i = 0; i < kWindows; ++i)
+            wr16(out + off_win + (c * kWindows + i) * 2, (uint16_t)(cnt[i] | (gap[i] << kWinGapShift)));
     });
 
     // 6. raw bytes

@@ -76,7 +76,7 @@ namespace {
 
 struct Layout {
     uint64_t n, n_chunks, total_bits;
-    uint64_t off_ci, off_gap, off_cnt, off_stream, stream_bytes, off_raw, raw_bytes, total;
+    uint64_t off_ci, off_win, off_stream, stream_bytes, off_raw, raw_bytes, total;
 };
 
 Layout layout_for(uint64_t n, uint64_t total_bits) {
@@ -85,9 +85,8 @@ Layout layout_for(uint64_t n, uint64_t total_bits) {
     L.n_chunks = (n + kChunk - 1) / kChunk;
     L.total_bits = total_bits;
     L.off_ci = kHeader;
-    L.off_gap = up256(L.off_ci + (L.n_chunks + 1) * 16);
-    L.off_cnt = up256(L.off_gap + L.n_chunks * kWindows);
-    L.off_stream = up256(L.off_cnt + L.n_chunks * kWindows * 2);
+    L.off_win = up256(L.off_ci + (L.n_chunks + 1) * 16);
+    L.off_stream = up256(L.off_win + L.n_chunks * kWindows * 2);
     L.stream_bytes = up16((total_bits + 7) / 8) + 16;
     L.off_raw = up256(L.off_stream + L.stream_bytes);
     L.raw_bytes = up16(n);
@@ -203,7 +202,7 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     const Layout &L = M.L;
     if (L.n_chunks > (1u << 24)) return fail(DF11_E_UNSUPPORTED, "%llu chunks", (unsigned long long)L.n_chunks);
     if (rd32(c + 100) != L.n_chunks) return fail(DF11_E_FORMAT, "n_chunks field");
-    if (rd64(c + 112) != L.off_ci || rd64(c + 120) != L.off_gap || rd64(c + 128) != L.off_cnt ||
+    if (rd64(c + 112) != L.off_ci || rd64(c + 120) != L.off_win || rd64(c + 128) != 0 ||
         rd64(c + 136) != L.off_stream || rd64(c + 144) != L.stream_bytes ||
         rd64(c + 152) != L.off_raw || rd64(c + 160) != L.raw_bytes || rd64(c + 168) != L.total)
         return fail(DF11_E_FORMAT, "section offsets or sizes do not match the layout");
@@ -251,12 +250,12 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
         const uint32_t nbits = (uint32_t)(b1 - sb);   // <= 24 * kChunk, checked above
         uint64_t sum = 0;
         for (int i = 0; i < kWindows; ++i) {
-            const unsigned gap = c[L.off_gap + ch * kWindows + i];
-            const unsigned cnt = rd16(c + L.off_cnt + ch * kWindows * 2 + 2 * i);
+            const unsigned ent = rd16(c + L.off_win + (ch * kWindows + i) * 2);
+            const unsigned cnt = ent & kWinCntMask, gap = ent >> kWinGapShift;
             sum += cnt;
             const uint64_t ws = sb + window_edge(nbits, i), we = sb + window_edge(nbits, i + 1);
             if (cnt == 0) {
-                if (gap != 0xFF) return fail(DF11_E_FORMAT, "chunk %llu window %d: gap without codes", (unsigned long long)ch, i);
+                if (gap != 0) return fail(DF11_E_FORMAT, "chunk %llu window %d: gap without codes", (unsigned long long)ch, i);
                 continue;
             }
             if (gap >= (unsigned)kMaxLen || ws >= b1 || ws + gap >= we || cnt > we - ws - gap)
@@ -287,8 +286,10 @@ void fill_info(const Meta &M, df11_tensor_info *info) {
     info->total_bits = L.total_bits;
     info->container_bytes = L.total;
     info->meta_bytes = L.off_stream;
+    // chunk index (the plan's records stand in for it), one 16-bit entry per
+    // window, the code bits and one raw byte per element
     info->bytes_read_per_decode =
-        (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kWindows * 3 + (L.total_bits + 7) / 8 + L.n;
+        (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kWindows * 2 + (L.total_bits + 7) / 8 + L.n;
     memcpy(info->code_len, M.code_len, 256);
 }
 
@@ -389,8 +390,7 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
             memset(&r, 0, sizeof r);
             r.stream_off = L.off_stream + s0;
             r.raw_off = L.off_raw + elem0;
-            r.gap_off = L.off_gap + ch * kWindows;
-            r.cnt_off = L.off_cnt + ch * kWindows * 2;
+            r.win_off = L.off_win + ch * kWindows * 2;
             r.rel0 = (uint32_t)(b0 - 8 * s0);
             r.nbits = (uint32_t)(b1 - b0);
             r.s_len = (uint32_t)std::min<uint64_t>(s_end - s0, kCodeCap) | (s_end <= s0 + kCodeCap ? kStagedBit : 0u);

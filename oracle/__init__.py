@@ -117,7 +117,7 @@ def canonical_codes(lengths) -> np.ndarray:
 
 
 def encode(words: np.ndarray, shape=None) -> np.ndarray:
-    """Encode a uint16 array (BF16 bit patterns) into a version-3 container."""
+    """Encode a uint16 array (BF16 bit patterns) into a version-4 container."""
     w = np.ascontiguousarray(words, dtype=np.uint16).reshape(-1)
     shape = tuple(words.shape) if shape is None else tuple(shape)
     dims = np.array(shape if shape else (0,), dtype=np.uint64)
@@ -171,7 +171,7 @@ def check(container: np.ndarray) -> int:
     return int(lib().oracle_check(_p(c, ctypes.c_uint8), c.size))
 
 
-# ---- header fields of a version-3 container (layout in df11_oracle.c) ----
+# ---- header fields of a version-4 container (layout in df11_oracle.c) ----
 
 def header(container: np.ndarray) -> dict:
     c = np.ascontiguousarray(container, dtype=np.uint8)
@@ -191,7 +191,7 @@ def header(container: np.ndarray) -> dict:
         "dims": [u64(32 + 8 * i) for i in range(ndim)],
         "chunk_elems": u32(28), "max_code_len": int(c[96]), "windows": u16(98),
         "n_chunks": u32(100), "total_bits": u64(104),
-        "off_chunk_index": u64(112), "off_win_gap": u64(120), "off_win_cnt": u64(128),
+        "off_chunk_index": u64(112), "off_windows": u64(120),
         "off_stream": u64(136), "stream_bytes": u64(144), "off_raw": u64(152),
         "raw_bytes": u64(160), "total_bytes": u64(168),
         "code_len": c[208:464].copy(),

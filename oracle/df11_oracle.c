@@ -31,22 +31,28 @@
  *  - chunks of 32768 elements (64 KiB of BF16 output), each with its start
  *    bit; the N bits of a chunk are cut into 512 windows as evenly as
  *    integers allow (window i starts floor(i * N / 512) bits after the
- *    chunk's first bit), with (gap, cnt) per window.
+ *    chunk's first bit), with one 16-bit entry per window: the number of
+ *    codes that start in it (at most 1536, as a window has at most
+ *    ceil(32768 * 24 / 512) bits, so 11 bits) and the offset of the first of
+ *    them from the window's first bit (under 24, so 5 bits): a smaller block
+ *    index, in the spirit of the df11pack page's experimental 8-bit index
+ *    ("Beyond the official format").
  *
- * Container version 3 (all integers little-endian, sections 256-byte aligned):
+ * Container version 4 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
- *     0  char[8] magic "DF11HIPC"     8  u32 version (3)   12 u32 flags (0)
+ *     0  char[8] magic "DF11HIPC"     8  u32 version (4)   12 u32 flags (0)
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
  *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 reserved
  *    98  u16 windows                100  u32 n_chunks     104 u64 total_bits
- *   112  u64 off_chunk_index        120  u64 off_win_gap  128 u64 off_win_cnt
+ *   112  u64 off_chunk_index        120  u64 off_windows  128 u64 reserved
  *   136  u64 off_stream             144  u64 stream_bytes 152 u64 off_raw
  *   160  u64 raw_bytes              168  u64 total_bytes  176 reserved[32]
  *   208  u8 code_len[256]           464  reserved[48]
  *   chunk index: (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
  *                {total_bits, n_elems}
- *   window gap:  n_chunks x 512 x u8   (0xFF = window holds no code start)
- *   window cnt:  n_chunks x 512 x u16  (codes that start in the window)
+ *   windows:     n_chunks x 512 x u16: cnt | (gap << 11), cnt = codes that
+ *                start in the window, gap = offset of the first of them from
+ *                the window's first bit; 0 for a window with no code start
  *   stream:      ceil(total_bits/8) bytes rounded up to 16, plus 16 zero bytes
  *   raw:         n_elems bytes rounded up to 16
  *   Every byte not named above is zero.
@@ -59,7 +65,7 @@
 #define CAP 24
 #define CHUNK 32768u
 #define WINDOWS 512
-#define VERSION 3
+#define VERSION 4
 #define HDR 512u
 
 /* ------------------------------------------------------------------ */
@@ -193,7 +199,7 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code) {
 /* ------------------------------------------------------------------ */
 typedef struct {
     uint64_t n, n_chunks, total_bits;
-    uint64_t off_ci, off_gap, off_cnt, off_stream, stream_bytes, off_raw, raw_bytes, total;
+    uint64_t off_ci, off_win, off_stream, stream_bytes, off_raw, raw_bytes, total;
 } layout_t;
 
 static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
@@ -201,9 +207,8 @@ static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
     L->n_chunks = (n + CHUNK - 1) / CHUNK;
     L->total_bits = total_bits;
     L->off_ci = HDR;
-    L->off_gap = align256(L->off_ci + (L->n_chunks + 1) * 16);
-    L->off_cnt = align256(L->off_gap + L->n_chunks * WINDOWS);
-    L->off_stream = align256(L->off_cnt + L->n_chunks * WINDOWS * 2);
+    L->off_win = align256(L->off_ci + (L->n_chunks + 1) * 16);
+    L->off_stream = align256(L->off_win + L->n_chunks * WINDOWS * 2);
     L->stream_bytes = round16((total_bits + 7) / 8) + 16;
     L->off_raw = align256(L->off_stream + L->stream_bytes);
     L->raw_bytes = round16(n);
@@ -269,8 +274,7 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u32(out + 100, (uint32_t)L.n_chunks);
     put_u64(out + 104, total_bits);
     put_u64(out + 112, L.off_ci);
-    put_u64(out + 120, L.off_gap);
-    put_u64(out + 128, L.off_cnt);
+    put_u64(out + 120, L.off_win);
     put_u64(out + 136, L.off_stream);
     put_u64(out + 144, L.stream_bytes);
     put_u64(out + 152, L.off_raw);
@@ -294,27 +298,26 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     put_u64(out + L.off_ci + L.n_chunks * 16 + 8, n);
 
     /* 5. window index: the chunk's bits cut into 512 windows (window_edge);
-     *    per window the offset of its first code start from the window's
-     *    first bit and the number of code starts */
+     *    per window the number of code starts and the offset of the first
+     *    of them from the window's first bit */
     for (uint64_t c = 0; c < L.n_chunks; c++) {
         uint64_t b0 = get_u64(out + L.off_ci + c * 16);
         uint64_t b1 = get_u64(out + L.off_ci + (c + 1) * 16);
-        uint8_t *gap = out + L.off_gap + c * WINDOWS;
-        uint8_t *cntp = out + L.off_cnt + c * WINDOWS * 2;
-        unsigned cnt[WINDOWS];
+        unsigned cnt[WINDOWS], gap[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
-        for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
+        memset(gap, 0, sizeof(gap));
         uint64_t p = b0;
         int win = 0;
         uint64_t j_end = (c + 1) * CHUNK < n ? (c + 1) * CHUNK : n;
         for (uint64_t j = c * CHUNK; j < j_end; j++) {
             /* the window holding bit p: the last one that starts at or before it */
             while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= p) win++;
-            if (cnt[win] == 0) gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)));
+            if (cnt[win] == 0) gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)));
             cnt[win]++;
             p += len[exponent_of(words[j])];
         }
-        for (int i = 0; i < WINDOWS; i++) put_u16(cntp + 2 * i, (uint16_t)cnt[i]);
+        for (int i = 0; i < WINDOWS; i++)
+            put_u16(out + L.off_win + (c * WINDOWS + i) * 2, (uint16_t)(cnt[i] | (gap[i] << 11)));
     }
 
     /* 6. raw bytes: sign and fraction, as is */
@@ -346,8 +349,8 @@ static int parse(const uint8_t *c, uint64_t bytes, parsed_t *P) {
     const layout_t *L = &P->L;
     if (get_u32(c + 28) != CHUNK || c[96] != CAP || get_u16(c + 98) != WINDOWS) return ORACLE_E_FORMAT;
     if (get_u32(c + 100) != L->n_chunks) return ORACLE_E_FORMAT;
-    if (get_u64(c + 112) != L->off_ci || get_u64(c + 120) != L->off_gap ||
-        get_u64(c + 128) != L->off_cnt || get_u64(c + 136) != L->off_stream ||
+    if (get_u64(c + 112) != L->off_ci || get_u64(c + 120) != L->off_win ||
+        get_u64(c + 128) != 0 || get_u64(c + 136) != L->off_stream ||
         get_u64(c + 144) != L->stream_bytes || get_u64(c + 152) != L->off_raw ||
         get_u64(c + 160) != L->raw_bytes || get_u64(c + 168) != L->total)
         return ORACLE_E_FORMAT;
@@ -428,14 +431,15 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
     uint64_t b0 = get_u64(c + P.L.off_ci + chunk * 16);
     uint64_t b1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16);
     uint64_t ws = b0 + window_edge(b1 - b0, (uint64_t)win);
-    unsigned gap = c[P.L.off_gap + chunk * WINDOWS + win];
-    unsigned cnt = get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * win);
+    const uint8_t *wins = c + P.L.off_win + chunk * WINDOWS * 2;
+    unsigned ent = get_u16(wins + 2 * win);
+    unsigned cnt = ent & 0x7FFu, gap = ent >> 11;
     /* output position of this window's first code: codes of earlier windows */
     uint64_t before = 0;
-    for (int i = 0; i < win; i++) before += get_u16(c + P.L.off_cnt + chunk * WINDOWS * 2 + 2 * i);
+    for (int i = 0; i < win; i++) before += get_u16(wins + 2 * i) & 0x7FFu;
     uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8) + before;
     *n_out = cnt;
-    if (cnt == 0) { *end_bit = ws; return gap == 0xFF ? ORACLE_OK : ORACLE_E_FORMAT; }
+    if (cnt == 0) { *end_bit = ws; return gap == 0 ? ORACLE_OK : ORACLE_E_FORMAT; }
     uint64_t pos = ws + gap;
     for (unsigned k = 0; k < cnt; k++) {
         int e = read_code(&P, stream, &pos);
@@ -479,25 +483,23 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
         uint64_t b0 = pos;
         uint64_t b1 = get_u64(ent + 16);
         if (b1 < b0 || b1 > L->total_bits) return ORACLE_E_FORMAT;
-        unsigned cnt[WINDOWS];
-        int gap[WINDOWS];
+        unsigned cnt[WINDOWS], gap[WINDOWS];
         memset(cnt, 0, sizeof(cnt));
-        for (int i = 0; i < WINDOWS; i++) gap[i] = 0xFF;
+        memset(gap, 0, sizeof(gap));
         int win = 0;
         uint64_t j_end = (ch + 1) * CHUNK < L->n ? (ch + 1) * CHUNK : L->n;
         for (uint64_t j = ch * CHUNK; j < j_end; j++) {
             if (pos >= b1) return ORACLE_E_FORMAT;
             while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= pos) win++;
-            if (cnt[win] == 0) gap[win] = (int)(pos - (b0 + window_edge(b1 - b0, win)));
+            if (cnt[win] == 0) gap[win] = (unsigned)(pos - (b0 + window_edge(b1 - b0, win)));
             cnt[win]++;
             int e = read_code(&P, stream, &pos);
             if (e < 0) return -e;
         }
         if (pos != b1) return ORACLE_E_FORMAT;
-        for (int i = 0; i < WINDOWS; i++) {
-            if (c[L->off_gap + ch * WINDOWS + i] != gap[i]) return ORACLE_E_FORMAT;
-            if (get_u16(c + L->off_cnt + ch * WINDOWS * 2 + 2 * i) != cnt[i]) return ORACLE_E_FORMAT;
-        }
+        for (int i = 0; i < WINDOWS; i++)
+            if (get_u16(c + L->off_win + (ch * WINDOWS + i) * 2) != (cnt[i] | (gap[i] << 11)))
+                return ORACLE_E_FORMAT;
     }
     if (pos != L->total_bits) return ORACLE_E_FORMAT;
     const uint8_t *sent = c + L->off_ci + L->n_chunks * 16;

@@ -11,7 +11,7 @@
  * fraction, which is kept as one raw byte.  Decoding must give back every
  * word bit for bit (same page, introduction and "Status", milestone 1).
  *
- * The container layout written here is this project's own (version 3); its
+ * The container layout written here is this project's own (version 4); its
  * fields are documented next to the writer in df11_oracle.c.
  */
 #ifndef DF11_ORACLE_H
@@ -42,7 +42,7 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code);
 /* Upper bound on the container size for n words. */
 uint64_t oracle_container_bound(uint64_t n);
 
-/* Encode n BF16 words (as uint16) into a version-3 container.
+/* Encode n BF16 words (as uint16) into a version-4 container.
  * dims[ndim] is the tensor shape (ndim <= 8, product must equal n).
  * Returns ORACLE_OK and the container size in *out_bytes. */
 int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims,

@@ -11,7 +11,7 @@ routines that the tests hold the oracle against:
   lightest weights); its cost is the optimum without a length cap.
 * `canonical_code_strings`: canonical code values by the counting
   construction of RFC 1951 section 3.2.2 (bl_count / next_code), as strings.
-* `decode_with_strings`: decodes a version-3 container by matching code
+* `decode_with_strings`: decodes a version-4 container by matching code
   strings against the bit string of the stream, ignoring every index.
 * `nf12_encode_tiny`: an NF12 container built a second way (field values by
   slicing the 16-bit pattern as a string, each group as one 96-bit integer).
@@ -95,7 +95,7 @@ def _u64(b, o):
 
 
 def decode_with_strings(container: bytes):
-    """Decode a version-3 container through its code strings only."""
+    """Decode a version-4 container through its code strings only."""
     b = bytes(container)
     assert b[:8] == b"DF11HIPC"
     n = _u64(b, 16)

@@ -74,7 +74,7 @@ def test_validate_accepts_and_describes():
     assert info["container_bytes"] == c.size
     assert (info["code_len"] == h["code_len"]).all()
     n_ch = h["n_chunks"]
-    assert info["bytes_read_per_decode"] == (n_ch + 1) * 16 + n_ch * 512 * 3 + \
+    assert info["bytes_read_per_decode"] == (n_ch + 1) * 16 + n_ch * 512 * 2 + \
         (h["total_bits"] + 7) // 8 + w.size
     # the metadata prefix alone is enough
     assert df11.validate(c[:info["meta_bytes"]])["n_elems"] == w.size
@@ -100,8 +100,8 @@ def test_validate_rejects_broken_containers():
 
     assert _status(c) == 0
     assert bad(lambda x: x.__setitem__(0, ord("X"))) == E_FORMAT                  # magic
-    assert bad(lambda x: x.__setitem__(8, 4)) == E_UNSUPPORTED                   # version
-    assert bad(lambda x: x.__setitem__(8, 2)) == E_UNSUPPORTED                   # an older version
+    assert bad(lambda x: x.__setitem__(8, 5)) == E_UNSUPPORTED                   # version
+    assert bad(lambda x: x.__setitem__(8, 3)) == E_UNSUPPORTED                   # an older version
     assert bad(lambda x: x.__setitem__(99, 1)) == E_UNSUPPORTED                  # windows
     assert bad(lambda x: x.__setitem__(97, 1)) == E_FORMAT                       # reserved
     assert bad(lambda x: x.__setitem__(96, 25)) == E_UNSUPPORTED                 # max length
@@ -116,20 +116,24 @@ def test_validate_rejects_broken_containers():
     # alone cannot tell; the decoder's window-end check reports it)
     assert bad(lambda x: put64(x, ci + 16, 0)) == E_FORMAT                       # not monotone
     assert bad(lambda x: put64(x, ci + 24, 5)) == E_FORMAT                       # out_elem
-    cnt0 = h["off_win_cnt"]
-    assert bad(lambda x: x.__setitem__(cnt0, int(x[cnt0]) + 1)) == E_FORMAT      # counts sum
-    gap0 = h["off_win_gap"]
-    assert bad(lambda x: x.__setitem__(gap0 + 7, 30)) == E_FORMAT                # gap >= 24
+    win0 = h["off_windows"]   # entries cnt | (gap << 11)
+
+    def put16(x, off, v):
+        x[off:off + 2] = np.array([v], np.uint16).view(np.uint8)
+
+    def get16(x, off):
+        return int(x[off:off + 2].view(np.uint16)[0])
+
+    assert bad(lambda x: put16(x, win0, get16(x, win0) + 1)) == E_FORMAT         # counts sum
+    assert bad(lambda x: put16(x, win0 + 14, (get16(x, win0 + 14) & 0x7FF) | (30 << 11))) == E_FORMAT  # gap >= 24
 
     def empty_with_gap(x):
         # move window 5's codes to window 4 and give window 5 a gap
-        k = cnt0 + 2 * 5
-        c5 = int(x[k:k + 2].view(np.uint16)[0])
-        x[k:k + 2] = np.array([0], np.uint16).view(np.uint8)
-        k4 = cnt0 + 2 * 4
-        x[k4:k4 + 2] = (x[k4:k4 + 2].view(np.uint16) + c5).view(np.uint8)
+        c5 = get16(x, win0 + 10) & 0x7FF
+        put16(x, win0 + 10, 3 << 11)
+        put16(x, win0 + 8, get16(x, win0 + 8) + c5)
     assert bad(empty_with_gap) == E_FORMAT
-    assert _status(c[:h["off_win_cnt"] + 10]) == E_FORMAT                        # truncated
+    assert _status(c[:h["off_windows"] + 10]) == E_FORMAT                        # truncated
     assert _status(c[:100]) == E_FORMAT
     assert bad(lambda x: x.__setitem__(h["off_raw"] + w.size, 1)) == E_FORMAT    # raw padding
     assert bad(lambda x: x.__setitem__(200, 1)) == E_FORMAT                      # reserved

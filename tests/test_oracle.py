@@ -275,20 +275,21 @@ def test_chunk_and_window_index_reproduce_the_source(n):
                 assert end - edges[win + 1] < 24
         assert (np.concatenate(parts) == w[lo:hi]).all()
         assert ends[-1][1] == b1
-        gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
-        assert ((gap < 24) | (gap == 0xFF)).all()
+        ent = c[h["off_windows"] + 2 * NW * ch:h["off_windows"] + 2 * NW * (ch + 1)].view(np.uint16)
+        cnt, gap = ent & 0x7FF, ent >> 11
+        assert (gap < 24).all() and (gap[cnt == 0] == 0).all()
         # the index from first principles: every code's start bit from the
         # source's exponents and the header's code lengths; a window's cnt is
-        # the number of starts inside it, its gap the first one's offset
+        # the number of starts inside it (low 11 bits of its entry), its gap
+        # the first one's offset (top 5 bits), both 0 for an empty window
         ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
         starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
         edges = edges[:NW]
         before = np.searchsorted(starts, edges, side="left")
         want_cnt = np.diff(np.append(before, hi - lo))
-        cnt = c[h["off_win_cnt"] + 2 * NW * ch:h["off_win_cnt"] + 2 * NW * (ch + 1)].view(np.uint16)
         assert (cnt == want_cnt).all()
         idx = np.minimum(before, hi - lo - 1)
-        want_gap = np.where(want_cnt > 0, starts[idx] - edges, 0xFF)
+        want_gap = np.where(want_cnt > 0, starts[idx] - edges, 0)
         assert (gap == want_gap).all()
 
 
@@ -333,10 +334,10 @@ def test_corruption_is_detected():
     bad[0] ^= 1                                      # magic
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_win_gap"] + 5] ^= 1                   # a window gap
+    bad[h["off_windows"] + 2 * 5 + 1] ^= 0x08        # a window gap (bit 11 of the entry)
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_win_cnt"] + 10] ^= 1                  # a window count
+    bad[h["off_windows"] + 2 * 10] ^= 1              # a window count
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
     bad[208 + 121] += 1                              # a code length: Kraft breaks

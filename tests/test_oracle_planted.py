@@ -38,8 +38,10 @@ MUTATIONS = [
     ("both bit writer and reader least significant bit first",
      None, None, 0),
     ("window gap off by one",
-     "gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)));",
-     "gap[win] = (uint8_t)(p - (b0 + window_edge(b1 - b0, win)) + 1);", 0),
+     "gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)));",
+     "gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)) + 1);", 0),
+    ("window entry packs the gap one bit low",
+     "(uint16_t)(cnt[i] | (gap[i] << 11))", "(uint16_t)(cnt[i] | (gap[i] << 10))", 0),
     ("window count misses a code that starts on the window's first bit",
      "            cnt[win]++;",
      "            cnt[win] += (p != b0 + window_edge(b1 - b0, win));", 0),
@@ -119,9 +121,9 @@ def _pins_pass() -> bool:
             edges = b0 + (np.arange(NW) * (b1 - b0)) // NW
             before = np.searchsorted(starts, edges, side="left")
             want_cnt = np.diff(np.append(before, hi - lo))
-            cnt = c[h["off_win_cnt"] + 2 * NW * ch:h["off_win_cnt"] + 2 * NW * (ch + 1)].view(np.uint16)
-            gap = c[h["off_win_gap"] + NW * ch:h["off_win_gap"] + NW * (ch + 1)]
-            want_gap = np.where(want_cnt > 0, starts[np.minimum(before, hi - lo - 1)] - edges, 0xFF)
+            ent = c[h["off_windows"] + 2 * NW * ch:h["off_windows"] + 2 * NW * (ch + 1)].view(np.uint16)
+            cnt, gap = ent & 0x7FF, ent >> 11
+            want_gap = np.where(want_cnt > 0, starts[np.minimum(before, hi - lo - 1)] - edges, 0)
             if not ((cnt == want_cnt).all() and (gap == want_gap).all()):
                 return False
         return True
