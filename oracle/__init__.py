@@ -29,6 +29,7 @@ _SRC = os.path.join(_HERE, "df11_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 OK, E_ARG, E_FORMAT, E_CORRUPT, E_TRUNCATED = 0, 1, 2, 3, 4
+FLAG_SHA256 = 1
 CHUNK = 32768
 WINDOWS = 512
 CAP = 24
@@ -59,6 +60,9 @@ def _configure(L):
     L.oracle_container_bound.restype = ctypes.c_uint64
     L.oracle_encode.argtypes = [u16p, ctypes.c_uint64, ctypes.c_int, u64p, u8p,
                                 ctypes.c_uint64, u64p]
+    L.oracle_encode_flags.argtypes = [u16p, ctypes.c_uint64, ctypes.c_int, u64p, ctypes.c_uint32, u8p,
+                                      ctypes.c_uint64, u64p]
+    L.oracle_sha256.argtypes = [u8p, ctypes.c_uint64, u8p]
     L.oracle_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64]
     L.oracle_decode_chunk.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64, u16p]
     L.oracle_decode_window.argtypes = [u8p, ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int,
@@ -116,8 +120,19 @@ def canonical_codes(lengths) -> np.ndarray:
     return out
 
 
-def encode(words: np.ndarray, shape=None) -> np.ndarray:
-    """Encode a uint16 array (BF16 bit patterns) into a version-4 container."""
+def sha256(data) -> bytes:
+    """SHA-256 digest of a bytes-like object (FIPS 180-4, the oracle's C)."""
+    b = np.frombuffer(bytes(data), dtype=np.uint8) if not isinstance(data, np.ndarray) else \
+        np.ascontiguousarray(data).view(np.uint8).reshape(-1)
+    out = np.zeros(32, np.uint8)
+    src = b if b.size else np.zeros(1, np.uint8)
+    lib().oracle_sha256(_p(src, ctypes.c_uint8), b.size, _p(out, ctypes.c_uint8))
+    return out.tobytes()
+
+
+def encode(words: np.ndarray, shape=None, sha256: bool = False) -> np.ndarray:
+    """Encode a uint16 array (BF16 bit patterns) into a version-4 container;
+    with sha256, the header holds the SHA-256 of the source words."""
     w = np.ascontiguousarray(words, dtype=np.uint16).reshape(-1)
     shape = tuple(words.shape) if shape is None else tuple(shape)
     dims = np.array(shape if shape else (0,), dtype=np.uint64)
@@ -125,8 +140,9 @@ def encode(words: np.ndarray, shape=None) -> np.ndarray:
     cap = int(lib().oracle_container_bound(w.size))
     out = np.zeros(cap, np.uint8)
     nbytes = np.zeros(1, np.uint64)
-    st = lib().oracle_encode(_p(w, ctypes.c_uint16), w.size, ndim, _p(dims, ctypes.c_uint64),
-                             _p(out, ctypes.c_uint8), cap, _p(nbytes, ctypes.c_uint64))
+    st = lib().oracle_encode_flags(_p(w, ctypes.c_uint16), w.size, ndim, _p(dims, ctypes.c_uint64),
+                                   FLAG_SHA256 if sha256 else 0,
+                                   _p(out, ctypes.c_uint8), cap, _p(nbytes, ctypes.c_uint64))
     if st:
         raise OracleError(st, "encode")
     return out[: int(nbytes[0])].copy()
@@ -195,4 +211,5 @@ def header(container: np.ndarray) -> dict:
         "off_stream": u64(136), "stream_bytes": u64(144), "off_raw": u64(152),
         "raw_bytes": u64(160), "total_bytes": u64(168),
         "code_len": c[208:464].copy(),
+        "flags": u32(12), "sha256": c[176:208].tobytes(),
     }

@@ -40,13 +40,13 @@
  *
  * Container version 4 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
- *     0  char[8] magic "DF11HIPC"     8  u32 version (4)   12 u32 flags (0)
+ *     0  char[8] magic "DF11HIPC"     8  u32 version (4)   12 u32 flags
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
  *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 reserved
  *    98  u16 windows                100  u32 n_chunks     104 u64 total_bits
  *   112  u64 off_chunk_index        120  u64 off_windows  128 u64 reserved
  *   136  u64 off_stream             144  u64 stream_bytes 152 u64 off_raw
- *   160  u64 raw_bytes              168  u64 total_bytes  176 reserved[32]
+ *   160  u64 raw_bytes              168  u64 total_bytes  176 u8 sha256[32]
  *   208  u8 code_len[256]           464  reserved[48]
  *   chunk index: (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
  *                {total_bits, n_elems}
@@ -55,6 +55,11 @@
  *                the window's first bit; 0 for a window with no code start
  *   stream:      ceil(total_bits/8) bytes rounded up to 16, plus 16 zero bytes
  *   raw:         n_elems bytes rounded up to 16
+ *   flags: bit 0 set = sha256 holds the SHA-256 (FIPS 180-4) of the source
+ *   tensor's bytes, each word least significant byte first (the df11pack
+ *   page, "Beyond the official format": a per-tensor SHA-256 in the header
+ *   lets a verify find corruption without the source); clear = sha256 is
+ *   zero.  No other flag bit is defined.
  *   Every byte not named above is zero.
  */
 #include "df11_oracle.h"
@@ -195,6 +200,115 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code) {
 }
 
 /* ------------------------------------------------------------------ */
+/* SHA-256 (FIPS 180-4, sections 4.1.2, 4.2.2, 5.1.1, 5.3.3, 6.2),      */
+/* one byte at a time                                                  */
+/* ------------------------------------------------------------------ */
+/* floor(x^(1/k)), k = 2 or 3, of x < 2^105, by bisection */
+static uint64_t iroot(unsigned __int128 x, int k) {
+    uint64_t lo = 0, hi = (uint64_t)1 << 36;
+    while (lo < hi) {
+        uint64_t mid = lo + (hi - lo + 1) / 2;
+        unsigned __int128 p = (unsigned __int128)mid * mid;
+        if (k == 3) p *= mid;
+        if (p <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+/* The first n primes. */
+static void first_primes(int n, uint32_t *p) {
+    int found = 0;
+    for (uint32_t c = 2; found < n; c++) {
+        int prime = 1;
+        for (uint32_t d = 2; d * d <= c; d++) if (c % d == 0) { prime = 0; break; }
+        if (prime) p[found++] = c;
+    }
+}
+
+typedef struct {
+    uint32_t k[64];     /* first 32 fraction bits of the cube roots of the first 64 primes */
+    uint32_t h[8];      /* the hash value; starts at the first 32 fraction bits of the
+                           square roots of the first 8 primes */
+    uint8_t block[64];
+    unsigned fill;
+    uint64_t length;    /* message bytes so far */
+} sha256_t;
+
+static uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+
+static void sha256_init(sha256_t *S) {
+    uint32_t p[64];
+    first_primes(64, p);
+    /* floor(2^32 * r) mod 2^32 for r = p^(1/k): floor((p * 2^(32k))^(1/k)) */
+    for (int i = 0; i < 64; i++) S->k[i] = (uint32_t)iroot((unsigned __int128)p[i] << 96, 3);
+    for (int i = 0; i < 8; i++) S->h[i] = (uint32_t)iroot((unsigned __int128)p[i] << 64, 2);
+    S->fill = 0;
+    S->length = 0;
+}
+
+/* One 512-bit block into the hash value (the compression function). */
+static void sha256_block(sha256_t *S) {
+    uint32_t w[64];
+    for (int t = 0; t < 16; t++)
+        w[t] = ((uint32_t)S->block[4 * t] << 24) | ((uint32_t)S->block[4 * t + 1] << 16) |
+               ((uint32_t)S->block[4 * t + 2] << 8) | S->block[4 * t + 3];
+    for (int t = 16; t < 64; t++) {
+        uint32_t s0 = rotr(w[t - 15], 7) ^ rotr(w[t - 15], 18) ^ (w[t - 15] >> 3);
+        uint32_t s1 = rotr(w[t - 2], 17) ^ rotr(w[t - 2], 19) ^ (w[t - 2] >> 10);
+        w[t] = s1 + w[t - 7] + s0 + w[t - 16];
+    }
+    uint32_t a = S->h[0], b = S->h[1], c = S->h[2], d = S->h[3];
+    uint32_t e = S->h[4], f = S->h[5], g = S->h[6], h = S->h[7];
+    for (int t = 0; t < 64; t++) {
+        uint32_t big1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+        uint32_t ch = (e & f) ^ (~e & g);
+        uint32_t t1 = h + big1 + ch + S->k[t] + w[t];
+        uint32_t big0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+        uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
+        uint32_t t2 = big0 + maj;
+        h = g; g = f; f = e; e = d + t1;
+        d = c; c = b; b = a; a = t1 + t2;
+    }
+    S->h[0] += a; S->h[1] += b; S->h[2] += c; S->h[3] += d;
+    S->h[4] += e; S->h[5] += f; S->h[6] += g; S->h[7] += h;
+}
+
+static void sha256_byte(sha256_t *S, uint8_t x) {
+    S->block[S->fill++] = x;
+    S->length++;
+    if (S->fill == 64) { sha256_block(S); S->fill = 0; }
+}
+
+/* Padding: a 1 bit, zeros up to 448 bits mod 512, the bit length (64 bits,
+ * big-endian); then the hash value, big-endian. */
+static void sha256_final(sha256_t *S, uint8_t out[32]) {
+    uint64_t bits = S->length * 8;
+    sha256_byte(S, 0x80);
+    while (S->fill != 56) sha256_byte(S, 0);
+    for (int i = 7; i >= 0; i--) sha256_byte(S, (uint8_t)(bits >> (8 * i)));
+    for (int i = 0; i < 8; i++)
+        for (int j = 0; j < 4; j++) out[4 * i + j] = (uint8_t)(S->h[i] >> (24 - 8 * j));
+}
+
+void oracle_sha256(const uint8_t *msg, uint64_t len, uint8_t out[32]) {
+    sha256_t S;
+    sha256_init(&S);
+    for (uint64_t i = 0; i < len; i++) sha256_byte(&S, msg[i]);
+    sha256_final(&S, out);
+}
+
+/* SHA-256 of n words as bytes, each word's low byte first. */
+static void sha256_words(const uint16_t *w, uint64_t n, uint8_t out[32]) {
+    sha256_t S;
+    sha256_init(&S);
+    for (uint64_t j = 0; j < n; j++) {
+        sha256_byte(&S, (uint8_t)(w[j] & 0xFFu));
+        sha256_byte(&S, (uint8_t)(w[j] >> 8));
+    }
+    sha256_final(&S, out);
+}
+
+/* ------------------------------------------------------------------ */
 /* Encoder                                                             */
 /* ------------------------------------------------------------------ */
 typedef struct {
@@ -233,9 +347,10 @@ static unsigned get_bit(const uint8_t *stream, uint64_t pos) {
     return (stream[pos / 8] >> (7 - pos % 8)) & 1u;
 }
 
-int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims,
-                  uint8_t *out, uint64_t out_cap, uint64_t *out_bytes) {
-    if ((!words && n) || !out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims))
+int oracle_encode_flags(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims, uint32_t flags,
+                        uint8_t *out, uint64_t out_cap, uint64_t *out_bytes) {
+    if ((!words && n) || !out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims) ||
+        (flags & ~(uint32_t)ORACLE_FLAG_SHA256))
         return ORACLE_E_ARG;
     uint64_t prod = 1;
     for (int i = 0; i < ndim; i++) prod *= dims[i];
@@ -264,7 +379,8 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
     /* header */
     memcpy(out, "DF11HIPC", 8);
     put_u32(out + 8, VERSION);
-    put_u32(out + 12, 0);
+    put_u32(out + 12, flags);
+    if (flags & ORACLE_FLAG_SHA256) sha256_words(words, n, out + 176);
     put_u64(out + 16, n);
     put_u32(out + 24, (uint32_t)ndim);
     put_u32(out + 28, CHUNK);
@@ -325,6 +441,11 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
 
     *out_bytes = L.total;
     return ORACLE_OK;
+}
+
+int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims,
+                  uint8_t *out, uint64_t out_cap, uint64_t *out_bytes) {
+    return oracle_encode_flags(words, n, ndim, dims, 0, out, out_cap, out_bytes);
 }
 
 /* ------------------------------------------------------------------ */
@@ -461,7 +582,8 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
 
     /* shape */
     uint32_t ndim = get_u32(c + 24);
-    if (ndim > 8 || get_u32(c + 12) != 0) return ORACLE_E_FORMAT;
+    uint32_t flags = get_u32(c + 12);
+    if (ndim > 8 || (flags & ~(uint32_t)ORACLE_FLAG_SHA256)) return ORACLE_E_FORMAT;
     uint64_t prod = 1;
     for (uint32_t i = 0; i < ndim; i++) prod *= get_u64(c + 32 + 8 * i);
     if ((ndim > 0 && prod != L->n) || (ndim == 0 && L->n != 1)) return ORACLE_E_FORMAT;
@@ -506,12 +628,24 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
     if (get_u64(sent) != L->total_bits || get_u64(sent + 8) != L->n) return ORACLE_E_FORMAT;
 
     /* every byte the layout does not name is zero (a canonical container) */
-    for (uint64_t i = 176; i < 208; i++) if (c[i]) return ORACLE_E_FORMAT;
+    if (!(flags & ORACLE_FLAG_SHA256))
+        for (uint64_t i = 176; i < 208; i++) if (c[i]) return ORACLE_E_FORMAT;
     for (uint64_t i = 464; i < HDR; i++) if (c[i]) return ORACLE_E_FORMAT;
     if (c[97]) return ORACLE_E_FORMAT;
     for (uint32_t i = ndim; i < 8; i++) if (get_u64(c + 32 + 8 * i)) return ORACLE_E_FORMAT;
     for (uint64_t b = L->total_bits; b < L->stream_bytes * 8; b++)
         if (get_bit(stream, b)) return ORACLE_E_FORMAT;
     for (uint64_t i = L->n; i < L->raw_bytes; i++) if (c[L->off_raw + i]) return ORACLE_E_FORMAT;
+    /* the stored source hash against the hash of the decoded words */
+    if (flags & ORACLE_FLAG_SHA256) {
+        uint16_t *w = (uint16_t *)malloc((L->n ? L->n : 1) * sizeof(uint16_t));
+        if (!w) return ORACLE_E_ARG;
+        int st2 = oracle_decode(c, bytes, w, L->n);
+        uint8_t h[32];
+        if (!st2) sha256_words(w, L->n, h);
+        free(w);
+        if (st2) return st2;
+        if (memcmp(h, c + 176, 32) != 0) return ORACLE_E_CORRUPT;
+    }
     return ORACLE_OK;
 }

@@ -42,11 +42,21 @@ int oracle_canonical_codes(const uint8_t *len, uint32_t *code);
 /* Upper bound on the container size for n words. */
 uint64_t oracle_container_bound(uint64_t n);
 
+/* Header flag: the header holds the SHA-256 of the source words. */
+#define ORACLE_FLAG_SHA256 1u
+
 /* Encode n BF16 words (as uint16) into a version-4 container.
  * dims[ndim] is the tensor shape (ndim <= 8, product must equal n).
  * Returns ORACLE_OK and the container size in *out_bytes. */
 int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims,
                   uint8_t *out, uint64_t out_cap, uint64_t *out_bytes);
+
+/* The same with header flags (0 or ORACLE_FLAG_SHA256). */
+int oracle_encode_flags(const uint16_t *words, uint64_t n, int ndim, const uint64_t *dims, uint32_t flags,
+                        uint8_t *out, uint64_t out_cap, uint64_t *out_bytes);
+
+/* SHA-256 (FIPS 180-4) of len bytes; the 32-byte digest to out. */
+void oracle_sha256(const uint8_t *msg, uint64_t len, uint8_t out[32]);
 
 /* Bit-serial decode of a whole container: reads one bit at a time through
  * the canonical table, ignores the chunk and window index.  out[n]. */
@@ -62,7 +72,9 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
                        uint16_t *out, uint64_t *n_out, uint64_t *end_bit);
 
 /* Structural check of a container (header fields, Kraft sum, chunk index
- * against a re-walk of the stream, window index against the code starts). */
+ * against a re-walk of the stream, window index against the code starts);
+ * with the SHA-256 flag, also the stored hash against the hash of the
+ * decoded words (ORACLE_E_CORRUPT when they differ). */
 int oracle_check(const uint8_t *c, uint64_t bytes);
 
 #ifdef __cplusplus

@@ -4,6 +4,7 @@ flipped bit order, a wrong comparison) makes at least one pin fail.
 
 Mistakes are planted on the CPU only, in a temporary copy; the oracle under
 `oracle/` is never modified."""
+import hashlib
 import os
 import shutil
 import subprocess
@@ -60,12 +61,36 @@ MUTATIONS = [
     ("leaves sorted by symbol only",
      "(freq[sym[j]] > freq[s] || (freq[sym[j]] == freq[s] && sym[j] > s))",
      "(sym[j] > s)", 0),
+    ("SHA-256 schedule rotates by 8 instead of 7",
+     "rotr(w[t - 15], 7)", "rotr(w[t - 15], 8)", 0),
+    ("SHA-256 round constants from square roots",
+     "S->k[i] = (uint32_t)iroot((unsigned __int128)p[i] << 96, 3);",
+     "S->k[i] = (uint32_t)iroot((unsigned __int128)p[i] << 64, 2);", 0),
+    ("SHA-256 length field in bytes",
+     "uint64_t bits = S->length * 8;", "uint64_t bits = S->length;", 0),
+    ("SHA-256 majority replaced by choice",
+     "uint32_t maj = (a & b) ^ (a & c) ^ (b & c);", "uint32_t maj = (a & b) ^ (~a & c);", 0),
+    ("source words hashed high byte first",
+     "sha256_byte(&S, (uint8_t)(w[j] & 0xFFu));\n        sha256_byte(&S, (uint8_t)(w[j] >> 8));",
+     "sha256_byte(&S, (uint8_t)(w[j] >> 8));\n        sha256_byte(&S, (uint8_t)(w[j] & 0xFFu));", 0),
 ]
 
 
 def _pins_pass() -> bool:
     """A compact battery of the pins; False as soon as one fails."""
     try:
+        # SHA-256 against hashlib around the padding boundaries, and the
+        # source hash of a container against hashlib of the words' bytes
+        for n in (0, 3, 55, 56, 64, 119, 1000):
+            b = bytes(range(256)) * 4
+            if oracle.sha256(b[:n]) != hashlib.sha256(b[:n]).digest():
+                return False
+        w = W.normal_bf16((5000,), seed=2)
+        c = oracle.encode(w, sha256=True)
+        if oracle.header(c)["sha256"] != hashlib.sha256(w.astype("<u2").tobytes()).digest():
+            return False
+        if oracle.check(c) != 0:
+            return False
         # golden BF16 fields and the exhaustive tensor
         w = W.exhaustive_words()
         c = oracle.encode(w)
