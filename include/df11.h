@@ -15,13 +15,13 @@
  * integers little-endian; every section starts on a 256-byte boundary):
  *
  *   header (512 bytes)
- *      0 char[8] magic "DF11HIPC"    8 u32 version = 4      12 u32 flags = 0
+ *      0 char[8] magic "DF11HIPC"    8 u32 version = 4      12 u32 flags
  *     16 u64 n_elems                24 u32 ndim            28 u32 chunk_elems = 32768
  *     32 u64 dims[8]                96 u8 max_code_len = 24 97 u8 0
  *     98 u16 windows = 512         100 u32 n_chunks       104 u64 total_bits
  *    112 u64 off_chunk_index       120 u64 off_windows    128 u64 0
  *    136 u64 off_stream            144 u64 stream_bytes   152 u64 off_raw
- *    160 u64 raw_bytes             168 u64 total_bytes    176 u8[32] 0
+ *    160 u64 raw_bytes             168 u64 total_bytes    176 u8 sha256[32]
  *    208 u8 code_len[256]          464 u8[48] 0
  *   chunk index  (n_chunks + 1) x { u64 start_bit, u64 out_elem }; the last
  *                entry is { total_bits, n_elems }
@@ -31,6 +31,11 @@
  *                rounded up to 16, plus 16 zero bytes
  *   raw          one byte per element: (sign << 7) | fraction; n_elems bytes
  *                rounded up to 16
+ *   flags: bit 0 (DF11_FLAG_SHA256) set = sha256 is the SHA-256 (FIPS 180-4)
+ *   of the source tensor's bytes, each word least significant byte first
+ *   (df11pack page, "Beyond the official format": a per-tensor SHA-256 in the
+ *   header lets a verify find corruption without the source; the other
+ *   sections are the same with or without it); clear = sha256 is zero.
  *   Bytes not named above are zero.
  *
  * Code: code_len[e] is the length of the code of exponent byte e (0 = absent),
@@ -63,11 +68,14 @@
 extern "C" {
 #endif
 
-#define DF11_ABI_VERSION 1
+#define DF11_ABI_VERSION 2
 #define DF11_HEADER_BYTES 512
 #define DF11_CHUNK_ELEMS 32768
 #define DF11_WINDOWS 512
 #define DF11_MAX_CODE_LEN 24
+/* Header flag and encode option: the header holds the SHA-256 of the
+ * source words. */
+#define DF11_FLAG_SHA256 1u
 /* Tensors decoded by one kernel launch; larger batches are split. */
 #define DF11_MAX_BATCH 64
 
@@ -93,6 +101,8 @@ typedef struct {
     uint64_t meta_bytes;          /* header + chunk index + window index (what df11_plan needs) */
     uint64_t bytes_read_per_decode;  /* index + stream + raw bytes a decode reads */
     uint8_t code_len[256];
+    uint32_t flags;               /* header flags (DF11_FLAG_SHA256) */
+    uint8_t sha256[32];           /* the source hash when flags has DF11_FLAG_SHA256, else zero */
 } df11_tensor_info;
 
 /* ---------------------------------------------------------------- host-only */
@@ -121,6 +131,27 @@ uint64_t df11_container_bound(uint64_t n_elems);
 df11_status df11_encode(const uint16_t *host_words, uint64_t n_elems, int ndim,
                         const uint64_t *dims, void *out, uint64_t out_cap,
                         uint64_t *out_bytes, int threads);
+
+/* df11_encode with options: flags = 0 or DF11_FLAG_SHA256 (the header then
+ * holds the SHA-256 of the source words, computed on one more thread while
+ * the others encode; the other bytes are those df11_encode writes).  Any
+ * other flag bit: DF11_E_ARG. */
+df11_status df11_encode_ex(const uint16_t *host_words, uint64_t n_elems, int ndim,
+                           const uint64_t *dims, uint32_t flags, void *out, uint64_t out_cap,
+                           uint64_t *out_bytes, int threads);
+
+/* SHA-256 (FIPS 180-4) of `bytes` bytes of HOST memory into digest[32]. */
+void df11_sha256(const void *host_data, uint64_t bytes, uint8_t *digest);
+
+/* Verify decoded words against the source hash in a container's header:
+ * host_meta holds at least the container's metadata prefix (HOST memory),
+ * host_words the n decoded words (HOST memory).  Returns DF11_OK when the
+ * SHA-256 of the words equals the header's, DF11_E_CORRUPT when it differs,
+ * DF11_E_UNSUPPORTED when the header holds no hash, DF11_E_ARG when n is not
+ * the container's element count, DF11_E_FORMAT for an invalid container (the
+ * df11pack page's verify exit codes: pass, a check failed, could not check). */
+df11_status df11_verify_words(const void *host_meta, size_t bytes, const uint16_t *host_words,
+                              uint64_t n_elems);
 
 /* -------------------------------------------------------------------- plan */
 

@@ -19,6 +19,7 @@ DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-pa
 SOURCES = [
     ("host.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("encode.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
+    ("sha256.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("decode.hip", DEVICE),
     ("control.hip", DEVICE),
     ("nf12.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),

@@ -16,6 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdf11.so")
 
 OK, E_ARG, E_FORMAT, E_UNSUPPORTED, E_HIP, E_CORRUPT, E_NOMEM = range(7)
+FLAG_SHA256 = 1
 MAX_BATCH = 64
 
 
@@ -36,6 +37,8 @@ class TensorInfo(ctypes.Structure):
         ("meta_bytes", ctypes.c_uint64),
         ("bytes_read_per_decode", ctypes.c_uint64),
         ("code_len", ctypes.c_uint8 * 256),
+        ("flags", ctypes.c_uint32),
+        ("sha256", ctypes.c_uint8 * 32),
     ]
 
     def as_dict(self) -> dict:
@@ -45,13 +48,15 @@ class TensorInfo(ctypes.Structure):
             "container_bytes": self.container_bytes, "meta_bytes": self.meta_bytes,
             "bytes_read_per_decode": self.bytes_read_per_decode,
             "code_len": np.array(self.code_len[:], np.uint8),
+            "flags": self.flags, "sha256": bytes(self.sha256),
         }
 
 
 _lib = None
 
 EXPORTS = [
-    "df11_validate", "df11_container_bound", "df11_encode", "df11_plan", "df11_plan_destroy",
+    "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_sha256",
+    "df11_verify_words", "df11_plan", "df11_plan_destroy",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
     "df11_nf12_bound", "df11_nf12_encode", "df11_nf12_validate", "df11_nf12_decode",
@@ -76,6 +81,13 @@ def lib():
     L.df11_encode.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), vp, u64,
                               ctypes.POINTER(u64), ctypes.c_int]
     L.df11_encode.restype = ctypes.c_int
+    L.df11_encode_ex.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), ctypes.c_uint32, vp, u64,
+                                 ctypes.POINTER(u64), ctypes.c_int]
+    L.df11_encode_ex.restype = ctypes.c_int
+    L.df11_sha256.argtypes = [vp, u64, vp]
+    L.df11_sha256.restype = None
+    L.df11_verify_words.argtypes = [vp, sz, vp, u64]
+    L.df11_verify_words.restype = ctypes.c_int
     L.df11_plan.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(sz), ctypes.c_int, ctypes.c_int,
                             ctypes.c_uint32, ctypes.POINTER(vp)]
     L.df11_plan.restype = ctypes.c_int
@@ -130,20 +142,57 @@ def container_bound(n: int) -> int:
     return int(lib().df11_container_bound(n))
 
 
-def encode(words, shape=None, threads: int = 0) -> np.ndarray:
+def encode(words, shape=None, threads: int = 0, sha256: bool = False) -> np.ndarray:
     """Encode BF16 bit patterns (uint16/int16 numpy array, host) into a
-    version-4 container (uint8 numpy array)."""
+    version-4 container (uint8 numpy array); with sha256, the header holds
+    the SHA-256 of the source words."""
     w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
     shape = tuple(np.asarray(words).shape) if shape is None else tuple(shape)
     dims = (ctypes.c_uint64 * max(1, len(shape)))(*shape)
     cap = container_bound(w.size)
     out = np.empty(cap, np.uint8)
     nbytes = ctypes.c_uint64(0)
-    st = lib().df11_encode(w.ctypes.data, w.size, len(shape), dims, out.ctypes.data, cap,
-                           ctypes.byref(nbytes), threads)
+    st = lib().df11_encode_ex(w.ctypes.data, w.size, len(shape), dims, FLAG_SHA256 if sha256 else 0,
+                              out.ctypes.data, cap, ctypes.byref(nbytes), threads)
     if st != OK:
-        raise DF11Error(st, f"df11_encode: status {st}")
+        raise DF11Error(st, f"df11_encode_ex: status {st}")
     return out[: nbytes.value]
+
+
+def sha256(data) -> bytes:
+    """SHA-256 digest of a host buffer (bytes or a numpy array's bytes)."""
+    a = np.ascontiguousarray(np.frombuffer(data, np.uint8) if isinstance(data, (bytes, bytearray))
+                             else np.asarray(data)).view(np.uint8).reshape(-1)
+    out = np.zeros(32, np.uint8)
+    lib().df11_sha256(a.ctypes.data if a.size else None, a.size, out.ctypes.data)
+    return out.tobytes()
+
+
+def verify_status(container, words) -> int:
+    """df11_verify_words status: OK when the SHA-256 of `words` (host,
+    16-bit) equals the one in the container's header, E_CORRUPT when it
+    differs, E_UNSUPPORTED when the header holds none."""
+    c = _host_u8(container)
+    w = np.ascontiguousarray(np.asarray(words).view(np.uint16).reshape(-1))
+    return int(lib().df11_verify_words(c.ctypes.data, c.size, w.ctypes.data if w.size else None, w.size))
+
+
+def verify(container, words) -> bool:
+    """True when the words' SHA-256 equals the header's, False when it
+    differs; raises DF11Error when the container cannot be checked."""
+    st = verify_status(container, words)
+    if st == E_CORRUPT:
+        return False
+    _raise(st)
+    return True
+
+
+def verify_decoded(container, out, stream=None) -> bool:
+    """verify() of a decoded device tensor: waits for `stream`, copies the
+    words to host memory and checks their hash against the header's."""
+    import torch
+    (stream or torch.cuda.current_stream()).synchronize()
+    return verify(container, out.view(torch.int16).cpu().numpy())
 
 
 def validate(container) -> dict:

@@ -124,6 +124,9 @@ struct DecodeArgs {
     uint16_t *outs[DF11_MAX_BATCH];
 };
 
+// SHA-256 (FIPS 180-4) of `bytes` bytes (sha256.cpp).
+void sha256(const void *data, uint64_t bytes, uint8_t out[32]);
+
 // Records the error text that df11_last_error returns and gives back st
 // (host.cpp; printf-style message).
 df11_status report_error(df11_status st, const char *fmt, ...);

@@ -119,15 +119,24 @@ void canonical_codes(const uint8_t *len, uint32_t *code) {
 
 }  // namespace
 
-extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, const uint64_t *dims,
-                                   void *out_v, uint64_t out_cap, uint64_t *out_bytes, int threads) {
+extern "C" df11_status df11_encode_ex(const uint16_t *w, uint64_t n, int ndim, const uint64_t *dims, uint32_t flags,
+                                      void *out_v, uint64_t out_cap, uint64_t *out_bytes, int threads) {
     uint8_t *out = (uint8_t *)out_v;
-    if ((!w && n) || !out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims)) return DF11_E_ARG;
+    if ((!w && n) || !out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims) || (flags & ~DF11_FLAG_SHA256))
+        return DF11_E_ARG;
     uint64_t prod = 1;
     for (int i = 0; i < ndim; ++i) prod *= dims[i];
     if ((ndim && prod != n) || (!ndim && n != 1)) return DF11_E_ARG;
     if (n > (uint64_t(1) << 46)) return DF11_E_UNSUPPORTED;
     if (threads <= 0) threads = (int)std::max(1u, std::thread::hardware_concurrency());
+    // the source hash, on a thread of its own while the rest is encoded
+    uint8_t digest[32] = {};
+    std::thread hasher;
+    if (flags & DF11_FLAG_SHA256) hasher = std::thread([&] { sha256(w, 2 * n, digest); });
+    struct Join {
+        std::thread &t;
+        ~Join() { if (t.joinable()) t.join(); }
+    } join{hasher};
 
     // 1. exponent histogram
     const uint64_t n_slices = std::max<uint64_t>(1, std::min<uint64_t>((n + (1 << 20) - 1) >> 20, 4096));
@@ -247,6 +256,16 @@ extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, cons
         for (uint64_t j = lo; j < hi; ++j) r[j] = (uint8_t)(((w[j] >> 8) & 0x80) | (w[j] & 0x7F));
     });
 
+    if (hasher.joinable()) hasher.join();
+    if (flags & DF11_FLAG_SHA256) {
+        wr32(out + 12, flags);
+        memcpy(out + 176, digest, 32);
+    }
     *out_bytes = total;
     return DF11_OK;
+}
+
+extern "C" df11_status df11_encode(const uint16_t *w, uint64_t n, int ndim, const uint64_t *dims,
+                                   void *out_v, uint64_t out_cap, uint64_t *out_bytes, int threads) {
+    return df11_encode_ex(w, n, ndim, dims, 0, out_v, out_cap, out_bytes, threads);
 }

@@ -99,6 +99,8 @@ struct Meta {
     uint32_t ndim;
     uint64_t dims[8];
     uint8_t code_len[256];
+    uint32_t flags;
+    uint8_t sha256[32];
 };
 
 // Canonical code tables from a length vector (deflate construction).
@@ -189,7 +191,8 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     if (bytes < kHeader) return fail(DF11_E_FORMAT, "%zu bytes is shorter than the header", bytes);
     if (memcmp(c, "DF11HIPC", 8) != 0) return fail(DF11_E_FORMAT, "bad magic");
     if (rd32(c + 8) != kVersion) return fail(DF11_E_UNSUPPORTED, "container version %u", rd32(c + 8));
-    if (rd32(c + 12) != 0) return fail(DF11_E_UNSUPPORTED, "flags %#x", rd32(c + 12));
+    M.flags = rd32(c + 12);
+    if (M.flags & ~DF11_FLAG_SHA256) return fail(DF11_E_UNSUPPORTED, "flags %#x", M.flags);
     if (rd32(c + 28) != kChunk) return fail(DF11_E_UNSUPPORTED, "chunk_elems %u", rd32(c + 28));
     if (c[96] != kMaxLen) return fail(DF11_E_UNSUPPORTED, "max_code_len %u", c[96]);
     if (rd16(c + 98) != kWindows) return fail(DF11_E_UNSUPPORTED, "windows %u", rd16(c + 98));
@@ -216,7 +219,9 @@ df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     }
     if ((M.ndim && prod != n) || (!M.ndim && n != 1)) return fail(DF11_E_FORMAT, "shape does not match n_elems");
     if (c[97]) return fail(DF11_E_FORMAT, "reserved header bytes");
-    for (int i = 176; i < 208; ++i) if (c[i]) return fail(DF11_E_FORMAT, "reserved header bytes");
+    memcpy(M.sha256, c + 176, 32);
+    if (!(M.flags & DF11_FLAG_SHA256))
+        for (int i = 176; i < 208; ++i) if (c[i]) return fail(DF11_E_FORMAT, "hash bytes without the hash flag");
     for (int i = 464; i < (int)kHeader; ++i) if (c[i]) return fail(DF11_E_FORMAT, "reserved header bytes");
 
     memcpy(M.code_len, c + 208, 256);
@@ -291,6 +296,8 @@ void fill_info(const Meta &M, df11_tensor_info *info) {
     info->bytes_read_per_decode =
         (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kWindows * 2 + (L.total_bits + 7) / 8 + L.n;
     memcpy(info->code_len, M.code_len, 256);
+    info->flags = M.flags;
+    memcpy(info->sha256, M.sha256, 32);
 }
 
 }  // namespace
@@ -300,6 +307,21 @@ extern "C" df11_status df11_validate(const void *host_meta, size_t bytes, df11_t
     df11_status st = parse_and_validate((const uint8_t *)host_meta, bytes, M);
     if (st) return st;
     if (info) fill_info(M, info);
+    return DF11_OK;
+}
+
+extern "C" df11_status df11_verify_words(const void *host_meta, size_t bytes, const uint16_t *host_words,
+                                         uint64_t n) {
+    Meta M;
+    df11_status st = parse_and_validate((const uint8_t *)host_meta, bytes, M);
+    if (st) return st;
+    if (!(M.flags & DF11_FLAG_SHA256)) return fail(DF11_E_UNSUPPORTED, "the container holds no source hash");
+    if (n != M.L.n || (!host_words && n))
+        return fail(DF11_E_ARG, "%llu words for a container of %llu", (unsigned long long)n,
+                    (unsigned long long)M.L.n);
+    uint8_t h[32];
+    sha256(host_words, 2 * n, h);   // the words' bytes, low byte first (little-endian host)
+    if (memcmp(h, M.sha256, 32) != 0) return fail(DF11_E_CORRUPT, "the words' SHA-256 differs from the header's");
     return DF11_OK;
 }
 

@@ -222,6 +222,29 @@ def test_corrupted_stream_sets_the_flag():
     assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
+def test_source_hash_verifies_decoded_output():
+    """Hashed containers (the oracle's, flag DF11_FLAG_SHA256) decode like
+    plain ones; the decoded device words verify against the header's hash
+    with no source at hand; a flipped fraction bit in the device copy, which
+    no structural check can see, fails the verify."""
+    torch = _torch()
+    log("source hash verify")
+    ws = [W.normal_bf16((65536 + 77,), seed=21), W.heavy_tail_bf16((40000,), seed=22)]
+    cs = [oracle.encode(w, sha256=True) for w in ws]
+    plan = df11.Plan(cs)
+    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in ws]
+    df11.decode_batch(plan, [to_device_u8(c) for c in cs], outs)
+    df11.check(plan)
+    for w, c, o in zip(ws, cs, outs):
+        assert (o.cpu().numpy().view(np.uint16) == w).all()
+        assert df11.verify_decoded(c, o)
+    bad = cs[0].copy()
+    bad[oracle.header(bad)["off_raw"] + 999] ^= 0x01
+    df11.decode(plan, 0, to_device_u8(bad), outs[0])
+    df11.check(plan)                       # the structure is intact
+    assert not df11.verify_decoded(cs[0], outs[0])
+
+
 def test_bad_arguments_are_rejected():
     torch = _torch()
     w = W.normal_bf16((1000,), seed=2)

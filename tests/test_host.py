@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     assert len(names) >= 12
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.df11_abi_version() == 1
+    assert lib.df11_abi_version() == 2
     assert lib.df11_status_str(2) == b"DF11_E_FORMAT"
 
 
