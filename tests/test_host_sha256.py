@@ -21,6 +21,24 @@ def test_sha256_matches_hashlib(n):
     assert df11.sha256(b) == hashlib.sha256(b.tobytes()).digest()
 
 
+def test_portable_sha256_matches_hashlib():
+    """The portable code path (the library picks the processor's SHA
+    extensions when it has them; the environment variable forces the
+    portable one), in a fresh process."""
+    import os
+    import subprocess
+    import sys
+    code = ("import hashlib, numpy as np, lossless_bf16_weight_amd as d\n"
+            "for n in (0, 1, 55, 56, 63, 64, 65, 119, 120, 128, 100003):\n"
+            "    b = np.random.default_rng(n).integers(0, 256, n).astype(np.uint8)\n"
+            "    assert d.sha256(b) == hashlib.sha256(b.tobytes()).digest(), n\n"
+            "print('ok')\n")
+    env = dict(os.environ, DF11_SHA256_PORTABLE="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=root, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr[-2000:]
+
+
 @pytest.mark.parametrize("n", [0, 1, 1000, 32768, 32769, 100003])
 def test_hashed_encode_matches_oracle_bytes(n):
     w = W.normal_bf16((n,), seed=n)
