@@ -140,6 +140,20 @@ df11_status df11_encode_ex(const uint16_t *host_words, uint64_t n_elems, int ndi
                            const uint64_t *dims, uint32_t flags, void *out, uint64_t out_cap,
                            uint64_t *out_bytes, int threads);
 
+/* Encode n BF16 words held in DEVICE memory (16-byte aligned) into a
+ * version-4 container in DEVICE memory `d_out` (16-byte aligned, capacity
+ * out_cap, at least df11_container_bound(n)), on `stream` of device
+ * `hip_device`: the bytes df11_encode writes for the same words and shape.
+ * The exponent histogram, the chunk bit counts, the chunk index, the packed
+ * code stream, the window index and the raw bytes are computed by kernels;
+ * the 256-symbol code and the header are built on the host between the
+ * histogram and the rest, so the call waits for the stream twice and returns
+ * when the container is complete.  Allocates 2 KiB of device memory on the
+ * stream for the histogram.  No source hash (df11_encode_ex adds it). */
+df11_status df11_encode_device(const void *d_words, uint64_t n_elems, int ndim, const uint64_t *dims,
+                               void *d_out, uint64_t out_cap, uint64_t *out_bytes, int hip_device,
+                               hipStream_t stream);
+
 /* SHA-256 (FIPS 180-4) of `bytes` bytes of HOST memory into digest[32]. */
 void df11_sha256(const void *host_data, uint64_t bytes, uint8_t *digest);
 

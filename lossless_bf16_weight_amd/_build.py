@@ -24,6 +24,7 @@ SOURCES = [
     ("control.hip", DEVICE),
     ("nf12.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"]),
     ("nf12.hip", DEVICE),
+    ("encode_gpu.hip", DEVICE),
 ]
 
 

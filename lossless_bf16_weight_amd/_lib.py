@@ -55,7 +55,7 @@ class TensorInfo(ctypes.Structure):
 _lib = None
 
 EXPORTS = [
-    "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_sha256",
+    "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_encode_device", "df11_sha256",
     "df11_verify_words", "df11_plan", "df11_plan_destroy",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
@@ -84,6 +84,9 @@ def lib():
     L.df11_encode_ex.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), ctypes.c_uint32, vp, u64,
                                  ctypes.POINTER(u64), ctypes.c_int]
     L.df11_encode_ex.restype = ctypes.c_int
+    L.df11_encode_device.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), vp, u64, ctypes.POINTER(u64),
+                                     ctypes.c_int, vp]
+    L.df11_encode_device.restype = ctypes.c_int
     L.df11_sha256.argtypes = [vp, u64, vp]
     L.df11_sha256.restype = None
     L.df11_verify_words.argtypes = [vp, sz, vp, u64]
@@ -156,6 +159,22 @@ def encode(words, shape=None, threads: int = 0, sha256: bool = False) -> np.ndar
                               out.ctypes.data, cap, ctypes.byref(nbytes), threads)
     if st != OK:
         raise DF11Error(st, f"df11_encode_ex: status {st}")
+    return out[: nbytes.value]
+
+
+def encode_device(words, shape=None, stream=None):
+    """Encode a 16-bit device tensor (BF16 bit patterns, on a GPU) into a
+    version-4 container on the same device (uint8 tensor): the bytes
+    encode() writes for the same words, computed by the GPU kernels."""
+    import torch
+    w = words.contiguous().view(torch.int16).reshape(-1)
+    shape = tuple(words.shape) if shape is None else tuple(shape)
+    dims = (ctypes.c_uint64 * max(1, len(shape)))(*shape)
+    out = torch.empty(container_bound(w.numel()), dtype=torch.uint8, device=w.device)
+    nbytes = ctypes.c_uint64(0)
+    _raise(lib().df11_encode_device(w.data_ptr() if w.numel() else None, w.numel(), len(shape), dims,
+                                    out.data_ptr(), out.numel(), ctypes.byref(nbytes), w.device.index or 0,
+                                    _stream_handle(stream)))
     return out[: nbytes.value]
 
 

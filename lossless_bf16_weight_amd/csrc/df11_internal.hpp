@@ -124,6 +124,18 @@ struct DecodeArgs {
     uint16_t *outs[DF11_MAX_BATCH];
 };
 
+// Encoder pieces shared by the host and the GPU encoders (encode.cpp): the
+// length-limited canonical code of a histogram, the container layout for a
+// total bit count, and the 512-byte header.
+struct EncodeLayout {
+    uint64_t n_chunks, total_bits;
+    uint64_t off_ci, off_win, off_stream, stream_bytes, off_raw, raw_bytes, total;
+};
+void build_code(const uint64_t *freq, uint8_t *len, uint32_t *code);
+EncodeLayout encode_layout(uint64_t n, uint64_t total_bits);
+void write_header(uint8_t *out, uint64_t n, int ndim, const uint64_t *dims, const EncodeLayout &L,
+                  const uint8_t *len);
+
 // SHA-256 (FIPS 180-4) of `bytes` bytes (sha256.cpp).
 void sha256(const void *data, uint64_t bytes, uint8_t out[32]);
 

@@ -119,6 +119,52 @@ void canonical_codes(const uint8_t *len, uint32_t *code) {
 
 }  // namespace
 
+namespace df11 {
+
+void build_code(const uint64_t *freq, uint8_t *len, uint32_t *code) {
+    package_merge(freq, kMaxLen, len);
+    canonical_codes(len, code);
+}
+
+EncodeLayout encode_layout(uint64_t n, uint64_t total_bits) {
+    EncodeLayout L;
+    L.n_chunks = (n + kChunk - 1) / kChunk;
+    L.total_bits = total_bits;
+    L.off_ci = kHeader;
+    L.off_win = up256(L.off_ci + (L.n_chunks + 1) * 16);
+    L.off_stream = up256(L.off_win + L.n_chunks * kWindows * 2);
+    L.stream_bytes = up16((total_bits + 7) / 8) + 16;
+    L.off_raw = up256(L.off_stream + L.stream_bytes);
+    L.raw_bytes = up16(n);
+    L.total = L.off_raw + L.raw_bytes;
+    return L;
+}
+
+void write_header(uint8_t *out, uint64_t n, int ndim, const uint64_t *dims, const EncodeLayout &L,
+                  const uint8_t *len) {
+    memset(out, 0, kHeader);
+    memcpy(out, "DF11HIPC", 8);
+    wr32(out + 8, kVersion);
+    wr64(out + 16, n);
+    wr32(out + 24, (uint32_t)ndim);
+    wr32(out + 28, kChunk);
+    for (int i = 0; i < ndim; ++i) wr64(out + 32 + 8 * i, dims[i]);
+    out[96] = kMaxLen;
+    wr16(out + 98, kWindows);
+    wr32(out + 100, (uint32_t)L.n_chunks);
+    wr64(out + 104, L.total_bits);
+    wr64(out + 112, L.off_ci);
+    wr64(out + 120, L.off_win);
+    wr64(out + 136, L.off_stream);
+    wr64(out + 144, L.stream_bytes);
+    wr64(out + 152, L.off_raw);
+    wr64(out + 160, L.raw_bytes);
+    wr64(out + 168, L.total);
+    memcpy(out + 208, len, 256);
+}
+
+}  // namespace df11
+
 extern "C" df11_status df11_encode_ex(const uint16_t *w, uint64_t n, int ndim, const uint64_t *dims, uint32_t flags,
                                       void *out_v, uint64_t out_cap, uint64_t *out_bytes, int threads) {
     uint8_t *out = (uint8_t *)out_v;
@@ -153,8 +199,7 @@ extern "C" df11_status df11_encode_ex(const uint16_t *w, uint64_t n, int ndim, c
     // 2. lengths, 3. canonical codes
     uint8_t len[256];
     uint32_t code[256];
-    package_merge(freq, kMaxLen, len);
-    canonical_codes(len, code);
+    build_code(freq, len, code);
 
     // 4. per-chunk bit counts and start bits
     const uint64_t n_chunks = (n + kChunk - 1) / kChunk;
@@ -169,13 +214,9 @@ extern "C" df11_status df11_encode_ex(const uint16_t *w, uint64_t n, int ndim, c
     const uint64_t total_bits = start[n_chunks];
 
     // layout
-    const uint64_t off_ci = kHeader;
-    const uint64_t off_win = up256(off_ci + (n_chunks + 1) * 16);
-    const uint64_t off_stream = up256(off_win + n_chunks * kWindows * 2);
-    const uint64_t stream_bytes = up16((total_bits + 7) / 8) + 16;
-    const uint64_t off_raw = up256(off_stream + stream_bytes);
-    const uint64_t raw_bytes = up16(n);
-    const uint64_t total = off_raw + raw_bytes;
+    const EncodeLayout EL = encode_layout(n, total_bits);
+    const uint64_t off_ci = EL.off_ci, off_win = EL.off_win, off_stream = EL.off_stream;
+    const uint64_t off_raw = EL.off_raw, total = EL.total;
     if (out_cap < total) return DF11_E_ARG;
 
     // zero everything (padding and reserved bytes stay zero)
@@ -185,24 +226,7 @@ extern "C" df11_status df11_encode_ex(const uint16_t *w, uint64_t n, int ndim, c
         memset(out + lo, 0, hi - lo);
     });
 
-    memcpy(out, "DF11HIPC", 8);
-    wr32(out + 8, kVersion);
-    wr64(out + 16, n);
-    wr32(out + 24, (uint32_t)ndim);
-    wr32(out + 28, kChunk);
-    for (int i = 0; i < ndim; ++i) wr64(out + 32 + 8 * i, dims[i]);
-    out[96] = kMaxLen;
-    wr16(out + 98, kWindows);
-    wr32(out + 100, (uint32_t)n_chunks);
-    wr64(out + 104, total_bits);
-    wr64(out + 112, off_ci);
-    wr64(out + 120, off_win);
-    wr64(out + 136, off_stream);
-    wr64(out + 144, stream_bytes);
-    wr64(out + 152, off_raw);
-    wr64(out + 160, raw_bytes);
-    wr64(out + 168, total);
-    memcpy(out + 208, len, 256);
+    write_header(out, n, ndim, dims, EL, len);
     for (uint64_t c = 0; c <= n_chunks; ++c) {
         wr64(out + off_ci + c * 16, start[c]);
         wr64(out + off_ci + c * 16 + 8, std::min<uint64_t>(c * kChunk, n));

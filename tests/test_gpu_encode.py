@@ -1,0 +1,75 @@
+"""GPU parity of the GPU encoder (df11_encode_device): its containers must be
+the oracle's byte for byte (the oracle encodes tensors up to a few hundred
+thousand words in seconds; larger tensors are compared with the host
+encoder, which the host tests pin to the oracle's bytes), and decode back to
+the source words on the GPU."""
+import numpy as np
+import pytest
+
+import oracle
+import lossless_bf16_weight_amd as df11
+from lossless_bf16_weight_amd import workloads as W
+
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_encode(w, shape=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to("cuda")
+    c = df11.encode_device(t.reshape(w.shape if shape is None else shape))
+    return c.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 9, 63, 64, 65, 127, 128, 129, 1000, 32767, 32768, 32769,
+                               65536 + 5, 250000])
+def test_edge_sizes_match_oracle_bytes(n):
+    log(f"gpu encode {n}")
+    w = W.normal_bf16((n,), seed=n)
+    want = oracle.encode(w)
+    got = _gpu_encode(w)
+    assert got.size == want.size and (got == want).all()
+
+
+def test_special_tensors_match_oracle_bytes():
+    log("gpu encode special")
+    rng = np.random.default_rng(5)
+    cases = [W.exhaustive_words(), rng.permutation(W.exhaustive_words()),
+             np.zeros(70000, np.uint16),                                      # one symbol: 1-bit codes
+             np.where(np.arange(50001) % 3 == 0, 0x3F80, 0x4000).astype(np.uint16),
+             W.heavy_tail_bf16((300001,), seed=2),                             # long codes up to the cap
+             np.full(1, 0x7F80, np.uint16)]
+    for w in cases:
+        want = oracle.encode(w)
+        got = _gpu_encode(w)
+        assert got.size == want.size and (got == want).all(), w.size
+
+
+def test_empty_tensor_and_shapes():
+    import torch
+    w = np.zeros(0, np.uint16)
+    assert (_gpu_encode(w) == oracle.encode(w)).all()
+    w = W.normal_bf16((300, 417), seed=9)
+    assert (_gpu_encode(w) == oracle.encode(w)).all()
+    with pytest.raises(df11.DF11Error):   # misaligned words
+        t = torch.zeros(1001, dtype=torch.int16, device="cuda")
+        df11.encode_device(t[1:])
+
+
+@pytest.mark.parametrize("name", ["llama8b_block", "flux_dit_block"])
+def test_workloads_match_host_encoder_and_round_trip(name):
+    import torch
+    log(f"gpu encode workload {name}")
+    for s in W.WORKLOADS[name]():
+        w = s.make(threads=16)
+        want = df11.encode(w.reshape(-1), shape=s.shape, threads=16)
+        t = torch.from_numpy(w.view(np.int16)).to("cuda")
+        c = df11.encode_device(t)
+        got = c.cpu().numpy()
+        assert got.size == want.size and (got == want).all(), s.name
+        plan = df11.Plan([got])
+        out = torch.empty(w.size, dtype=torch.int16, device="cuda")
+        df11.decode(plan, 0, c, out)
+        df11.check(plan)
+        assert torch.equal(out, t.reshape(-1)), s.name

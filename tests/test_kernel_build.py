@@ -40,7 +40,7 @@ def _remark(stderr, name):
     return [int(a or b) for a, b in m]
 
 
-@pytest.mark.parametrize("src", ["decode.hip", "nf12.hip", "control.hip"])
+@pytest.mark.parametrize("src", ["decode.hip", "nf12.hip", "control.hip", "encode_gpu.hip"])
 def test_no_scratch_and_no_flat_memory(src, tmp_path):
     asm, remarks = _compile(src, tmp_path)
     assert all(v == 0 for v in _remark(remarks, r"ScratchSize \[bytes/lane\]")), src
