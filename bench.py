@@ -116,10 +116,27 @@ def cpu_baseline(containers, infos, min_wall_s: float = 1.5, max_wall_s: float =
     dt = time.perf_counter() - t0
     what = (f"{passes} full pass(es) over all {len(jobs)} chunks" if chunks == passes * len(jobs)
             else f"{chunks} of {len(jobs)} chunks")
+    # one thread, over a prefix of the same (interleaved) chunk list
+    one = 0
+    t1 = time.perf_counter()
+    for j in jobs:
+        one += run(j)
+        if time.perf_counter() - t1 >= min_wall_s:
+            break
+    dt1 = time.perf_counter() - t1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(2.0 * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{what} of the {WORKLOAD} containers ({done} elements decoded), "
-                      f"bit-serial oracle decode on {threads} threads, {dt:.1f} s wall"}
+                      f"bit-serial oracle decode on {threads} threads, {dt:.1f} s wall",
+            "single_thread": {"value": round(2.0 * one / dt1 / 1e9, 4), "unit": "GB/s",
+                              "sample": f"{one} elements of the same chunk list, {dt1:.1f} s wall"},
+            "host_cpus": os.cpu_count(), "cpu_model": model}
 
 
 def jit_overlap(n_layers: int, token_counts, reps: int):
