@@ -146,13 +146,24 @@ df11_status df11_encode_ex(const uint16_t *host_words, uint64_t n_elems, int ndi
  * `hip_device`: the bytes df11_encode writes for the same words and shape.
  * The exponent histogram, the chunk bit counts, the chunk index, the packed
  * code stream, the window index and the raw bytes are computed by kernels;
- * the 256-symbol code and the header are built on the host between the
- * histogram and the rest, so the call waits for the stream twice and returns
- * when the container is complete.  Allocates 2 KiB of device memory on the
- * stream for the histogram.  No source hash (df11_encode_ex adds it). */
+ * the 256-symbol code and the layout are built on the host once the
+ * histogram is back, so the call waits for the stream once and returns with
+ * the rest enqueued on it (*out_bytes is the container size; the bytes are
+ * there once the stream reaches that point).  Allocates 2 KiB of device
+ * memory on the stream for the histogram.  No source hash (df11_encode_ex
+ * adds it on the host). */
 df11_status df11_encode_device(const void *d_words, uint64_t n_elems, int ndim, const uint64_t *dims,
                                void *d_out, uint64_t out_cap, uint64_t *out_bytes, int hip_device,
                                hipStream_t stream);
+
+/* df11_encode_device for n_tensors tensors at once, sharing the one wait:
+ * d_words[t], n_elems[t], ndims[t], dims[8 t .. 8 t + ndims[t]), d_outs[t],
+ * out_caps[t] and out_bytes[t] describe tensor t.  Allocates 2 KiB of device
+ * memory per tensor on the stream. */
+df11_status df11_encode_device_batch(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                                     const int *ndims, const uint64_t *dims, void *const *d_outs,
+                                     const uint64_t *out_caps, uint64_t *out_bytes, int hip_device,
+                                     hipStream_t stream);
 
 /* SHA-256 (FIPS 180-4) of `bytes` bytes of HOST memory into digest[32]. */
 void df11_sha256(const void *host_data, uint64_t bytes, uint8_t *digest);

@@ -55,7 +55,7 @@ class TensorInfo(ctypes.Structure):
 _lib = None
 
 EXPORTS = [
-    "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_encode_device", "df11_sha256",
+    "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_encode_device", "df11_encode_device_batch", "df11_sha256",
     "df11_verify_words", "df11_plan", "df11_plan_destroy",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
@@ -87,6 +87,10 @@ def lib():
     L.df11_encode_device.argtypes = [vp, u64, ctypes.c_int, ctypes.POINTER(u64), vp, u64, ctypes.POINTER(u64),
                                      ctypes.c_int, vp]
     L.df11_encode_device.restype = ctypes.c_int
+    L.df11_encode_device_batch.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(u64),
+                                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(u64), ctypes.POINTER(vp),
+                                           ctypes.POINTER(u64), ctypes.POINTER(u64), ctypes.c_int, vp]
+    L.df11_encode_device_batch.restype = ctypes.c_int
     L.df11_sha256.argtypes = [vp, u64, vp]
     L.df11_sha256.restype = None
     L.df11_verify_words.argtypes = [vp, sz, vp, u64]
@@ -176,6 +180,29 @@ def encode_device(words, shape=None, stream=None):
                                     out.data_ptr(), out.numel(), ctypes.byref(nbytes), w.device.index or 0,
                                     _stream_handle(stream)))
     return out[: nbytes.value]
+
+
+def encode_device_batch(tensors, stream=None):
+    """encode_device() for several device tensors (one device) sharing one
+    wait on the stream; returns their containers (uint8 device tensors)."""
+    import torch
+    ws = [t.contiguous().view(torch.int16) for t in tensors]
+    k = len(ws)
+    if k == 0:
+        return []
+    dev = ws[0].device
+    outs = [torch.empty(container_bound(w.numel()), dtype=torch.uint8, device=dev) for w in ws]
+    dims = (ctypes.c_uint64 * (8 * k))()
+    for t, w in enumerate(ws):
+        for i, d in enumerate(w.shape):
+            dims[8 * t + i] = d
+    nbytes = (ctypes.c_uint64 * k)()
+    _raise(lib().df11_encode_device_batch(
+        k, (ctypes.c_void_p * k)(*[w.data_ptr() if w.numel() else None for w in ws]),
+        (ctypes.c_uint64 * k)(*[w.numel() for w in ws]), (ctypes.c_int * k)(*[w.dim() for w in ws]), dims,
+        (ctypes.c_void_p * k)(*[o.data_ptr() for o in outs]), (ctypes.c_uint64 * k)(*[o.numel() for o in outs]),
+        nbytes, dev.index or 0, _stream_handle(stream)))
+    return [o[: nbytes[t]] for t, o in enumerate(outs)]
 
 
 def sha256(data) -> bytes:

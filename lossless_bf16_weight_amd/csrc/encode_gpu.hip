@@ -311,24 +311,44 @@ __global__ __launch_bounds__(kEncThreads) void enc_pack(PackArgs a, CodeTable T)
     a.win[c * (kWindows / 2) + tid] = e0 | (e1 << 16);
 }
 
+// The 512-byte header, from a kernel argument (so that no host buffer has to
+// outlive the call).
+struct Header {
+    uint32_t w[kHeader / 4];
+};
+__global__ __launch_bounds__(kHeader / 4) void enc_header(Header h, GLOBAL uint32_t *out) {
+    out[threadIdx.x] = h.w[threadIdx.x];
+}
+
 }  // namespace
 
 }  // namespace df11
 
 using namespace df11;
 
-extern "C" df11_status df11_encode_device(const void *d_words, uint64_t n, int ndim, const uint64_t *dims,
-                                          void *d_out, uint64_t out_cap, uint64_t *out_bytes, int hip_device,
-                                          hipStream_t stream) {
-    if ((!d_words && n) || !d_out || !out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims))
-        return report_error(DF11_E_ARG, "df11_encode_device: bad argument");
-    uint64_t prod = 1;
-    for (int i = 0; i < ndim; ++i) prod *= dims[i];
-    if ((ndim && prod != n) || (!ndim && n != 1))
-        return report_error(DF11_E_ARG, "df11_encode_device: shape does not match %llu elements", (unsigned long long)n);
-    if (n > (uint64_t(1) << 46)) return report_error(DF11_E_UNSUPPORTED, "df11_encode_device: %llu elements", (unsigned long long)n);
-    if (((uintptr_t)d_words & 15) || ((uintptr_t)d_out & 15))
-        return report_error(DF11_E_ARG, "df11_encode_device: words and output must be 16-byte aligned");
+extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                                                const int *ndims, const uint64_t *dims, void *const *d_outs,
+                                                const uint64_t *out_caps, uint64_t *out_bytes, int hip_device,
+                                                hipStream_t stream) {
+    if (n_tensors < 0 || (n_tensors && (!d_words || !n_elems || !ndims || !dims || !d_outs || !out_caps || !out_bytes)))
+        return report_error(DF11_E_ARG, "df11_encode_device_batch: bad argument");
+    for (int t = 0; t < n_tensors; ++t) {
+        const uint64_t n = n_elems[t];
+        const int ndim = ndims[t];
+        if ((!d_words[t] && n) || !d_outs[t] || ndim < 0 || ndim > 8)
+            return report_error(DF11_E_ARG, "df11_encode_device_batch: tensor %d: bad argument", t);
+        uint64_t prod = 1;
+        for (int i = 0; i < ndim; ++i) prod *= dims[8 * t + i];
+        if ((ndim && prod != n) || (!ndim && n != 1))
+            return report_error(DF11_E_ARG, "tensor %d: shape does not match %llu elements", t, (unsigned long long)n);
+        if (n > (uint64_t(1) << 46)) return report_error(DF11_E_UNSUPPORTED, "tensor %d: %llu elements", t, (unsigned long long)n);
+        if (((uintptr_t)d_words[t] & 15) || ((uintptr_t)d_outs[t] & 15))
+            return report_error(DF11_E_ARG, "tensor %d: words and output must be 16-byte aligned", t);
+        if (out_caps[t] < df11_container_bound(n))
+            return report_error(DF11_E_ARG, "tensor %d: %llu bytes of output, below df11_container_bound (%llu)", t,
+                                (unsigned long long)out_caps[t], (unsigned long long)df11_container_bound(n));
+    }
+    if (n_tensors == 0) return DF11_OK;
     int prev = -1;
     if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(hip_device) != hipSuccess)
         return report_error(DF11_E_HIP, "df11_encode_device: device %d", hip_device);
@@ -340,59 +360,65 @@ extern "C" df11_status df11_encode_device(const void *d_words, uint64_t n, int n
         return report_error(DF11_E_HIP, "df11_encode_device: %s: %s", what, hipGetErrorString(e));
     };
     hipError_t e;
-    const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words;
 
-    // 1. histogram, to the host
-    uint64_t freq[256] = {};
-    if (n) {
-        unsigned long long *hist = nullptr;
-        if ((e = hipMallocAsync((void **)&hist, 256 * sizeof(unsigned long long), stream)) != hipSuccess)
-            return hip_fail(e, "hipMallocAsync");
-        int n_cu = 0;
-        (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device);
-        const uint64_t need = (n + kEncThreads * 8 - 1) / (kEncThreads * 8);
+    // 1. every tensor's histogram, back to the host in one copy
+    std::vector<uint64_t> freq((size_t)n_tensors * 256, 0);
+    unsigned long long *hist = nullptr;
+    const size_t hist_bytes = (size_t)n_tensors * 256 * sizeof(unsigned long long);
+    if ((e = hipMallocAsync((void **)&hist, hist_bytes, stream)) != hipSuccess) return hip_fail(e, "hipMallocAsync");
+    int n_cu = 0;
+    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device);
+    e = hipMemsetAsync(hist, 0, hist_bytes, stream);
+    for (int t = 0; t < n_tensors && e == hipSuccess; ++t) {
+        if (!n_elems[t]) continue;
+        const uint64_t need = (n_elems[t] + kEncThreads * 8 - 1) / (kEncThreads * 8);
         const int grid = (int)std::min<uint64_t>(need, (uint64_t)std::max(1, n_cu) * 8);
-        e = hipMemsetAsync(hist, 0, 256 * sizeof(unsigned long long), stream);
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL(enc_hist, dim3(grid), dim3(kEncThreads), 0, stream, w, n,
-                               (GLOBAL unsigned long long *)hist);
-            e = hipGetLastError();
+        hipLaunchKernelGGL(enc_hist, dim3(grid), dim3(kEncThreads), 0, stream, (const GLOBAL uint16_t *)d_words[t],
+                           n_elems[t], (GLOBAL unsigned long long *)(hist + 256 * (size_t)t));
+        e = hipGetLastError();
+    }
+    if (e == hipSuccess) e = hipMemcpyAsync(freq.data(), hist, hist_bytes, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    const hipError_t ef = hipFreeAsync(hist, stream);
+    if (e != hipSuccess) return hip_fail(e, "histogram");
+    if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+
+    // 2.-4. per tensor: the code, layout and header on the host; the header,
+    // chunk bits, chunk index and packing enqueued (nothing waits for them)
+    for (int t = 0; t < n_tensors; ++t) {
+        const uint64_t n = n_elems[t];
+        const uint64_t *f = freq.data() + 256 * (size_t)t;
+        CodeTable T;
+        build_code(f, T.len, T.code);
+        uint64_t total_bits = 0;
+        for (int sy = 0; sy < 256; ++sy) total_bits += f[sy] * T.len[sy];
+        const EncodeLayout L = encode_layout(n, total_bits);
+        Header h;
+        write_header(reinterpret_cast<uint8_t *>(h.w), n, ndims[t], dims + 8 * t, L, T.len);
+        uint8_t *out = static_cast<uint8_t *>(d_outs[t]);
+        if ((e = hipMemsetAsync(out, 0, L.total, stream)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+        hipLaunchKernelGGL(enc_header, dim3(1), dim3(kHeader / 4), 0, stream, h, (GLOBAL uint32_t *)out);
+        if (n) {
+            const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
+            GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
+            hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, w, n, T, ci);
+            hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n);
+            PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
+                        (GLOBAL uint8_t *)(out + L.off_raw)};
+            hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, pa, T);
         }
-        if (e == hipSuccess) e = hipMemcpyAsync(freq, hist, sizeof freq, hipMemcpyDeviceToHost, stream);
-        if (e == hipSuccess) e = hipStreamSynchronize(stream);
-        const hipError_t ef = hipFreeAsync(hist, stream);
-        if (e != hipSuccess) return hip_fail(e, "histogram");
-        if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
-    }
-
-    // the code, the layout and the header, on the host
-    CodeTable T;
-    build_code(freq, T.len, T.code);
-    uint64_t total_bits = 0;
-    for (int s = 0; s < 256; ++s) total_bits += freq[s] * T.len[s];
-    const EncodeLayout L = encode_layout(n, total_bits);
-    if (out_cap < L.total)
-        return report_error(DF11_E_ARG, "df11_encode_device: %llu bytes of output for a %llu-byte container",
-                            (unsigned long long)out_cap, (unsigned long long)L.total);
-    std::vector<uint8_t> header(kHeader);
-    write_header(header.data(), n, ndim, dims, L, T.len);
-    uint8_t *out = static_cast<uint8_t *>(d_out);
-    if ((e = hipMemsetAsync(out, 0, L.total, stream)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
-    if ((e = hipMemcpyAsync(out, header.data(), kHeader, hipMemcpyHostToDevice, stream)) != hipSuccess)
-        return hip_fail(e, "header copy");
-
-    // 2.-4. chunk bits, start bits, packing
-    if (n) {
-        GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
-        hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, w, n, T, ci);
-        hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n);
-        PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
-                    (GLOBAL uint8_t *)(out + L.off_raw)};
-        hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, pa, T);
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
+        out_bytes[t] = L.total;
     }
-    // (the header copy reads host memory that ends with this call)
-    if ((e = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    *out_bytes = L.total;
     return DF11_OK;
+}
+
+extern "C" df11_status df11_encode_device(const void *d_words, uint64_t n, int ndim, const uint64_t *dims,
+                                          void *d_out, uint64_t out_cap, uint64_t *out_bytes, int hip_device,
+                                          hipStream_t stream) {
+    if (!out_bytes || ndim < 0 || ndim > 8 || (ndim && !dims))
+        return report_error(DF11_E_ARG, "df11_encode_device: bad argument");
+    uint64_t d8[8] = {};
+    for (int i = 0; i < ndim; ++i) d8[i] = dims[i];
+    return df11_encode_device_batch(1, &d_words, &n, &ndim, d8, &d_out, &out_cap, out_bytes, hip_device, stream);
 }

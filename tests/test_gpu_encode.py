@@ -73,3 +73,22 @@ def test_workloads_match_host_encoder_and_round_trip(name):
         df11.decode(plan, 0, c, out)
         df11.check(plan)
         assert torch.equal(out, t.reshape(-1)), s.name
+
+
+def test_batch_of_mixed_tensors_matches_single_calls():
+    """One batched call (one wait on the stream) over tensors of mixed sizes,
+    shapes and distributions, an empty one included: each container equals
+    the oracle's."""
+    import torch
+    log("gpu encode batch")
+    ws = [W.normal_bf16((513, 77), seed=1), np.zeros(0, np.uint16), W.heavy_tail_bf16((100003,), seed=3),
+          W.exhaustive_words(), np.full(1, 0x3F80, np.uint16).reshape(()), W.normal_bf16((2 * 32768 + 9,), seed=4)]
+    # (np.ascontiguousarray would give the 0-d tensor a dimension)
+    ts = [torch.from_numpy(w.view(np.int16)).to("cuda") for w in ws]
+    assert [t.dim() for t in ts] == [w.ndim for w in ws]
+    cs = df11.encode_device_batch(ts)
+    torch.cuda.synchronize()
+    for w, c in zip(ws, cs):
+        want = oracle.encode(w)
+        got = c.cpu().numpy()
+        assert got.size == want.size and (got == want).all(), w.shape
