@@ -656,21 +656,26 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             na = ca;
             nb = cb;
         }
-        const uint32_t mn = wave_min(min(na, nb));
-        uint32_t T = __builtin_amdgcn_readfirstlane(mn >= 1 ? (mn - 1) / kMaxPerLookup : 0u);
-
-        // Peeks at p <= pmax stay inside the source; the counted loop moves a
-        // window by at most 24*T bits, so starts are kept at or below
-        // pmax - 24*T (only a container that disagrees with its index
-        // starts higher).
+        // Peeks at p <= pmax stay inside the source.  A start past pmax:
+        // only a container that disagrees with its index (valid starts lie
+        // before the chunk's last bit, and the stream's 16 bytes of padding
+        // and the staging area keep that below pmax).
         const uint32_t pmax = it.staged ? 32u * (kCodeWords - 1) : 32u * (it.n_words - 1);
-        T = min(T, pmax / 48u);
-        const uint32_t plim = pmax - 24u * T;
-        bad |= (sa > plim) | (sb > plim);
-        Chain A{min(sa, plim) + kPosBias, qa << 3, qa + na};
+        bad |= (sa > pmax) | (sb > pmax);
+        const uint32_t pa = min(sa, pmax), pb = min(sb, pmax);
+        // T counted look-ups: while no window of the wave can run out of
+        // codes (a look-up takes at most three) and no peek can pass pmax (a
+        // look-up moves a window at most 24 bits; a bound on T alone, 24 T
+        // below pmax for every start, would move the valid starts of chunks
+        // that end near pmax)
+        const uint32_t room = (pmax - max(pa, pb)) / 24u;
+        const uint32_t m = min(na, nb);
+        const uint32_t T =
+            __builtin_amdgcn_readfirstlane(wave_min(min(m >= 1 ? (m - 1) / kMaxPerLookup : 0u, room)));
+        Chain A{pa + kPosBias, qa << 3, qa + na};
         const L2Bounds l2{(uint32_t)__builtin_amdgcn_readfirstlane(L.lut.l2_base),
                           (uint32_t)__builtin_amdgcn_readfirstlane(L.lut.l2_size)};
-        Chain B{min(sb, plim) + kPosBias, qb << 3, qb + nb};
+        Chain B{pb + kPosBias, qb << 3, qb + nb};
         if (it.staged) {
             // code-word reads: codes[k .. k+2] with k = P / 32 <= kCodeWords - 1
             const LdsCodes src{L.codes, pmax + kPosBias};

@@ -99,6 +99,18 @@ def heavy_tail_bf16(shape, seed: int = 0, threads: Optional[int] = None) -> np.n
     return base.reshape(shape)
 
 
+def exponent_mix_bf16(n: int, seed: int, probs, e0: int = 120) -> np.ndarray:
+    """n BF16 words whose biased exponent is e0 + k with probability probs[k],
+    with a random sign and 7-bit fraction: a tensor whose coded size per
+    element is set directly by the exponent distribution."""
+    rng = np.random.default_rng(seed)
+    p = np.asarray(probs, np.float64)
+    e = e0 + rng.choice(len(p), size=n, p=p / p.sum())
+    sign = rng.integers(0, 2, n)
+    frac = rng.integers(0, 128, n)
+    return ((sign << 15) | (e << 7) | frac).astype(np.uint16)
+
+
 @dataclass
 class TensorSpec:
     name: str

@@ -222,6 +222,45 @@ def test_corrupted_stream_sets_the_flag():
     assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
+@pytest.mark.parametrize("r,n", [(0.0603, 32768 * 64), (0.09, 32768 * 16 + 32000)])
+def test_chunks_ending_near_the_source_end(r, n):
+    """Six exponents at probability q and four at r (3- and 4-bit codes, 3 +
+    4r bits per element).  At r = 0.0603 (3.24 bits) many chunks' codes end
+    within a few hundred bits of the 13 KiB LDS staging area's end; at r =
+    0.09 (3.36 bits) the codes are read from global memory and the last
+    chunk ends at the stream's end.  Windows there start within 24 bits per
+    counted look-up of the end of what the decoder's peeks may read: each
+    still starts where its index says, and the tensor decodes exactly, in a
+    batch and on its own."""
+    torch = _torch()
+    log(f"chunks ending near the source end r={r}")
+    q = (1 - 4 * r) / 6
+    w = W.exponent_mix_bf16(n, seed=41, probs=[q] * 6 + [r] * 4)
+    small = W.normal_bf16((5000,), seed=42)
+    cs = oracle_encode_many([w, small])
+    h = oracle.header(cs[0])
+    ci = cs[0][h["off_chunk_index"]:h["off_chunk_index"] + 16 * (h["n_chunks"] + 1)].view(np.uint64)
+    bits = np.diff(ci[0::2].astype(np.int64))
+    if r < 0.07:
+        assert ((bits > 105900) & (bits < 106240)).sum() >= 8   # staged, near the cap
+    else:
+        assert bits[-1] > 3.3 * 32000                           # not staged
+    plan = df11.Plan(cs)
+    dcs = [to_device_u8(c) for c in cs]
+    bufs = [empty_words(m, guard=32) for m in (n, 5000)]
+    df11.decode_batch(plan, dcs, [o for _, o in bufs])
+    df11.check(plan)
+    for src, (buf, _), m in zip([w, small], bufs, (n, 5000)):
+        host = buf.cpu().numpy().view(np.uint16)
+        assert (host[32:32 + m] == src).all()
+    buf, out = empty_words(n, guard=32)
+    df11.decode(plan, 0, dcs[0], out)
+    df11.check(plan)
+    host = buf.cpu().numpy().view(np.uint16)
+    assert (host[32:32 + n] == w).all()
+    assert (host[:32] == 0x5A5A).all() and (host[32 + n:] == 0x5A5A).all()
+
+
 def test_source_hash_verifies_decoded_output():
     """Hashed containers (the oracle's, flag DF11_FLAG_SHA256) decode like
     plain ones; the decoded device words verify against the header's hash
