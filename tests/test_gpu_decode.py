@@ -10,7 +10,7 @@ import oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from gpu_util import empty_words, log, oracle_encode_many, to_device_u8, to_device_words
+from gpu_util import ENTROPY_MIXES, empty_words, entropy_mix_words, log, oracle_encode_many, to_device_u8, to_device_words
 
 pytestmark = pytest.mark.gpu
 
@@ -261,30 +261,14 @@ def test_chunks_ending_near_the_source_end(r, n):
     assert (host[:32] == 0x5A5A).all() and (host[32 + n:] == 0x5A5A).all()
 
 
-def _mix(r):
-    q = (1 - 4 * r) / 6
-    return [q] * 6 + [r] * 4
-
-
-ENTROPY_MIXES = {
-    "1bit": [1, 1], "1.5bit": [2, 1, 1], "2bit": [1] * 4, "2.4bit": [1] * 5, "3bit": [1] * 8,
-    "3.2bit": _mix(0.05), "3.24bit": _mix(0.0603), "3.28bit": _mix(0.07), "3.36bit": _mix(0.09),
-    "3.35bit": _mix(0.12), "3.7bit": [1] * 12, "4bit": [1] * 16, "5bit": [1] * 32, "6bit": [1] * 64,
-    "7bit": [1] * 128, "7.7bit": [1] * 200,
-}
-
-
 @pytest.mark.parametrize("name", list(ENTROPY_MIXES))
 def test_exponent_entropy_sweep(name):
     """Code rates from 1 to 7.7 bits per element (exponents drawn from a given
     distribution, random sign and fraction), so that chunk code sizes fall on
     both sides of the LDS staging area and anywhere relative to the ends of
     what the decoder reads; 40 whole chunks and a ragged one, bit-exact."""
-    torch = _torch()
-    probs = ENTROPY_MIXES[name]
     log(f"entropy sweep {name}")
-    n = 32768 * 40 + 3001
-    w = W.exponent_mix_bf16(n, seed=len(probs) * 7 + 3, probs=probs, e0=max(1, 127 - len(probs) // 2))
+    w = entropy_mix_words(name, 32768 * 40 + 3001)
     got, ok_guard, _ = _decode_one(w, guard=32)
     assert ok_guard
     assert (got == w).all()

@@ -10,7 +10,7 @@ import oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from gpu_util import log
+from gpu_util import ENTROPY_MIXES, entropy_mix_words, log
 
 pytestmark = pytest.mark.gpu
 
@@ -27,6 +27,18 @@ def _gpu_encode(w, shape=None):
 def test_edge_sizes_match_oracle_bytes(n):
     log(f"gpu encode {n}")
     w = W.normal_bf16((n,), seed=n)
+    want = oracle.encode(w)
+    got = _gpu_encode(w)
+    assert got.size == want.size and (got == want).all()
+
+
+@pytest.mark.parametrize("name", list(ENTROPY_MIXES))
+def test_exponent_entropy_sweep_matches_oracle_bytes(name):
+    """Code rates from 1 to 7.7 bits per element: every lane's bit count,
+    the words two lanes share and the window entries, over 6 whole chunks
+    and a ragged one."""
+    log(f"gpu encode entropy {name}")
+    w = entropy_mix_words(name, 32768 * 6 + 3001)
     want = oracle.encode(w)
     got = _gpu_encode(w)
     assert got.size == want.size and (got == want).all()

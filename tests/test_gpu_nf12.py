@@ -10,7 +10,7 @@ from oracle import nf12 as nf12_oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from gpu_util import empty_words, log, to_device_u8
+from gpu_util import ENTROPY_MIXES, empty_words, entropy_mix_words, log, to_device_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -31,6 +31,19 @@ def test_edge_sizes_bit_exact(n):
     log(f"nf12 size {n}")
     w = W.normal_bf16((n,), seed=n)
     w[::53] = 0                       # outlier groups spread through the tensor
+    c = df11.nf12_encode(w)
+    got = _decode(c, n)
+    assert (got == w).all()
+    assert (got == nf12_oracle.decode(c, n)).all()
+
+
+@pytest.mark.parametrize("name", list(ENTROPY_MIXES))
+def test_exponent_spread_sweep(name):
+    """Exponent distributions from 2 to 200 values: from no escaped group to
+    nearly all groups escaped, against the oracle and the source words."""
+    log(f"nf12 exponent spread {name}")
+    n = 100000 + 13
+    w = entropy_mix_words(name, n)
     c = df11.nf12_encode(w)
     got = _decode(c, n)
     assert (got == w).all()
