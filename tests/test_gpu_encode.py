@@ -10,7 +10,8 @@ import oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from gpu_util import ENTROPY_MIXES, entropy_mix_words, log
+from exponent_mixes import ENTROPY_MIXES, entropy_mix_words
+from gpu_util import log
 
 pytestmark = pytest.mark.gpu
 

@@ -10,7 +10,8 @@ from oracle import nf12 as nf12_oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from gpu_util import ENTROPY_MIXES, empty_words, entropy_mix_words, log, to_device_u8
+from exponent_mixes import ENTROPY_MIXES, entropy_mix_words
+from gpu_util import empty_words, log, to_device_u8
 
 pytestmark = pytest.mark.gpu
 

@@ -12,6 +12,8 @@ import oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
+from exponent_mixes import ENTROPY_MIXES, entropy_mix_words
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -37,6 +39,18 @@ def test_encoder_matches_oracle_bytes(n):
     a = df11.encode(w)
     b = oracle.encode(w)
     assert a.size == b.size and (a == b).all()
+
+
+@pytest.mark.parametrize("name", list(ENTROPY_MIXES))
+def test_encoder_matches_oracle_over_code_rates(name):
+    """Code rates from 1 to 7.7 bits per element, over two whole chunks and a
+    ragged one: the host encoder's bytes are the oracle's, validate, and the
+    oracle decodes them back to the words."""
+    w = entropy_mix_words(name, 32768 * 2 + 1001)
+    c = df11.encode(w, threads=4)
+    assert (c == oracle.encode(w)).all()
+    assert df11.validate(c)["n_elems"] == w.size
+    assert (oracle.decode(c, w.size) == w).all()
 
 
 def test_encoder_matches_oracle_on_special_tensors():
