@@ -76,11 +76,12 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(containers, infos, min_wall_s: float = 1.5, max_wall_s: float = 20.0):
+def cpu_baseline(containers, infos, min_wall_s: float = 1.5, max_wall_s: float = 20.0, workload: str = WORKLOAD):
     """Oracle decode of whole chunks of the same containers on host threads:
     whole passes over every chunk until at least `min_wall_s` of wall time
     (about 10-30 s of CPU work on 8-16 threads), or a prefix of one pass when
-    a pass would take longer than `max_wall_s`."""
+    a pass would take longer than `max_wall_s`; then one thread over a
+    prefix of the same chunk list for `min_wall_s`."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -132,7 +133,7 @@ def cpu_baseline(containers, infos, min_wall_s: float = 1.5, max_wall_s: float =
         pass
     return {"value": round(2.0 * done / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{what} of the {WORKLOAD} containers ({done} elements decoded), "
+            "sample": f"{what} of the {workload} containers ({done} elements decoded), "
                       f"bit-serial oracle decode on {threads} threads, {dt:.1f} s wall",
             "single_thread": {"value": round(2.0 * one / dt1 / 1e9, 4), "unit": "GB/s",
                               "sample": f"{one} elements of the same chunk list, {dt1:.1f} s wall"},
@@ -226,9 +227,12 @@ def stack_loop(passes: int, warmup: int):
     plans, dconts, hdrs, nconts, counts, shas = [], [], [], [], [], []
     read = {"df11": 0, "nf12": 0}
     stored = {"df11": 0, "nf12": 0}
-    for g in groups:
+    sample = []   # host containers of layer 0 and the embedding, for the oracle's rate
+    for gi, g in enumerate(groups):
         ws = [s.make(threads=threads).reshape(-1) for s in g]
         cs = [df11.encode(w, shape=s.shape, threads=threads) for w, s in zip(ws, g)]
+        if gi in (0, len(groups) - 1):
+            sample += cs
         ns = [df11.nf12_encode(w, threads=threads) for w in ws]
         shas.append([hashlib.sha256(w.view(np.uint8)).hexdigest() for w in ws])
         counts.append([w.size for w in ws])
@@ -335,12 +339,17 @@ def stack_loop(passes: int, warmup: int):
                     "by_streams": rows, "block_launch_ms_mean": blk, "embedding_launch_ms": emb,
                     "bit_exact": exact(fmt)}
     best = max(res["df11"]["by_streams"], key=lambda r: r["value"])
+    # the oracle on layer 0 and the embedding; its rate per element is the
+    # same on every layer, so a whole pass would take 2 n / rate
+    cpu = cpu_baseline(sample, [df11.validate(c) for c in sample], min_wall_s=1.5, max_wall_s=10.0,
+                       workload="llama8b_stack layer 0 + embedding")
+    cpu["pass_s_extrapolated"] = round(2.0 * n_total / (cpu["value"] * 1e9), 1)
     print(json.dumps({
         "metric": "just-in-time layer loop over the resident 32-layer stack: sustained decode rate",
         "value": best["value"], "unit": "GB/s of BF16 output", "streams": best["streams"],
         "passes": passes, "warmup": warmup, "launches_per_pass": len(groups),
         "config": {"workload": "llama8b_stack", "layers": 32, "elements": n_total, "bf16_bytes": 2 * n_total},
-        "df11": res["df11"], "nf12": res["nf12"],
+        "df11": res["df11"], "nf12": res["nf12"], "cpu_baseline": cpu,
     }), flush=True)
     if not (res["df11"]["bit_exact"] and res["nf12"]["bit_exact"]):
         sys.exit(1)
@@ -426,7 +435,9 @@ def workload_table(rounds: int = 3):
                      "ratio": round(sum(c.size for c in conts) / (2 * n), 4),
                      "algorithmic_bytes": algo, "warm": stats(warm), "flushed": stats(cold),
                      "write_flushed": stats(wcold),
-                     "bit_exact": bool(ok)})
+                     "bit_exact": bool(ok),
+                     "cpu_baseline": cpu_baseline(conts, plan.infos, min_wall_s=1.0, max_wall_s=8.0,
+                                                  workload=name)})
         del dc, outs, plan
     print(json.dumps({"metric": "DF11 decode of each workload: one batched call, warm and with the "
                                 "last-level cache flushed", "results": rows}), flush=True)
