@@ -29,7 +29,9 @@
 //      word, and ORs the exponent bytes (rotated, see rot_exp) into a 32 KiB
 //      LDS tile at their chunk positions.  A counted loop with no per-lane
 //      control flow runs while no window of the wave can run out (each
-//      look-up takes at most three codes); a masked loop finishes;
+//      look-up takes at most three codes) and no peek can pass the end of
+//      the staged words (each moves a window at most 24 bits); a masked
+//      loop finishes;
 //   4. check: a window must end exactly where the next non-empty window's
 //      first code starts (or at the chunk end); otherwise the plan's flag is
 //      set;
