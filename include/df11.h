@@ -222,7 +222,12 @@ df11_status df11_decode_batch(df11_plan_t plan, const void *const *d_containers,
 
 /* Synchronize `stream`, then read and clear the plan's corruption flag:
  * DF11_OK, or DF11_E_CORRUPT if some decode since the last check found a
- * lane whose codes did not end where the index says the next one starts. */
+ * window whose codes did not end where the index says the next window's
+ * first code starts (or that starts past the chunk's bytes).  The flag is
+ * one per plan: a decode of the plan on another stream that is still running
+ * may set it after the read, and its finding then waits for the next check;
+ * one that sets it between the read and the clear is lost, so check after the
+ * decodes of interest have finished. */
 df11_status df11_check(df11_plan_t plan, hipStream_t stream);
 
 /* ------------------------------------------------------------ measurement */
