@@ -262,6 +262,30 @@ def test_chunks_ending_near_the_source_end(r, n):
     assert (host[:32] == 0x5A5A).all() and (host[32 + n:] == 0x5A5A).all()
 
 
+@pytest.mark.parametrize("order", ["short_first", "long_first"])
+def test_chunks_sorted_by_code_length(order):
+    """Each chunk's words sorted by code length: one exponent at probability
+    1/2 (a 1-bit code) and the other 255 uniform (8- and 9-bit codes), so
+    that the windows over the short codes hold hundreds of codes and those
+    over the long ones a few dozen. The wave minimum that bounds the counted
+    look-ups is small, most look-ups run masked, and the waves differ
+    widely in work."""
+    log(f"chunks sorted by code length, {order}")
+    w = W.exponent_mix_bf16(32768 * 12 + 999, seed=5, probs=[255.0] + [1.0] * 255, e0=0)
+    code_len = oracle.header(oracle.encode(w))["code_len"].astype(np.int64)
+    for c0 in range(0, w.size, 32768):
+        part = w[c0:c0 + 32768]
+        key = code_len[(part >> 7) & 0xFF]
+        idx = np.argsort(key if order == "short_first" else -key, kind="stable")
+        w[c0:c0 + 32768] = part[idx]
+    got, ok_guard, c = _decode_one(w, guard=32)
+    h = oracle.header(c)
+    win = c[h["off_windows"]:h["off_windows"] + 1024 * h["n_chunks"]].view(np.uint16) & 0x7FF
+    assert win.max() >= 250 and win[win > 0].min() <= 40   # the skew is there
+    assert ok_guard
+    assert (got == w).all()
+
+
 @pytest.mark.parametrize("name", list(ENTROPY_MIXES))
 def test_exponent_entropy_sweep(name):
     """Code rates from 1 to 7.7 bits per element (exponents drawn from a given
