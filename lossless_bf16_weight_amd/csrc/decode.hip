@@ -725,6 +725,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         //      raw registers take the next item's bytes right after use.
         //      The next item's window entries, code bytes and tables are
         //      requested first: they are needed first.
+        // (the assembly issues all of the kernel's memory traffic, the
+        // decode only VALU and LDS work: a wave assembling goes first, so
+        // that the compute unit's other waves' decodes do not hold back its
+        // loads and stores; about 1% faster)
+        __builtin_amdgcn_s_setprio(3);
         const Item nx = item_at(a, L, sl ^ 1u);
         const uint32_t win_nx = load_windows(nx, tid);
         load_codes(nx, tid, cw);
@@ -763,6 +768,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // the next item's tables (nothing reads them during the assembly)
         put_lut(L, tid, lr);
         win = win_nx;
+        __builtin_amdgcn_s_setprio(0);
     }
     if (__ballot(bad_any) && lane == 0) atomicOr(a.status, 1u);
     // The last workgroup to finish (every ticket of the launch has been
