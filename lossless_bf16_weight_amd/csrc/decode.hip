@@ -276,7 +276,11 @@ __device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent) {
     const uint32_t off = tile_off(c.p8 >> 5);
     tile_or(L, off, (uint32_t)x);
     tile_or(L, off + 4, (uint32_t)(x >> 32));
-    c.p8 += ent_count(ent) << 3;
+    // p8 += 8 x count as one v_lshl_add (the compiler's shift, mask and add
+    // is one VALU instruction more per chain and look-up)
+    uint32_t p8;
+    asm("v_lshl_add_u32 %0, %1, 3, %2" : "=v"(p8) : "v"(ent_count(ent)), "v"(c.p8));
+    c.p8 = p8;
     c.P += ent_bits(ent);
 }
 
