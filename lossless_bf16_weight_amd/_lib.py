@@ -18,6 +18,8 @@ LIB_PATH = os.path.join(_PKG, "libdf11.so")
 OK, E_ARG, E_FORMAT, E_UNSUPPORTED, E_HIP, E_CORRUPT, E_NOMEM = range(7)
 FLAG_SHA256 = 1
 MAX_BATCH = 64
+# DF11_ABI_VERSION of include/df11.h that these argument lists follow
+ABI_VERSION = 2
 
 
 class DF11Error(RuntimeError):
