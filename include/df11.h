@@ -99,7 +99,8 @@ typedef struct {
     uint64_t total_bits;
     uint64_t container_bytes;     /* whole container */
     uint64_t meta_bytes;          /* header + chunk index + window index (what df11_plan needs) */
-    uint64_t bytes_read_per_decode;  /* index + stream + raw bytes a decode reads */
+    uint64_t bytes_read_per_decode;  /* what a decode reads: the plan's 64-byte record per chunk,
+                                        the window index, the code bits and the raw bytes */
     uint8_t code_len[256];
     uint32_t flags;               /* header flags (DF11_FLAG_SHA256) */
     uint8_t sha256[32];           /* the source hash when flags has DF11_FLAG_SHA256, else zero */
@@ -180,7 +181,13 @@ df11_status df11_verify_words(const void *host_meta, size_t bytes, const uint16_
 
 /* -------------------------------------------------------------------- plan */
 
-/* Build a decode plan for n_tensors containers.  host_meta[t] points to HOST
+/* Build a decode plan for n_tensors containers (the set of weights a caller
+ * keeps compressed in GPU memory and decodes as it needs them: mlx-dfloat
+ * project page, introduction).  Validation is the structural check the
+ * df11pack page's verify runs with no source ("Use"); the decode tables are
+ * built from the code lengths alone, every entry no valid stream reaches set
+ * to zero (df11pack page, "Beyond the official format", the correct-LUTs
+ * option).  host_meta[t] points to HOST
  * memory holding (at least) the metadata prefix of container t, of
  * host_meta_bytes[t] bytes.  Every prefix is validated (df11_validate).  The
  * plan builds each tensor's decode tables (a 1024-entry first-level table
@@ -201,7 +208,11 @@ df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info)
 
 /* ------------------------------------------------------------------ decode */
 
-/* Decode tensor `tensor` of the plan.  d_container: DEVICE pointer to the
+/* Decode tensor `tensor` of the plan: rebuild every BF16 word from its raw
+ * byte (sign, 7-bit fraction) and its exponent byte, read as a prefix code
+ * from the stream, bit for bit the original (mlx-dfloat project page,
+ * introduction and its 16-bit weight diagram; df11pack project page,
+ * introduction).  d_container: DEVICE pointer to the
  * whole container (16-byte aligned, at least container_bytes long, same
  * bytes as the prefix given to df11_plan).  d_out: DEVICE pointer to
  * n_elems * 2 bytes (16-byte aligned), not overlapping the container.
@@ -214,13 +225,17 @@ df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info)
 df11_status df11_decode(df11_plan_t plan, int tensor, const void *d_container,
                         void *d_out, hipStream_t stream);
 
-/* Decode every tensor of the plan in one launch (one launch per
- * DF11_MAX_BATCH tensors): d_containers[t] / d_outs[t] are HOST arrays of
+/* Decode every tensor of the plan in one launch: a block's weights decoded
+ * together, just before they are used (mlx-dfloat project page,
+ * introduction: each block decoded on the GPU as it runs); one launch per
+ * DF11_MAX_BATCH tensors.  d_containers[t] / d_outs[t] are HOST arrays of
  * DEVICE pointers, with the rules of df11_decode for each t. */
 df11_status df11_decode_batch(df11_plan_t plan, const void *const *d_containers,
                               void *const *d_outs, hipStream_t stream);
 
-/* Synchronize `stream`, then read and clear the plan's corruption flag:
+/* The decode-side analogue of the df11pack page's verify ("Use": a check
+ * passes or fails; exit codes 0, 1, 2): synchronize `stream`, then read and
+ * clear the plan's corruption flag:
  * DF11_OK, or DF11_E_CORRUPT if some decode since the last check found a
  * window whose codes did not end where the index says the next window's
  * first code starts (or that starts past the chunk's bytes).  The flag is

@@ -291,10 +291,11 @@ void fill_info(const Meta &M, df11_tensor_info *info) {
     info->total_bits = L.total_bits;
     info->container_bytes = L.total;
     info->meta_bytes = L.off_stream;
-    // chunk index (the plan's records stand in for it), one 16-bit entry per
-    // window, the code bits and one raw byte per element
+    // what a decode reads: the plan's 64-byte record per chunk (the kernel
+    // never reads the container's chunk index), one 16-bit entry per window,
+    // the code bits and one raw byte per element
     info->bytes_read_per_decode =
-        (L.n_chunks + (L.n_chunks ? 1 : 0)) * 16 + L.n_chunks * kWindows * 2 + (L.total_bits + 7) / 8 + L.n;
+        L.n_chunks * sizeof(ChunkRec) + L.n_chunks * kWindows * 2 + (L.total_bits + 7) / 8 + L.n;
     memcpy(info->code_len, M.code_len, 256);
     info->flags = M.flags;
     memcpy(info->sha256, M.sha256, 32);

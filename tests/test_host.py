@@ -88,7 +88,9 @@ def test_validate_accepts_and_describes():
     assert info["container_bytes"] == c.size
     assert (info["code_len"] == h["code_len"]).all()
     n_ch = h["n_chunks"]
-    assert info["bytes_read_per_decode"] == (n_ch + 1) * 16 + n_ch * 512 * 2 + \
+    # a decode reads the plan's 64-byte record per chunk, the window index,
+    # the code bits and the raw bytes (not the container's chunk index)
+    assert info["bytes_read_per_decode"] == n_ch * 64 + n_ch * 512 * 2 + \
         (h["total_bits"] + 7) // 8 + w.size
     # the metadata prefix alone is enough
     assert df11.validate(c[:info["meta_bytes"]])["n_elems"] == w.size
