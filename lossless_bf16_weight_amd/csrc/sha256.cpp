@@ -154,7 +154,7 @@ void sha256(const void *data, uint64_t bytes, uint8_t out[32]) {
     // the tail, a 1 bit, zeros and the message length in bits, big-endian
     uint8_t tail[128] = {};
     const uint64_t rest = bytes - 64 * whole;
-    memcpy(tail, p + 64 * whole, rest);
+    if (rest) memcpy(tail, p + 64 * whole, rest);   // (p may be NULL for an empty message)
     tail[rest] = 0x80;
     const uint64_t tail_len = rest + 9 <= 64 ? 64 : 128;
     const uint64_t bits = bytes * 8;

@@ -1,0 +1,133 @@
+// Sanitizer driver for the host code of libdf11 (validation, encoders, SHA-256,
+// NF12 host code), built with g++ -fsanitize=address,undefined on the CPU.
+//
+// Reads a manifest of "<kind> <path>" lines:
+//   df11  <container file>  df11_validate on the whole file and on prefixes
+//   nf12  <container file>  df11_nf12_validate on the whole file and on prefixes
+//   words <16-bit words>    df11_encode (1 and 4 threads), df11_encode_ex with the
+//                           source hash, df11_validate and df11_verify_words on
+//                           the result, df11_nf12_encode + validate; the DF11
+//                           container is written to <path>.asan.df11
+// Any memory error or undefined behaviour aborts with the sanitizer's report;
+// a status that contradicts the input's kind exits 3.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "df11.h"
+#include "df11_internal.hpp"
+#include "nf12_internal.hpp"
+
+// The kernels are not part of this build: the driver never plans or decodes.
+namespace df11 {
+hipError_t launch_decode(const DecodeArgs &, int, hipStream_t) { abort(); }
+int decode_wgs_per_cu() { abort(); }
+hipError_t launch_bw_control(const void *, uint64_t, void *, uint64_t, int, hipStream_t) { abort(); }
+hipError_t launch_nf12_decode(const Nf12Args &, int, hipStream_t) { abort(); }
+}  // namespace df11
+
+static std::vector<uint8_t> read_file(const char *path) {
+    std::vector<uint8_t> b;
+    FILE *f = fopen(path, "rb");
+    if (!f) {
+        fprintf(stderr, "cannot open %s\n", path);
+        exit(2);
+    }
+    uint8_t buf[1 << 16];
+    size_t k;
+    while ((k = fread(buf, 1, sizeof buf, f)) > 0) b.insert(b.end(), buf, buf + k);
+    fclose(f);
+    return b;
+}
+
+// Validates prefixes of a container; each copy is exactly as long as the
+// prefix, so a read past it is a heap overflow the sanitizer reports.
+template <class F>
+static void prefixes(const std::vector<uint8_t> &c, F validate) {
+    const size_t cuts[] = {0, 1, 8, 16, 100, 255, 256, 511, 512, 513, 1024, 4096, c.size() / 3, c.size() / 2,
+                           c.size() > 0 ? c.size() - 1 : 0, c.size()};
+    for (size_t n : cuts) {
+        if (n > c.size()) continue;
+        std::vector<uint8_t> p(c.begin(), c.begin() + n);
+        validate(p.empty() ? nullptr : p.data(), n);
+    }
+}
+
+static int check_words(const char *path) {
+    std::vector<uint8_t> raw = read_file(path);
+    const uint64_t n = raw.size() / 2;
+    std::vector<uint16_t> w(n);
+    if (n) memcpy(w.data(), raw.data(), 2 * n);
+    const uint64_t dims[1] = {n};
+    const uint64_t cap = df11_container_bound(n);
+    std::vector<uint8_t> a(cap), b(cap), h(cap);
+    uint64_t na = 0, nb = 0, nh = 0;
+    if (df11_encode(w.data(), n, 1, dims, a.data(), cap, &na, 1) != DF11_OK) return 3;
+    if (df11_encode(w.data(), n, 1, dims, b.data(), cap, &nb, 4) != DF11_OK) return 3;
+    if (na != nb || memcmp(a.data(), b.data(), na) != 0) return 3;
+    if (df11_encode_ex(w.data(), n, 1, dims, DF11_FLAG_SHA256, h.data(), cap, &nh, 3) != DF11_OK) return 3;
+    if (nh != na) return 3;
+    df11_tensor_info info;
+    if (df11_validate(a.data(), na, &info) != DF11_OK || info.n_elems != n) return 3;
+    if (df11_validate(h.data(), nh, &info) != DF11_OK) return 3;
+    if (df11_verify_words(h.data(), nh, w.data(), n) != DF11_OK) return 3;
+    if (df11_verify_words(a.data(), na, w.data(), n) != DF11_E_UNSUPPORTED) return 3;
+    // a container smaller than the bound: the encoder must refuse, not overrun
+    if (na > 1 && df11_encode(w.data(), n, 1, dims, b.data(), na - 1, &nb, 2) == DF11_OK) return 3;
+    const uint64_t ncap = df11_nf12_bound(n);
+    std::vector<uint8_t> f(ncap ? ncap : 1);
+    uint64_t nf = 0;
+    if (df11_nf12_encode(w.data(), n, f.data(), ncap, &nf, 2) != DF11_OK) return 3;
+    uint64_t ne = 0;
+    if (df11_nf12_validate(f.data(), nf, &ne) != DF11_OK || ne != n) return 3;
+    std::string out = std::string(path) + ".asan.df11";
+    FILE *o = fopen(out.c_str(), "wb");
+    if (!o || fwrite(a.data(), 1, na, o) != na) return 2;
+    fclose(o);
+    return 0;
+}
+
+int main(int argc, char **argv) {
+    if (argc != 2) {
+        fprintf(stderr, "usage: %s MANIFEST\n", argv[0]);
+        return 2;
+    }
+    FILE *m = fopen(argv[1], "r");
+    if (!m) return 2;
+    char kind[16], path[4096];
+    long n_df11 = 0, n_nf12 = 0, n_words = 0;
+    while (fscanf(m, "%15s %4095s", kind, path) == 2) {
+        if (!strcmp(kind, "df11")) {
+            const std::vector<uint8_t> c = read_file(path);
+            prefixes(c, [](const uint8_t *p, size_t n) {
+                df11_tensor_info info;
+                (void)df11_validate(p, n, &info);
+                (void)df11_validate(p, n, nullptr);
+            });
+            ++n_df11;
+        } else if (!strcmp(kind, "nf12")) {
+            const std::vector<uint8_t> c = read_file(path);
+            prefixes(c, [](const uint8_t *p, size_t n) {
+                uint64_t ne;
+                (void)df11_nf12_validate(p, n, &ne);
+            });
+            ++n_nf12;
+        } else if (!strcmp(kind, "words")) {
+            const int r = check_words(path);
+            if (r) {
+                fprintf(stderr, "words %s: status %d\n", path, r);
+                return r;
+            }
+            ++n_words;
+        } else {
+            return 2;
+        }
+    }
+    fclose(m);
+    printf("ok: %ld df11, %ld nf12, %ld word files\n", n_df11, n_nf12, n_words);
+    return 0;
+}
