@@ -131,7 +131,7 @@ def sha256(data) -> bytes:
 
 
 def encode(words: np.ndarray, shape=None, sha256: bool = False) -> np.ndarray:
-    """Encode a uint16 array (BF16 bit patterns) into a version-5 container;
+    """Encode a uint16 array (BF16 bit patterns) into a version-4 container;
     with sha256, the header holds the SHA-256 of the source words."""
     w = np.ascontiguousarray(words, dtype=np.uint16).reshape(-1)
     shape = tuple(words.shape) if shape is None else tuple(shape)
@@ -187,7 +187,7 @@ def check(container: np.ndarray) -> int:
     return int(lib().oracle_check(_p(c, ctypes.c_uint8), c.size))
 
 
-# ---- header fields of a version-5 container (layout in df11_oracle.c) ----
+# ---- header fields of a version-4 container (layout in df11_oracle.c) ----
 
 def header(container: np.ndarray) -> dict:
     c = np.ascontiguousarray(container, dtype=np.uint8)
@@ -205,8 +205,7 @@ def header(container: np.ndarray) -> dict:
     return {
         "n_elems": u64(16), "ndim": ndim,
         "dims": [u64(32 + 8 * i) for i in range(ndim)],
-        "chunk_elems": u32(28), "max_code_len": int(c[96]), "entry_bytes": int(c[97]),
-        "windows": u16(98), "window_base": u32(128),
+        "chunk_elems": u32(28), "max_code_len": int(c[96]), "windows": u16(98),
         "n_chunks": u32(100), "total_bits": u64(104),
         "off_chunk_index": u64(112), "off_windows": u64(120),
         "off_stream": u64(136), "stream_bytes": u64(144), "off_raw": u64(152),

@@ -29,32 +29,30 @@
  *    0 is the first bit;
  *  - raw byte: (sign << 7) | fraction, i.e. ((w >> 8) & 0x80) | (w & 0x7F);
  *  - chunks of 32768 elements (64 KiB of BF16 output), each with its start
- *    bit; a chunk's codes are cut into windows of 64 consecutive codes (the
- *    last one of a chunk may hold fewer); per window except each chunk's
- *    last, its length in bits minus the tensor's smallest such length, in
- *    one byte (two when some length is 256 or more above the smallest): a
- *    block index of 520 bytes per chunk, in the spirit of the df11pack
- *    page's experimental 8-bit index ("Beyond the official format").  A
- *    window's first code is the prefix sum of the lengths before it; its
- *    first output element is 64 times its number.
+ *    bit; the N bits of a chunk are cut into 512 windows as evenly as
+ *    integers allow (window i starts floor(i * N / 512) bits after the
+ *    chunk's first bit), with one 16-bit entry per window: the number of
+ *    codes that start in it (at most 1536, as a window has at most
+ *    ceil(32768 * 24 / 512) bits, so 11 bits) and the offset of the first of
+ *    them from the window's first bit (under 24, so 5 bits): a smaller block
+ *    index, in the spirit of the df11pack page's experimental 8-bit index
+ *    ("Beyond the official format").
  *
- * Container version 5 (all integers little-endian, sections 256-byte aligned):
+ * Container version 4 (all integers little-endian, sections 256-byte aligned):
  *   header, 512 bytes:
- *     0  char[8] magic "DF11HIPC"     8  u32 version (5)   12 u32 flags
+ *     0  char[8] magic "DF11HIPC"     8  u32 version (4)   12 u32 flags
  *    16  u64 n_elems                 24  u32 ndim          28 u32 chunk_elems
- *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 entry_bytes
+ *    32  u64 dims[8]                 96  u8 max_code_len   97 u8 reserved
  *    98  u16 windows                100  u32 n_chunks     104 u64 total_bits
- *   112  u64 off_chunk_index        120  u64 off_windows  128 u32 window_base
- *   132  u32 reserved               136  u64 off_stream   144 u64 stream_bytes
- *   152  u64 off_raw                160  u64 raw_bytes    168 u64 total_bytes
- *   176  u8 sha256[32]              208  u8 code_len[256] 464 reserved[48]
- *   chunk index: (n_chunks+1) x u64 start_bit, the last = total_bits
- *   windows:     n_chunks x 512 x entry_bytes: for chunk c of m elements and
- *                w = ceil(m / 64) windows, entry k < w - 1 is the bit length
- *                of codes 64k .. 64k+63 of the chunk minus window_base;
- *                entries w - 1 .. 511 are zero.  window_base = the smallest
- *                of those lengths over the tensor (0 when there is none);
- *                entry_bytes = 1 when every entry fits a byte, else 2
+ *   112  u64 off_chunk_index        120  u64 off_windows  128 u64 reserved
+ *   136  u64 off_stream             144  u64 stream_bytes 152 u64 off_raw
+ *   160  u64 raw_bytes              168  u64 total_bytes  176 u8 sha256[32]
+ *   208  u8 code_len[256]           464  reserved[48]
+ *   chunk index: (n_chunks+1) x {u64 start_bit, u64 out_elem}, last = sentinel
+ *                {total_bits, n_elems}
+ *   windows:     n_chunks x 512 x u16: cnt | (gap << 11), cnt = codes that
+ *                start in the window, gap = offset of the first of them from
+ *                the window's first bit; 0 for a window with no code start
  *   stream:      ceil(total_bits/8) bytes rounded up to 16, plus 16 zero bytes
  *   raw:         n_elems bytes rounded up to 16
  *   flags: bit 0 set = sha256 holds the SHA-256 (FIPS 180-4) of the source
@@ -72,8 +70,7 @@
 #define CAP 24
 #define CHUNK 32768u
 #define WINDOWS 512
-#define VERSION 5
-#define WCODES 64u   /* codes per window */
+#define VERSION 4
 #define HDR 512u
 
 /* ------------------------------------------------------------------ */
@@ -315,18 +312,17 @@ static void sha256_words(const uint16_t *w, uint64_t n, uint8_t out[32]) {
 /* Encoder                                                             */
 /* ------------------------------------------------------------------ */
 typedef struct {
-    uint64_t n, n_chunks, total_bits, entry_bytes;
+    uint64_t n, n_chunks, total_bits;
     uint64_t off_ci, off_win, off_stream, stream_bytes, off_raw, raw_bytes, total;
 } layout_t;
 
-static void make_layout(uint64_t n, uint64_t total_bits, uint64_t entry_bytes, layout_t *L) {
+static void make_layout(uint64_t n, uint64_t total_bits, layout_t *L) {
     L->n = n;
     L->n_chunks = (n + CHUNK - 1) / CHUNK;
     L->total_bits = total_bits;
-    L->entry_bytes = entry_bytes;
     L->off_ci = HDR;
-    L->off_win = align256(L->off_ci + (L->n_chunks + 1) * 8);
-    L->off_stream = align256(L->off_win + L->n_chunks * WINDOWS * entry_bytes);
+    L->off_win = align256(L->off_ci + (L->n_chunks + 1) * 16);
+    L->off_stream = align256(L->off_win + L->n_chunks * WINDOWS * 2);
     L->stream_bytes = round16((total_bits + 7) / 8) + 16;
     L->off_raw = align256(L->off_stream + L->stream_bytes);
     L->raw_bytes = round16(n);
@@ -335,24 +331,14 @@ static void make_layout(uint64_t n, uint64_t total_bits, uint64_t entry_bytes, l
 
 uint64_t oracle_container_bound(uint64_t n) {
     layout_t L;
-    make_layout(n, n * CAP, 2, &L);
+    make_layout(n, n * CAP, &L);
     return L.total;
 }
 
-/* Elements of chunk c of a tensor of n elements, and its number of windows
- * (ceil(elements / 64)). */
-static uint64_t chunk_elems(uint64_t n, uint64_t c) {
-    return (c + 1) * CHUNK < n ? CHUNK : n - c * CHUNK;
-}
-static uint64_t chunk_windows(uint64_t n, uint64_t c) {
-    return (chunk_elems(n, c) + WCODES - 1) / WCODES;
-}
-
-/* Window entry k of chunk c. */
-static uint64_t get_entry(const uint8_t *c, const layout_t *L, uint64_t chunk, uint64_t k) {
-    const uint8_t *p = c + L->off_win + (chunk * WINDOWS + k) * L->entry_bytes;
-    return L->entry_bytes == 1 ? p[0] : get_u16(p);
-}
+/* First bit of window i (0 <= i <= 512) of a chunk of N bits, counted from
+ * the chunk's first bit: the windows split the N bits as evenly as integers
+ * allow (every window has floor(N/512) or ceil(N/512) bits). */
+static uint64_t window_edge(uint64_t N, uint64_t i) { return i * N / WINDOWS; }
 
 static void put_bit(uint8_t *stream, uint64_t pos, unsigned bit) {
     if (bit) stream[pos / 8] |= (uint8_t)(0x80u >> (pos % 8));
@@ -385,31 +371,9 @@ int oracle_encode_flags(const uint16_t *words, uint64_t n, int ndim, const uint6
     uint64_t total_bits = 0;
     for (int s = 0; s < 256; s++) total_bits += freq[s] * len[s];
 
-    /* 4. window lengths: the bits of every 64 consecutive codes of a chunk,
-     *    for each window but the chunk's last; their smallest value is the
-     *    base, and the entry width is one byte if every length is at most
-     *    255 above it */
-    uint64_t n_chunks = (n + CHUNK - 1) / CHUNK;
-    uint32_t *wbits = (uint32_t *)calloc(n_chunks ? n_chunks * WINDOWS : 1, sizeof(uint32_t));
-    if (!wbits) return ORACLE_E_ARG;
-    uint64_t lo = 0, hi = 0;
-    int any = 0;
-    for (uint64_t c = 0; c < n_chunks; c++) {
-        uint64_t nw = chunk_windows(n, c);
-        for (uint64_t k = 0; k + 1 < nw; k++) {
-            uint64_t bits = 0;
-            for (uint64_t i = 0; i < WCODES; i++) bits += len[exponent_of(words[c * CHUNK + k * WCODES + i])];
-            wbits[c * WINDOWS + k] = (uint32_t)bits;
-            if (!any || bits < lo) lo = bits;
-            if (!any || bits > hi) hi = bits;
-            any = 1;
-        }
-    }
-    uint64_t entry_bytes = hi - lo <= 255 ? 1 : 2;
-
     layout_t L;
-    make_layout(n, total_bits, entry_bytes, &L);
-    if (out_cap < L.total) { free(wbits); return ORACLE_E_ARG; }
+    make_layout(n, total_bits, &L);
+    if (out_cap < L.total) return ORACLE_E_ARG;
     memset(out, 0, L.total);
 
     /* header */
@@ -422,13 +386,11 @@ int oracle_encode_flags(const uint16_t *words, uint64_t n, int ndim, const uint6
     put_u32(out + 28, CHUNK);
     for (int i = 0; i < ndim; i++) put_u64(out + 32 + 8 * i, dims[i]);
     out[96] = CAP;
-    out[97] = (uint8_t)entry_bytes;
     put_u16(out + 98, WINDOWS);
     put_u32(out + 100, (uint32_t)L.n_chunks);
     put_u64(out + 104, total_bits);
     put_u64(out + 112, L.off_ci);
     put_u64(out + 120, L.off_win);
-    put_u32(out + 128, (uint32_t)lo);
     put_u64(out + 136, L.off_stream);
     put_u64(out + 144, L.stream_bytes);
     put_u64(out + 152, L.off_raw);
@@ -436,29 +398,45 @@ int oracle_encode_flags(const uint16_t *words, uint64_t n, int ndim, const uint6
     put_u64(out + 168, L.total);
     memcpy(out + 208, len, 256);
 
-    /* 5. bitstream, most significant bit of each code first, and the chunk
+    /* 4. bitstream, most significant bit of each code first, and the chunk
      *    index (start bit of every 32768th code) */
     uint8_t *stream = out + L.off_stream;
     uint64_t pos = 0;
     for (uint64_t j = 0; j < n; j++) {
-        if (j % CHUNK == 0) put_u64(out + L.off_ci + (j / CHUNK) * 8, pos);
+        if (j % CHUNK == 0) {
+            put_u64(out + L.off_ci + (j / CHUNK) * 16, pos);
+            put_u64(out + L.off_ci + (j / CHUNK) * 16 + 8, j);
+        }
         unsigned e = exponent_of(words[j]);
         for (int b = len[e] - 1; b >= 0; b--) put_bit(stream, pos++, (code[e] >> b) & 1u);
     }
-    put_u64(out + L.off_ci + L.n_chunks * 8, total_bits);
+    put_u64(out + L.off_ci + L.n_chunks * 16, total_bits);
+    put_u64(out + L.off_ci + L.n_chunks * 16 + 8, n);
 
-    /* 6. window entries */
-    for (uint64_t c = 0; c < n_chunks; c++) {
-        uint64_t nw = chunk_windows(n, c);
-        for (uint64_t k = 0; k + 1 < nw; k++) {
-            uint64_t e = wbits[c * WINDOWS + k] - lo;
-            uint8_t *q = out + L.off_win + (c * WINDOWS + k) * entry_bytes;
-            if (entry_bytes == 1) q[0] = (uint8_t)e; else put_u16(q, (uint16_t)e);
+    /* 5. window index: the chunk's bits cut into 512 windows (window_edge);
+     *    per window the number of code starts and the offset of the first
+     *    of them from the window's first bit */
+    for (uint64_t c = 0; c < L.n_chunks; c++) {
+        uint64_t b0 = get_u64(out + L.off_ci + c * 16);
+        uint64_t b1 = get_u64(out + L.off_ci + (c + 1) * 16);
+        unsigned cnt[WINDOWS], gap[WINDOWS];
+        memset(cnt, 0, sizeof(cnt));
+        memset(gap, 0, sizeof(gap));
+        uint64_t p = b0;
+        int win = 0;
+        uint64_t j_end = (c + 1) * CHUNK < n ? (c + 1) * CHUNK : n;
+        for (uint64_t j = c * CHUNK; j < j_end; j++) {
+            /* the window holding bit p: the last one that starts at or before it */
+            while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= p) win++;
+            if (cnt[win] == 0) gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)));
+            cnt[win]++;
+            p += len[exponent_of(words[j])];
         }
+        for (int i = 0; i < WINDOWS; i++)
+            put_u16(out + L.off_win + (c * WINDOWS + i) * 2, (uint16_t)(cnt[i] | (gap[i] << 11)));
     }
-    free(wbits);
 
-    /* 7. raw bytes: sign and fraction, as is */
+    /* 6. raw bytes: sign and fraction, as is */
     for (uint64_t j = 0; j < n; j++) out[L.off_raw + j] = (uint8_t)raw_of(words[j]);
 
     *out_bytes = L.total;
@@ -475,7 +453,6 @@ int oracle_encode(const uint16_t *words, uint64_t n, int ndim, const uint64_t *d
 /* ------------------------------------------------------------------ */
 typedef struct {
     layout_t L;
-    uint64_t base;             /* window_base */
     uint8_t len[256];
     /* canonical decode table, one bit at a time */
     uint32_t first[CAP + 1];   /* code value of the first symbol of each length */
@@ -489,14 +466,12 @@ static int parse(const uint8_t *c, uint64_t bytes, parsed_t *P) {
     if (memcmp(c, "DF11HIPC", 8) != 0 || get_u32(c + 8) != VERSION) return ORACLE_E_FORMAT;
     uint64_t n = get_u64(c + 16);
     uint64_t total_bits = get_u64(c + 104);
-    if (c[97] != 1 && c[97] != 2) return ORACLE_E_FORMAT;
-    make_layout(n, total_bits, c[97], &P->L);
+    make_layout(n, total_bits, &P->L);
     const layout_t *L = &P->L;
     if (get_u32(c + 28) != CHUNK || c[96] != CAP || get_u16(c + 98) != WINDOWS) return ORACLE_E_FORMAT;
     if (get_u32(c + 100) != L->n_chunks) return ORACLE_E_FORMAT;
-    P->base = get_u32(c + 128);
     if (get_u64(c + 112) != L->off_ci || get_u64(c + 120) != L->off_win ||
-        get_u32(c + 132) != 0 || get_u64(c + 136) != L->off_stream ||
+        get_u64(c + 128) != 0 || get_u64(c + 136) != L->off_stream ||
         get_u64(c + 144) != L->stream_bytes || get_u64(c + 152) != L->off_raw ||
         get_u64(c + 160) != L->raw_bytes || get_u64(c + 168) != L->total)
         return ORACLE_E_FORMAT;
@@ -554,14 +529,16 @@ int oracle_decode_chunk(const uint8_t *c, uint64_t bytes, uint64_t chunk, uint16
     if (st) return st;
     if (chunk >= P.L.n_chunks || !out) return ORACLE_E_ARG;
     const uint8_t *stream = c + P.L.off_stream;
-    uint64_t pos = get_u64(c + P.L.off_ci + chunk * 8);
-    uint64_t j0 = chunk * CHUNK, j1 = j0 + chunk_elems(P.L.n, chunk);
+    uint64_t pos = get_u64(c + P.L.off_ci + chunk * 16);
+    uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8);
+    uint64_t j1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16 + 8);
+    if (j0 > j1 || j1 > P.L.n) return ORACLE_E_FORMAT;
     for (uint64_t j = j0; j < j1; j++) {
         int e = read_code(&P, stream, &pos);
         if (e < 0) return -e;
         out[j - j0] = join((unsigned)e, c[P.L.off_raw + j]);
     }
-    return pos == get_u64(c + P.L.off_ci + (chunk + 1) * 8) ? ORACLE_OK : ORACLE_E_CORRUPT;
+    return pos == get_u64(c + P.L.off_ci + (chunk + 1) * 16) ? ORACLE_OK : ORACLE_E_CORRUPT;
 }
 
 int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int win,
@@ -572,24 +549,24 @@ int oracle_decode_window(const uint8_t *c, uint64_t bytes, uint64_t chunk, int w
     if (chunk >= P.L.n_chunks || win < 0 || win >= WINDOWS || !n_out || !end_bit)
         return ORACLE_E_ARG;
     const uint8_t *stream = c + P.L.off_stream;
-    uint64_t m = chunk_elems(P.L.n, chunk), nw = chunk_windows(P.L.n, chunk);
-    /* the window's first code: the chunk's start bit plus the lengths of the
-     * windows before it (base + entry each) */
-    uint64_t pos = get_u64(c + P.L.off_ci + chunk * 8);
-    for (int k = 0; k < win && (uint64_t)k + 1 < nw; k++) pos += P.base + get_entry(c, &P.L, chunk, (uint64_t)k);
-    if ((uint64_t)win >= nw) {
-        *n_out = 0;
-        *end_bit = get_u64(c + P.L.off_ci + (chunk + 1) * 8);
-        return ORACLE_OK;
-    }
-    uint64_t j0 = chunk * CHUNK + (uint64_t)win * WCODES;
-    uint64_t cnt = (uint64_t)win + 1 < nw ? WCODES : m - (uint64_t)win * WCODES;
-    for (uint64_t k = 0; k < cnt; k++) {
+    uint64_t b0 = get_u64(c + P.L.off_ci + chunk * 16);
+    uint64_t b1 = get_u64(c + P.L.off_ci + (chunk + 1) * 16);
+    uint64_t ws = b0 + window_edge(b1 - b0, (uint64_t)win);
+    const uint8_t *wins = c + P.L.off_win + chunk * WINDOWS * 2;
+    unsigned ent = get_u16(wins + 2 * win);
+    unsigned cnt = ent & 0x7FFu, gap = ent >> 11;
+    /* output position of this window's first code: codes of earlier windows */
+    uint64_t before = 0;
+    for (int i = 0; i < win; i++) before += get_u16(wins + 2 * i) & 0x7FFu;
+    uint64_t j0 = get_u64(c + P.L.off_ci + chunk * 16 + 8) + before;
+    *n_out = cnt;
+    if (cnt == 0) { *end_bit = ws; return gap == 0 ? ORACLE_OK : ORACLE_E_FORMAT; }
+    uint64_t pos = ws + gap;
+    for (unsigned k = 0; k < cnt; k++) {
         int e = read_code(&P, stream, &pos);
         if (e < 0) return -e;
         if (out) out[k] = join((unsigned)e, c[P.L.off_raw + j0 + k]);
     }
-    *n_out = cnt;
     *end_bit = pos;
     return ORACLE_OK;
 }
@@ -619,43 +596,42 @@ int oracle_check(const uint8_t *c, uint64_t bytes) {
     if (present == 1 && kraft != ((uint64_t)1 << (CAP - 1))) return ORACLE_E_FORMAT;
     if (present >= 2 && kraft != ((uint64_t)1 << CAP)) return ORACLE_E_FORMAT;
 
-    /* re-walk the stream: start bits, sentinel, window lengths */
+    /* re-walk the stream: start bits, sentinel, windows */
     const uint8_t *stream = c + L->off_stream;
-    uint64_t pos = 0, lo = 0, hi = 0;
-    int any = 0;
+    uint64_t pos = 0;
     for (uint64_t ch = 0; ch < L->n_chunks; ch++) {
-        if (get_u64(c + L->off_ci + ch * 8) != pos) return ORACLE_E_FORMAT;
-        uint64_t b1 = get_u64(c + L->off_ci + (ch + 1) * 8);
-        if (b1 < pos || b1 > L->total_bits) return ORACLE_E_FORMAT;
-        uint64_t m = chunk_elems(L->n, ch), nw = chunk_windows(L->n, ch);
-        uint64_t wstart = pos;
-        for (uint64_t i = 0; i < m; i++) {
+        const uint8_t *ent = c + L->off_ci + ch * 16;
+        if (get_u64(ent) != pos || get_u64(ent + 8) != ch * CHUNK) return ORACLE_E_FORMAT;
+        uint64_t b0 = pos;
+        uint64_t b1 = get_u64(ent + 16);
+        if (b1 < b0 || b1 > L->total_bits) return ORACLE_E_FORMAT;
+        unsigned cnt[WINDOWS], gap[WINDOWS];
+        memset(cnt, 0, sizeof(cnt));
+        memset(gap, 0, sizeof(gap));
+        int win = 0;
+        uint64_t j_end = (ch + 1) * CHUNK < L->n ? (ch + 1) * CHUNK : L->n;
+        for (uint64_t j = ch * CHUNK; j < j_end; j++) {
             if (pos >= b1) return ORACLE_E_FORMAT;
+            while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= pos) win++;
+            if (cnt[win] == 0) gap[win] = (unsigned)(pos - (b0 + window_edge(b1 - b0, win)));
+            cnt[win]++;
             int e = read_code(&P, stream, &pos);
             if (e < 0) return -e;
-            if ((i + 1) % WCODES == 0 && (i + 1) / WCODES < nw) {
-                /* window (i + 1) / 64 - 1 is complete and is not the last */
-                uint64_t k = (i + 1) / WCODES - 1, bits = pos - wstart;
-                if (bits < P.base || get_entry(c, L, ch, k) != bits - P.base) return ORACLE_E_FORMAT;
-                if (!any || bits < lo) lo = bits;
-                if (!any || bits > hi) hi = bits;
-                any = 1;
-                wstart = pos;
-            }
         }
         if (pos != b1) return ORACLE_E_FORMAT;
-        for (uint64_t k = nw ? nw - 1 : 0; k < WINDOWS; k++)
-            if (get_entry(c, L, ch, k) != 0) return ORACLE_E_FORMAT;
+        for (int i = 0; i < WINDOWS; i++)
+            if (get_u16(c + L->off_win + (ch * WINDOWS + i) * 2) != (cnt[i] | (gap[i] << 11)))
+                return ORACLE_E_FORMAT;
     }
     if (pos != L->total_bits) return ORACLE_E_FORMAT;
-    if (get_u64(c + L->off_ci + L->n_chunks * 8) != L->total_bits) return ORACLE_E_FORMAT;
-    /* the base is the smallest window length, the width the smallest that fits */
-    if (P.base != (any ? lo : 0) || L->entry_bytes != (hi - lo <= 255 ? 1u : 2u)) return ORACLE_E_FORMAT;
+    const uint8_t *sent = c + L->off_ci + L->n_chunks * 16;
+    if (get_u64(sent) != L->total_bits || get_u64(sent + 8) != L->n) return ORACLE_E_FORMAT;
 
     /* every byte the layout does not name is zero (a canonical container) */
     if (!(flags & ORACLE_FLAG_SHA256))
         for (uint64_t i = 176; i < 208; i++) if (c[i]) return ORACLE_E_FORMAT;
     for (uint64_t i = 464; i < HDR; i++) if (c[i]) return ORACLE_E_FORMAT;
+    if (c[97]) return ORACLE_E_FORMAT;
     for (uint32_t i = ndim; i < 8; i++) if (get_u64(c + 32 + 8 * i)) return ORACLE_E_FORMAT;
     for (uint64_t b = L->total_bits; b < L->stream_bytes * 8; b++)
         if (get_bit(stream, b)) return ORACLE_E_FORMAT;

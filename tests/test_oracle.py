@@ -246,20 +246,7 @@ SHA_FLUX_VEC15 = "2b2473e3773fe5e667f7ad4200ca4c1759ab147ce158cc046af508385c0501
 
 # ------------------------------------------------------------ the index --
 
-def _window_lengths_from_first_principles(w, code_len):
-    """Per chunk, the bit lengths of its windows of 64 consecutive codes, all
-    but the chunk's last, from the source's exponent bytes and the code
-    lengths alone (no stream, no index)."""
-    ln = np.asarray(code_len, np.int64)[(w >> 7) & 0xFF]
-    out = []
-    for lo in range(0, w.size, 32768):
-        seg = ln[lo:lo + 32768]
-        nw = (seg.size + 63) // 64
-        out.append(seg[:64 * (nw - 1)].reshape(-1, 64).sum(axis=1))
-    return out
-
-
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 127, 128, 129, 32767, 32768, 32769, 3 * 32768 + 1000])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 32767, 32768, 32769, 3 * 32768 + 1000])
 def test_chunk_and_window_index_reproduce_the_source(n):
     w = W.normal_bf16((n,), seed=n)
     c = oracle.encode(w)
@@ -267,64 +254,43 @@ def test_chunk_and_window_index_reproduce_the_source(n):
     h = oracle.header(c)
     n_chunks = h["n_chunks"]
     assert n_chunks == (n + 32767) // 32768
-    ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 8 * (n_chunks + 1)].view(np.uint64)
-    # chunk start bits from first principles: cumulative code lengths
-    ln = h["code_len"].astype(np.int64)[(w >> 7) & 0xFF]
-    starts = np.concatenate([[0], np.cumsum(ln)])
-    assert (ci == starts[np.minimum(np.arange(n_chunks + 1) * 32768, n)]).all()
-    # window entries from first principles: lengths of 64-code groups minus
-    # the tensor's smallest, one byte each here
-    wl = _window_lengths_from_first_principles(w, h["code_len"])
-    allw = np.concatenate(wl) if wl else np.zeros(0, np.int64)
-    base = int(allw.min()) if allw.size else 0
-    assert h["window_base"] == base and h["entry_bytes"] == 1
-    NW = oracle.WINDOWS
+    ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 16 * (n_chunks + 1)].view(np.uint64)
     for ch in range(n_chunks):
         lo, hi = ch * 32768, min(n, (ch + 1) * 32768)
-        ent = c[h["off_windows"] + NW * ch:h["off_windows"] + NW * (ch + 1)].astype(np.int64)
-        nw = (hi - lo + 63) // 64
-        assert (ent[:nw - 1] == wl[ch] - base).all() and (ent[nw - 1:] == 0).all()
         # a chunk decodes from its start bit alone (df11pack, sampled chunks)
         assert (oracle.decode_chunk(c, ch, hi - lo) == w[lo:hi]).all()
-        # every window decodes its 64 codes (fewer in the chunk's last one)
-        # from the prefix sum of the lengths before it, and ends where the
-        # next one starts
-        b0, b1 = int(ci[ch]), int(ci[ch + 1])
-        edges = b0 + np.concatenate([[0], np.cumsum(wl[ch])])
-        parts = []
+        # the windows decode exactly their codes, back to back
+        NW = oracle.WINDOWS
+        parts, ends = [], []
+        b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
+        # window i starts floor(i * N / 512) bits into the chunk's N bits
+        edges = b0 + (np.arange(NW + 1) * (b1 - b0)) // NW
         for win in range(NW):
             words, end = oracle.decode_window(c, ch, win)
             parts.append(words)
-            if win < nw - 1:
-                assert len(words) == 64 and end == edges[win + 1]
-            elif win == nw - 1:
-                assert len(words) == hi - lo - 64 * (nw - 1) and end == b1
-            else:
-                assert len(words) == 0
+            if len(words):
+                ends.append((win, end))
+                # the window's last code starts inside it and may run past it
+                assert edges[win + 1] <= end <= b1
+                assert end - edges[win + 1] < 24
         assert (np.concatenate(parts) == w[lo:hi]).all()
-
-
-def test_window_entries_take_two_bytes_when_lengths_spread():
-    """Words sorted by code length: one chunk's windows run from 64 bits
-    (1-bit codes) to several hundred, more than a byte above the smallest."""
-    rng = np.random.default_rng(5)
-    e = np.where(rng.random(3 * 32768) < 0.5, 127, rng.integers(60, 200, 3 * 32768))
-    e.sort()
-    w = ((e.astype(np.uint16) << 7) | rng.integers(0, 128, e.size).astype(np.uint16))
-    c = oracle.encode(w)
-    h = oracle.header(c)
-    assert oracle.check(c) == oracle.OK and h["entry_bytes"] == 2
-    wl = np.concatenate(_window_lengths_from_first_principles(w, h["code_len"]))
-    assert h["window_base"] == wl.min() and wl.max() - wl.min() > 255
-    NW = oracle.WINDOWS
-    ent = c[h["off_windows"]:h["off_windows"] + 2 * NW * h["n_chunks"]].view(np.uint16).astype(np.int64)
-    for ch in range(h["n_chunks"]):
-        assert (ent[NW * ch:NW * ch + 511] == wl[511 * ch:511 * (ch + 1)] - wl.min()).all()
-    assert (oracle.decode(c, w.size) == w).all()
-    for ch in range(3):
-        for win in (0, 255, 510, 511):
-            words, _ = oracle.decode_window(c, ch, win)
-            assert (words == w[ch * 32768 + 64 * win:ch * 32768 + 64 * win + 64]).all()
+        assert ends[-1][1] == b1
+        ent = c[h["off_windows"] + 2 * NW * ch:h["off_windows"] + 2 * NW * (ch + 1)].view(np.uint16)
+        cnt, gap = ent & 0x7FF, ent >> 11
+        assert (gap < 24).all() and (gap[cnt == 0] == 0).all()
+        # the index from first principles: every code's start bit from the
+        # source's exponents and the header's code lengths; a window's cnt is
+        # the number of starts inside it (low 11 bits of its entry), its gap
+        # the first one's offset (top 5 bits), both 0 for an empty window
+        ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
+        starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
+        edges = edges[:NW]
+        before = np.searchsorted(starts, edges, side="left")
+        want_cnt = np.diff(np.append(before, hi - lo))
+        assert (cnt == want_cnt).all()
+        idx = np.minimum(before, hi - lo - 1)
+        want_gap = np.where(want_cnt > 0, starts[idx] - edges, 0)
+        assert (gap == want_gap).all()
 
 
 def test_degenerate_tensors():
@@ -368,16 +334,10 @@ def test_corruption_is_detected():
     bad[0] ^= 1                                      # magic
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_windows"] + 5] ^= 0x08                # a window length
+    bad[h["off_windows"] + 2 * 5 + 1] ^= 0x08        # a window gap (bit 11 of the entry)
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
-    bad[h["off_windows"] + 511] = 1                  # the chunk's last window holds no entry
-    assert oracle.check(bad) == oracle.E_FORMAT
-    bad = c.copy()
-    bad[128] += 1                                    # the window base
-    assert oracle.check(bad) == oracle.E_FORMAT
-    bad = c.copy()
-    bad[97] = 2                                      # the entry width
+    bad[h["off_windows"] + 2 * 10] ^= 1              # a window count
     assert oracle.check(bad) == oracle.E_FORMAT
     bad = c.copy()
     bad[208 + 121] += 1                              # a code length: Kraft breaks

@@ -38,26 +38,22 @@ MUTATIONS = [
      "stream[pos / 8] |= (uint8_t)(0x01u << (pos % 8));", 0),
     ("both bit writer and reader least significant bit first",
      None, None, 0),
-    ("window length misses its last code",
-     "for (uint64_t i = 0; i < WCODES; i++) bits += len[exponent_of(words[c * CHUNK + k * WCODES + i])];",
-     "for (uint64_t i = 0; i + 1 < WCODES; i++) bits += len[exponent_of(words[c * CHUNK + k * WCODES + i])];", 0),
-    ("window base is the first window's length, not the smallest",
-     "if (!any || bits < lo) lo = bits;", "if (!any) lo = bits;", 0),
-    ("the chunk's last window gets an entry",
-     "        for (uint64_t k = 0; k + 1 < nw; k++) {\n            uint64_t e = wbits[c * WINDOWS + k] - lo;",
-     "        for (uint64_t k = 0; k < nw && k < WINDOWS - 1; k++) {\n            uint64_t e = wbits[c * WINDOWS + k] - lo;", 0),
-    ("window decoder starts one window late",
-     "for (int k = 0; k < win && (uint64_t)k + 1 < nw; k++)",
-     "for (int k = 0; k <= win && (uint64_t)k + 1 < nw; k++)", 0),
-    ("window decoder leaves out the base",
-     "pos += P.base + get_entry(c, &P.L, chunk, (uint64_t)k);",
-     "pos += get_entry(c, &P.L, chunk, (uint64_t)k);", 0),
-    ("windows of 63 codes in the decoder",
-     "uint64_t j0 = chunk * CHUNK + (uint64_t)win * WCODES;",
-     "uint64_t j0 = chunk * CHUNK + (uint64_t)win * (WCODES - 1);", 0),
+    ("window gap off by one",
+     "gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)));",
+     "gap[win] = (unsigned)(p - (b0 + window_edge(b1 - b0, win)) + 1);", 0),
+    ("window entry packs the gap one bit low",
+     "(uint16_t)(cnt[i] | (gap[i] << 11))", "(uint16_t)(cnt[i] | (gap[i] << 10))", 0),
+    ("window count misses a code that starts on the window's first bit",
+     "            cnt[win]++;",
+     "            cnt[win] += (p != b0 + window_edge(b1 - b0, win));", 0),
+    ("window edges round up",
+     "return i * N / WINDOWS;", "return (i * N + WINDOWS - 1) / WINDOWS;", 0),
+    ("window search stops one window early",
+     "while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) <= p) win++;",
+     "while (win + 1 < WINDOWS && b0 + window_edge(b1 - b0, win + 1) < p) win++;", 0),
     ("chunk start bit recorded after the first code",
-     "if (j % CHUNK == 0) put_u64(out + L.off_ci + (j / CHUNK) * 8, pos);",
-     "if (j % CHUNK == 0) put_u64(out + L.off_ci + (j / CHUNK) * 8, pos + 1);", 0),
+     "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos);",
+     "put_u64(out + L.off_ci + (j / CHUNK) * 16, pos + 1);", 0),
     ("decoder accepts one code too many per length",
      "v - P->first[k] < P->count[k]", "v - P->first[k] <= P->count[k]", 0),
     ("decoder joins the exponent one bit too high",
@@ -139,27 +135,21 @@ def _pins_pass() -> bool:
             parts = [oracle.decode_window(c, ch, win)[0] for win in range(oracle.WINDOWS)]
             if not (np.concatenate(parts) == w[lo:hi]).all():
                 return False
-            # the index from first principles: chunk start bits are the
-            # cumulative code lengths; window entries the lengths of
-            # 64-code groups (all but the chunk's last) minus the smallest
+            # the index from first principles: code starts from the source
+            # and the header's code lengths, windows at floor(i * N / 512)
             h = oracle.header(c)
-            ln = h["code_len"].astype(np.int64)[(w >> 7) & 0xFF]
-            cum = np.concatenate([[0], np.cumsum(ln)])
-            ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 8 * (h["n_chunks"] + 1)].view(np.uint64)
-            if not (ci == cum[np.minimum(np.arange(h["n_chunks"] + 1) * 32768, w.size)]).all():
-                return False
-            groups = []
-            for c0 in range(0, w.size, 32768):
-                seg = ln[c0:c0 + 32768]
-                nw = (seg.size + 63) // 64
-                groups.append(seg[:64 * (nw - 1)].reshape(-1, 64).sum(axis=1))
-            base = int(np.concatenate(groups).min())
-            if h["window_base"] != base or h["entry_bytes"] != 1:
-                return False
+            ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 16 * (h["n_chunks"] + 1)].view(np.uint64)
+            b0, b1 = int(ci[2 * ch]), int(ci[2 * ch + 2])
+            ln = h["code_len"].astype(np.int64)[(w[lo:hi] >> 7) & 0xFF]
+            starts = b0 + np.concatenate([[0], np.cumsum(ln)[:-1]])
             NW = oracle.WINDOWS
-            ent = c[h["off_windows"] + NW * ch:h["off_windows"] + NW * (ch + 1)].astype(np.int64)
-            g = groups[ch]
-            if not ((ent[:g.size] == g - base).all() and (ent[g.size:] == 0).all()):
+            edges = b0 + (np.arange(NW) * (b1 - b0)) // NW
+            before = np.searchsorted(starts, edges, side="left")
+            want_cnt = np.diff(np.append(before, hi - lo))
+            ent = c[h["off_windows"] + 2 * NW * ch:h["off_windows"] + 2 * NW * (ch + 1)].view(np.uint16)
+            cnt, gap = ent & 0x7FF, ent >> 11
+            want_gap = np.where(want_cnt > 0, starts[np.minimum(before, hi - lo - 1)] - edges, 0)
+            if not ((cnt == want_cnt).all() and (gap == want_gap).all()):
                 return False
         return True
     except Exception:
