@@ -223,6 +223,38 @@ def test_corrupted_stream_sets_the_flag():
     assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
+@pytest.mark.parametrize("window", [1, 200, 300, 511])
+def test_wrong_window_gap_sets_the_flag(window):
+    """The gap of one window of chunk 1 raised by one bit in the device copy:
+    the window before it decodes exactly and ends where that window's first
+    code really starts, one bit before the index says, so df11_check must
+    report DF11_E_CORRUPT; the kernel writes only inside the output (guard
+    words stay) and the other chunks decode exactly."""
+    torch = _torch()
+    log(f"wrong window gap, window {window}")
+    w = W.normal_bf16((3 * 32768 + 77,), seed=9)
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    plan = df11.Plan([c])
+    bad = c.copy()
+    off = h["off_windows"] + 2 * (512 + window)
+    ent = int(bad[off:off + 2].view(np.uint16)[0])
+    assert ent & 0x7FF and (ent >> 11) < 24
+    bad[off:off + 2] = np.array([ent + (1 << 11)], np.uint16).view(np.uint8)
+    buf, o = empty_words(w.size, guard=64)
+    df11.decode(plan, 0, to_device_u8(bad), o)
+    with pytest.raises(df11.DF11Error) as e:
+        df11.check(plan)
+    assert e.value.status == 5
+    host = buf.cpu().numpy().view(np.uint16)
+    assert (host[:64] == 0x5A5A).all() and (host[64 + w.size:] == 0x5A5A).all()
+    assert (host[64:64 + 32768] == w[:32768]).all()
+    assert (host[64 + 65536:64 + w.size] == w[65536:]).all()
+    df11.decode(plan, 0, to_device_u8(c), o)
+    df11.check(plan)
+    assert (o.cpu().numpy().view(np.uint16) == w).all()
+
+
 @pytest.mark.parametrize("r,n", [(0.0603, 32768 * 64), (0.09, 32768 * 16 + 32000)])
 def test_chunks_ending_near_the_source_end(r, n):
     """Six exponents at probability q and four at r (3- and 4-bit codes, 3 +
