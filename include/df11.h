@@ -216,8 +216,15 @@ df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info)
  * whole container (16-byte aligned, at least container_bytes long, same
  * bytes as the prefix given to df11_plan).  d_out: DEVICE pointer to
  * n_elems * 2 bytes (16-byte aligned), not overlapping the container.
- * Enqueues on `stream` and returns; never allocates and never synchronizes
- * (safe under stream capture).  The chunk start bits come from the plan;
+ * Enqueues on `stream` and returns; never allocates and never waits on a
+ * stream.  Launches of one plan may run at the same time on any streams:
+ * each takes one of the plan's 256 ticket counters that no unfinished launch
+ * holds (a launch's last workgroup reports it finished through host memory);
+ * when all 256 are held, the call waits on the host for one to come free (at
+ * most 60 s, then DF11_E_HIP).  A launch made while `stream` is being
+ * captured keeps its counter for good, so that the graph may be replayed any
+ * number of times, one replay at a time; a plan gives at most 128 captured
+ * launches a counter (then DF11_E_UNSUPPORTED).  The chunk start bits come from the plan;
  * the window index, the stream and the raw bytes from d_container.  Memory
  * safety does not depend on the device bytes: a container that differs from
  * the planned one gives wrong words and sets the plan's corruption flag (see

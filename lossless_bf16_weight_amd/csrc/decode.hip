@@ -776,10 +776,12 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     }
     if (__ballot(bad_any) && lane == 0) atomicOr(a.status, 1u);
     // The last workgroup to finish (every ticket of the launch has been
-    // taken by then) clears the counter for the slot's next launch.
+    // taken by then) clears the counter for the slot's next launch, then
+    // tells the host the slot is free.
     if (tid == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
         atomicExch(a.work, 0u);
         atomicExch(a.work + 1, 0u);
+        __hip_atomic_store(a.fin, a.launch_id, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 

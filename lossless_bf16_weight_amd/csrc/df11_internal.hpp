@@ -107,17 +107,57 @@ constexpr uint32_t kStagedBit = 0x80000000u;
 // Work tickets.  A launch's workgroups take its chunks in order from a
 // ticket counter: work[0] = tickets handed out past the first gridDim.x,
 // work[1] = workgroups finished; the last workgroup to finish puts both back
-// to zero.  A plan holds kWorkSlots counters, 64 bytes apart, and gives them
-// to its launches in turn, so launches of one plan overlap safely while
-// fewer than kWorkSlots launches of it are issued in between.
-constexpr uint32_t kWorkSlots = 64;
+// to zero and then writes the launch's id to the slot's completion word in
+// host memory.  A plan holds kWorkSlots counters, 64 bytes apart; the host
+// gives a launch only a slot whose previous launch has written its id (so no
+// two running launches share a counter), and keeps for good the slot of a
+// launch made while its stream is being captured (every replay of the graph
+// uses it).
+constexpr uint32_t kWorkSlots = 256;
 constexpr uint32_t kWorkStride = 16;   // uint32 per counter slot
+// Slots a plan lets captured launches hold.
+constexpr uint32_t kGraphSlotsMax = kWorkSlots / 2;
+
+// The host side of the slots.  issued[s]: id of the last launch given slot s
+// (0: none yet); graph[s]: held by a captured launch.  fin[s] (host memory
+// the device writes): id of the last launch on slot s that finished.
+struct SlotTable {
+    uint32_t seq = 0, next = 0, n_graph = 0;
+    uint32_t issued[kWorkSlots] = {};
+    bool graph[kWorkSlots] = {};
+    // A free slot and the new launch's id (*id), or -1 when every slot is
+    // held by a running launch or a captured one.
+    int acquire(const uint32_t *fin, bool capture, uint32_t *id) {
+        if (capture && n_graph >= kGraphSlotsMax) return -1;
+        for (uint32_t i = 0; i < kWorkSlots; ++i) {
+            const uint32_t s = (next + i) % kWorkSlots;
+            if (graph[s]) continue;
+            if (issued[s] != 0 && __atomic_load_n(&fin[s], __ATOMIC_ACQUIRE) != issued[s]) continue;
+            if (++seq == 0) ++seq;
+            issued[s] = seq;
+            graph[s] = capture;
+            n_graph += capture;
+            next = s + 1;
+            *id = seq;
+            return (int)s;
+        }
+        return -1;
+    }
+    // A slot whose launch was never enqueued (the launch call failed).
+    void release(int s) {
+        if (graph[s]) --n_graph;
+        graph[s] = false;
+        issued[s] = 0;
+    }
+};
 
 struct DecodeArgs {
     const ChunkRec *recs;        // the launch's chunks, in order
     const LutRecord *luts;       // plan's table records (indexed by plan tensor)
     uint32_t *status;            // plan's corruption flag
     uint32_t *work;              // this launch's ticket counter slot
+    uint32_t *fin;               // the slot's completion word (host memory)
+    uint32_t launch_id;          // written to *fin when the launch is done
     uint32_t n_items;
     uint32_t tensor_base;        // plan index of the launch's tensor 0
     const uint8_t *containers[DF11_MAX_BATCH];

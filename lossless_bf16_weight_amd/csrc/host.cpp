@@ -11,6 +11,9 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
+#include <mutex>
+#include <thread>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -343,7 +346,10 @@ struct df11_plan_s {
     LutRecord *d_luts = nullptr;
     uint32_t *d_status = nullptr;
     uint32_t *d_work = nullptr;              // kWorkSlots ticket counters
-    std::atomic<uint32_t> launches{0};       // picks each launch's counter slot
+    uint32_t *h_fin = nullptr;               // kWorkSlots completion words (pinned host memory)
+    uint32_t *d_fin = nullptr;               // the same words, as the device addresses them
+    std::mutex slot_mu;
+    SlotTable slots;
 };
 
 namespace {
@@ -361,9 +367,39 @@ struct DeviceGuard {
     }
 };
 
-uint32_t *next_work_slot(df11_plan_s *p) {
-    const uint32_t k = p->launches.fetch_add(1, std::memory_order_relaxed) % kWorkSlots;
-    return p->d_work + kWorkStride * k;
+// A ticket counter no running launch of the plan holds, for a launch on
+// `stream` (fills a.work, a.fin, a.launch_id).  Waits on the host while every
+// slot is held (kWorkSlots launches of the plan queued and not finished),
+// for at most a minute.
+df11_status take_work_slot(df11_plan_s *p, hipStream_t stream, DecodeArgs &a, int &slot) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) cs = hipStreamCaptureStatusNone;
+    const bool capture = cs != hipStreamCaptureStatusNone;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (;;) {
+        {
+            std::lock_guard<std::mutex> lock(p->slot_mu);
+            uint32_t id = 0;
+            slot = p->slots.acquire(p->h_fin, capture, &id);
+            if (slot >= 0) {
+                a.work = p->d_work + kWorkStride * (uint32_t)slot;
+                a.fin = p->d_fin + slot;
+                a.launch_id = id;
+                return DF11_OK;
+            }
+            if (capture && p->slots.n_graph >= kGraphSlotsMax)
+                return fail(DF11_E_UNSUPPORTED, "%u captured decodes already hold counters of this plan", kGraphSlotsMax);
+        }
+        if (std::chrono::steady_clock::now() - t0 > std::chrono::seconds(60))
+            return fail(DF11_E_HIP, "no ticket counter came free in 60 s: %u decodes of this plan queued and unfinished",
+                        kWorkSlots);
+        std::this_thread::sleep_for(std::chrono::microseconds(20));
+    }
+}
+
+void give_back_slot(df11_plan_s *p, int slot) {
+    std::lock_guard<std::mutex> lock(p->slot_mu);
+    p->slots.release(slot);
 }
 
 int grid_for(const df11_plan_s *p, uint64_t items) {
@@ -455,16 +491,26 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
     p->d_luts = (LutRecord *)(base + off_luts);
     p->d_status = (uint32_t *)(base + off_status);
     p->d_work = (uint32_t *)(base + off_work);
+    // the slots' completion words: coherent pinned host memory the decode
+    // kernel writes at the end of each launch
+    e = hipHostMalloc((void **)&p->h_fin, sizeof(uint32_t) * kWorkSlots, hipHostMallocCoherent | hipHostMallocMapped);
+    if (e == hipSuccess) {
+        memset(p->h_fin, 0, sizeof(uint32_t) * kWorkSlots);
+        e = hipHostGetDevicePointer((void **)&p->d_fin, p->h_fin, 0);
+    }
+    if (e != hipSuccess) {
+        df11_plan_destroy(p);
+        return fail(DF11_E_HIP, "completion words: %s", hipGetErrorString(e));
+    }
     *out = p;
     return DF11_OK;
 }
 
 extern "C" void df11_plan_destroy(df11_plan_t p) {
     if (!p) return;
-    if (p->d_block) {
-        DeviceGuard guard(p->device);
-        (void)hipFree(p->d_block);
-    }
+    DeviceGuard guard(p->device);
+    if (p->d_block) (void)hipFree(p->d_block);
+    if (p->h_fin) (void)hipHostFree(p->h_fin);
     delete p;
 }
 
@@ -497,14 +543,20 @@ extern "C" df11_status df11_decode(df11_plan_t p, int tensor, const void *d_cont
     a.recs = p->d_recs + p->first_rec[tensor];
     a.luts = p->d_luts;
     a.status = p->d_status;
-    a.work = next_work_slot(p);
     a.n_items = n_chunks;
     a.tensor_base = (uint32_t)tensor;
     a.containers[0] = (const uint8_t *)d_container;
     a.outs[0] = (uint16_t *)d_out;
     DeviceGuard guard(p->device);
     if (guard.err != hipSuccess) return fail(DF11_E_HIP, "hipSetDevice: %s", hipGetErrorString(guard.err));
-    HIP_TRY(launch_decode(a, grid_for(p, n_chunks), stream));
+    int slot = -1;
+    st = take_work_slot(p, stream, a, slot);
+    if (st) return st;
+    const hipError_t e = launch_decode(a, grid_for(p, n_chunks), stream);
+    if (e != hipSuccess) {
+        give_back_slot(p, slot);
+        return fail(DF11_E_HIP, "decode launch: %s", hipGetErrorString(e));
+    }
     return DF11_OK;
 }
 
@@ -526,14 +578,20 @@ extern "C" df11_status df11_decode_batch(df11_plan_t p, const void *const *d_con
         a.recs = p->d_recs + r0;
         a.luts = p->d_luts;
         a.status = p->d_status;
-        a.work = next_work_slot(p);
         a.n_items = (uint32_t)(r1 - r0);
         a.tensor_base = (uint32_t)(g * DF11_MAX_BATCH);
         for (int t = (int)g * DF11_MAX_BATCH; t < t_end; ++t) {
             a.containers[t - g * DF11_MAX_BATCH] = (const uint8_t *)d_containers[t];
             a.outs[t - g * DF11_MAX_BATCH] = (uint16_t *)d_outs[t];
         }
-        HIP_TRY(launch_decode(a, grid_for(p, a.n_items), stream));
+        int slot = -1;
+        df11_status st = take_work_slot(p, stream, a, slot);
+        if (st) return st;
+        const hipError_t e = launch_decode(a, grid_for(p, a.n_items), stream);
+        if (e != hipSuccess) {
+            give_back_slot(p, slot);
+            return fail(DF11_E_HIP, "decode launch: %s", hipGetErrorString(e));
+        }
     }
     return DF11_OK;
 }

@@ -133,7 +133,7 @@ def verify_containers(containers: Sequence[np.ndarray], sources: Optional[Sequen
         bad = 0
         for t, c in pick:
             lo, hi = c * 32768, min((c + 1) * 32768, infos[t]["n_elems"])
-            want = torch.from_numpy(np.ascontiguousarray(sources[t][lo:hi]).view(np.int16)).to(dev)
+            want = torch.from_numpy(np.array(sources[t][lo:hi], dtype=np.uint16).view(np.int16)).to(dev)
             if not torch.equal(outs[t][lo:hi], want):
                 bad += 1
                 if bad <= 5:

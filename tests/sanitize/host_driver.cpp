@@ -91,6 +91,56 @@ static int check_words(const char *path) {
     return 0;
 }
 
+// The host side of the decode's ticket-counter slots (SlotTable): no slot is
+// given out while the device has not reported its previous launch finished,
+// captured launches keep theirs, a failed launch gives its slot back.
+static int check_slots() {
+    using df11::kWorkSlots;
+    df11::SlotTable T;
+    uint32_t fin[kWorkSlots] = {};
+    uint32_t id = 0, ids[kWorkSlots];
+    bool seen[kWorkSlots] = {};
+    for (uint32_t i = 0; i < kWorkSlots; ++i) {
+        const int s = T.acquire(fin, false, &id);
+        if (s < 0 || seen[s] || id == 0) return 10;
+        seen[s] = true;
+        ids[s] = id;
+    }
+    if (T.acquire(fin, false, &id) >= 0) return 11;          // all held
+    fin[7] = ids[7];                                          // slot 7's launch finished
+    if (T.acquire(fin, false, &id) != 7 || id == ids[7]) return 12;
+    ids[7] = id;
+    if (T.acquire(fin, false, &id) >= 0) return 13;
+    fin[9] = ids[9] - 1;                                      // an older id: still running
+    if (T.acquire(fin, false, &id) >= 0) return 14;
+    fin[9] = ids[9];
+    if (T.acquire(fin, true, &id) != 9) return 15;           // captured: kept for good
+    fin[9] = id;
+    if (T.acquire(fin, false, &id) >= 0) return 16;
+    // once every launch has finished, every slot but the captured one comes
+    // back, each once before any comes back twice
+    for (uint32_t s = 0; s < kWorkSlots; ++s) fin[s] = T.issued[s];
+    bool back[kWorkSlots] = {};
+    for (uint32_t i = 0; i + 1 < kWorkSlots; ++i) {
+        const int s = T.acquire(fin, false, &id);
+        if (s < 0 || s == 9 || back[s]) return 18;
+        back[s] = true;
+    }
+    if (T.acquire(fin, false, &id) >= 0) return 17;          // all held again
+    // a launch call that failed gives its slot back at once
+    for (uint32_t s = 0; s < kWorkSlots; ++s) fin[s] = 0;
+    df11::SlotTable U;
+    const int a = U.acquire(fin, false, &id);
+    U.release(a);
+    if (U.acquire(fin, false, &id) < 0) return 19;
+    // captured launches: at most half of the slots
+    df11::SlotTable V;
+    int n_cap = 0;
+    while (V.acquire(fin, true, &id) >= 0) ++n_cap;
+    if (n_cap != (int)df11::kGraphSlotsMax || V.acquire(fin, false, &id) < 0) return 20;
+    return 0;
+}
+
 int main(int argc, char **argv) {
     if (argc != 2) {
         fprintf(stderr, "usage: %s MANIFEST\n", argv[0]);
@@ -116,6 +166,12 @@ int main(int argc, char **argv) {
                 (void)df11_nf12_validate(p, n, &ne);
             });
             ++n_nf12;
+        } else if (!strcmp(kind, "slots")) {
+            const int r = check_slots();
+            if (r) {
+                fprintf(stderr, "slot table check %d failed\n", r);
+                return 3;
+            }
         } else if (!strcmp(kind, "words")) {
             const int r = check_words(path);
             if (r) {

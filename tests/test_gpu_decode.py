@@ -166,8 +166,7 @@ def test_non_default_stream_and_repeats():
 def test_ticket_counters_across_many_launches_and_streams():
     """Every launch takes its chunks from one of the plan's ticket counters,
     which its last workgroup clears.  160 launches (single and batched, on
-    two streams that may run side by side) go round every counter slot more
-    than twice; every output must be exact."""
+    two streams that may run side by side); every output must be exact."""
     torch = _torch()
     log("ticket counters: 160 launches on two streams")
     sizes = [3 * 32768 + 5, 900001, 40000]
@@ -193,6 +192,44 @@ def test_ticket_counters_across_many_launches_and_streams():
     for o in outs:
         for w, t in zip(ws, o):
             assert (t.cpu().numpy().view(np.uint16) == w).all()
+
+
+def test_more_queued_launches_than_ticket_counters():
+    """A launch gets a ticket counter only once the last launch on it has
+    finished (its last workgroup reports to the host).  300 decodes of one
+    plan are queued on a stream held back behind a long copy on another
+    stream (more than the plan's 256 counters, so the host waits for
+    counters to come free), with 200 more on two free streams meanwhile; the
+    held-back launches then run beside later ones.  Every output is exact and
+    the flag stays clear."""
+    torch = _torch()
+    log("300 held-back launches and 200 free ones")
+    n = 1600 * 32768 + 999          # more chunks than workgroups: tickets are taken
+    w = W.normal_bf16((n,), seed=77)
+    c = oracle_encode_many([w])[0]
+    plan = df11.Plan([c])
+    dc = to_device_u8(c)
+    held, s1, s2, cp = (torch.cuda.Stream() for _ in range(4))
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big2 = torch.empty_like(big)
+    outs = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cp):
+        for _ in range(6):
+            big2.copy_(big)
+        ev = torch.cuda.Event()
+        ev.record(cp)
+    held.wait_event(ev)
+    for i in range(300):
+        df11.decode(plan, 0, dc, outs[0], stream=held)
+    for i in range(100):
+        df11.decode(plan, 0, dc, outs[1], stream=s1)
+        df11.decode(plan, 0, dc, outs[2], stream=s2)
+    for st in (held, s1, s2):
+        df11.check(plan, stream=st)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
 def test_corrupted_stream_sets_the_flag():

@@ -8,7 +8,10 @@ containers and word files, and a few thousand containers broken on purpose
 (header fields, code lengths, chunk and window index entries, random byte
 flips, truncations).  Every validation must return a status without a
 sanitizer report, every word file must round-trip, and the sanitized encoder
-must write the bytes the normal build writes."""
+must write the bytes the normal build writes.  The host side of the
+decode's ticket-counter slots is checked in the same driver: a slot is not
+given out again before the device reports its launch finished, and a
+captured launch keeps its slot."""
 import os
 import shutil
 import subprocess
@@ -139,7 +142,7 @@ def _run(exe, manifest):
 def test_host_code_and_oracle_under_sanitizers(drivers, tmp_path):
     host, orc = drivers
     rng = np.random.default_rng(2024)
-    lines = []
+    lines = ["slots -"]
     words = _word_sets()
     for name, w in words.items():
         p = tmp_path / f"{name}.u16"
