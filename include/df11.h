@@ -166,6 +166,26 @@ df11_status df11_encode_device_batch(int n_tensors, const void *const *d_words, 
                                      const uint64_t *out_caps, uint64_t *out_bytes, int hip_device,
                                      hipStream_t stream);
 
+/* df11_encode_device_batch for callers that cannot allocate memory (tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, the
+ * same kernels and the same bytes, but no device or host memory is allocated
+ * and nothing is freed.  The histograms live in a fixed 128 KiB array of
+ * device memory that each GPU the library runs on holds until the process
+ * ends; its address on a device is looked up on the first call there.
+ * At most 64 tensors per call (more: DF11_E_UNSUPPORTED, nothing enqueued);
+ * hip_device below 64.  Every call on a GPU shares that GPU's array, which
+ * keeps the last call's counts and is cleared at the start of each call:
+ * the library holds a process-wide lock from that clearing until the codes
+ * are built, so calls from several host threads take their turns instead of
+ * racing on it (calls from different processes each have their own array).
+ * Like df11_encode_device_batch it waits for the stream once, so it cannot
+ * be captured into a graph.  The caller still allocates the outputs. */
+df11_status df11_encode_device_batch_noalloc(int n_tensors, const void *const *d_words,
+                                             const uint64_t *n_elems, const int *ndims,
+                                             const uint64_t *dims, void *const *d_outs,
+                                             const uint64_t *out_caps, uint64_t *out_bytes,
+                                             int hip_device, hipStream_t stream);
+
 /* SHA-256 (FIPS 180-4) of `bytes` bytes of HOST memory into digest[32]. */
 void df11_sha256(const void *host_data, uint64_t bytes, uint8_t *digest);
 

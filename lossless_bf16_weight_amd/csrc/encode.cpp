@@ -50,8 +50,15 @@ inline void wr16(uint8_t *p, uint16_t v) { memcpy(p, &v, 2); }
 inline void wr32(uint8_t *p, uint32_t v) { memcpy(p, &v, 4); }
 inline void wr64(uint8_t *p, uint64_t v) { memcpy(p, &v, 8); }
 
-// Package-merge over a node pool: a node is a leaf (symbol) or a package of
-// two nodes of the level below.  Each level's list is kept sorted by weight.
+// Package-merge by levels.  Level 0's list is the leaves (symbols) by
+// weight; level d's list merges the leaves with the packages of level d-1
+// (package i pairs items 2i and 2i+1 of that list), a leaf before a package
+// of equal weight.  The lengths follow by counting, so each level keeps only
+// which of its items are packages: the 2n-2 lightest items of the top level
+// are selected, a selected prefix of level d holding p packages selects the
+// first 2p items of level d-1, and a symbol's length is the number of levels
+// whose selected prefix holds its leaf (the selected leaves of a level are
+// always the lightest ones).  Fixed-size arrays only: nothing is allocated.
 void package_merge(const uint64_t *freq, int cap, uint8_t *len) {
     memset(len, 0, 256);
     int sym[256], n = 0;
@@ -59,50 +66,46 @@ void package_merge(const uint64_t *freq, int cap, uint8_t *len) {
         if (freq[s]) sym[n++] = s;
     if (n == 0) return;
     if (n == 1) { len[sym[0]] = 1; return; }
-    std::stable_sort(sym, sym + n, [&](int a, int b) { return freq[a] < freq[b]; });
+    // by (frequency, symbol): a total order, so the result is the stable sort
+    std::sort(sym, sym + n, [&](int a, int b) { return freq[a] < freq[b] || (freq[a] == freq[b] && a < b); });
 
-    struct Node { uint64_t w; int sym; int a, b; };
-    std::vector<Node> pool;
-    pool.reserve((size_t)cap * 2 * n + n);
-    std::vector<int> leaves(n), level;
+    // a level's list has at most n + (2n - 2) / 2 < 512 items
+    static_assert(kMaxLen <= 32, "levels");
+    uint64_t wbuf[2][512];
+    uint8_t is_pkg[kMaxLen][512];
+    int count[kMaxLen];
+    uint64_t *below = wbuf[0], *cur = wbuf[1];
     for (int i = 0; i < n; ++i) {
-        leaves[i] = (int)pool.size();
-        pool.push_back({freq[sym[i]], sym[i], -1, -1});
+        below[i] = freq[sym[i]];
+        is_pkg[0][i] = 0;
     }
-    level = leaves;
+    count[0] = n;
     for (int d = 1; d < cap; ++d) {
-        std::vector<int> next;
-        next.reserve(2 * n);
-        size_t il = 0, ip = 0, np = level.size() / 2;
-        while (il < leaves.size() || ip < np) {
-            bool take_leaf;
-            if (ip >= np) take_leaf = true;
-            else if (il >= leaves.size()) take_leaf = false;
-            else take_leaf = pool[leaves[il]].w <= pool[level[2 * ip]].w + pool[level[2 * ip + 1]].w;
+        int il = 0, ip = 0, k = 0;
+        const int np = count[d - 1] / 2;
+        while (il < n || ip < np) {
+            const uint64_t pw = ip < np ? below[2 * ip] + below[2 * ip + 1] : 0;
+            const bool take_leaf = ip >= np || (il < n && freq[sym[il]] <= pw);
             if (take_leaf) {
-                next.push_back(leaves[il++]);
+                cur[k] = freq[sym[il++]];
+                is_pkg[d][k] = 0;
             } else {
-                const int a = level[2 * ip], b = level[2 * ip + 1];
-                next.push_back((int)pool.size());
-                pool.push_back({pool[a].w + pool[b].w, -1, a, b});
+                cur[k] = pw;
+                is_pkg[d][k] = 1;
                 ++ip;
             }
+            ++k;
         }
-        level.swap(next);
+        count[d] = k;
+        std::swap(below, cur);
     }
-    // each leaf occurrence under the 2n-2 lightest top-level nodes adds one bit
-    unsigned depth[256] = {};
-    std::vector<int> stack;
-    for (int i = 0; i < 2 * n - 2; ++i) {
-        stack.push_back(level[i]);
-        while (!stack.empty()) {
-            const Node &x = pool[stack.back()];
-            stack.pop_back();
-            if (x.sym >= 0) depth[x.sym]++;
-            else { stack.push_back(x.a); stack.push_back(x.b); }
-        }
+    int m = 2 * n - 2;
+    for (int d = cap - 1; d >= 0; --d) {
+        int leaves = 0, pkgs = 0;
+        for (int i = 0; i < m; ++i) is_pkg[d][i] ? ++pkgs : ++leaves;
+        for (int i = 0; i < leaves; ++i) len[sym[i]]++;
+        m = 2 * pkgs;
     }
-    for (int s = 0; s < 256; ++s) len[s] = (uint8_t)depth[s];
 }
 
 void canonical_codes(const uint8_t *len, uint32_t *code) {

@@ -25,11 +25,20 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "df11_internal.hpp"
 
 namespace df11 {
+
+// Histogram counters for the encoder entry point that allocates nothing:
+// 256 per tensor, for at most kNoAllocTensors tensors per call (128 KiB).
+// Each device holds its own copy until the process ends; host code reaches
+// it only through the address hipGetSymbolAddress gives for that device
+// (scratch_on below), never through this name.
+constexpr int kNoAllocTensors = 64;
+static __device__ __align__(256) unsigned long long scratch[kNoAllocTensors * 256];
 
 namespace {
 
@@ -320,55 +329,85 @@ __global__ __launch_bounds__(kHeader / 4) void enc_header(Header h, GLOBAL uint3
     out[threadIdx.x] = h.w[threadIdx.x];
 }
 
-}  // namespace
+// Zeroes n counters (the histograms, before they are counted).
+__global__ __launch_bounds__(kEncThreads) void enc_clear(GLOBAL unsigned long long *p, uint64_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * kEncThreads + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
 
-}  // namespace df11
+constexpr int kMaxDevices = 64;
+// Guards scratch_ptr, the host copy of the counts and every use of a
+// device's scratch: calls of the no-alloc entry point take turns.
+std::mutex g_scratch_mu;
+unsigned long long *g_scratch_ptr[kMaxDevices];
+uint64_t g_freq[kNoAllocTensors * 256];
 
-using namespace df11;
+// This device's scratch (hipGetSymbolAddress once per device, with the
+// device current; called with g_scratch_mu held).
+hipError_t scratch_on(int device, unsigned long long **ptr) {
+    if (!g_scratch_ptr[device]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = static_cast<unsigned long long *>(p);
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
 
-extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
-                                                const int *ndims, const uint64_t *dims, void *const *d_outs,
-                                                const uint64_t *out_caps, uint64_t *out_bytes, int hip_device,
-                                                hipStream_t stream) {
+df11_status check_batch(const char *who, int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                        const int *ndims, const uint64_t *dims, void *const *d_outs, const uint64_t *out_caps,
+                        uint64_t *out_bytes) {
     if (n_tensors < 0 || (n_tensors && (!d_words || !n_elems || !ndims || !dims || !d_outs || !out_caps || !out_bytes)))
-        return report_error(DF11_E_ARG, "df11_encode_device_batch: bad argument");
+        return report_error(DF11_E_ARG, "%s: bad argument", who);
     for (int t = 0; t < n_tensors; ++t) {
         const uint64_t n = n_elems[t];
         const int ndim = ndims[t];
         if ((!d_words[t] && n) || !d_outs[t] || ndim < 0 || ndim > 8)
-            return report_error(DF11_E_ARG, "df11_encode_device_batch: tensor %d: bad argument", t);
+            return report_error(DF11_E_ARG, "%s: tensor %d: bad argument", who, t);
         uint64_t prod = 1;
         for (int i = 0; i < ndim; ++i) prod *= dims[8 * t + i];
         if ((ndim && prod != n) || (!ndim && n != 1))
-            return report_error(DF11_E_ARG, "tensor %d: shape does not match %llu elements", t, (unsigned long long)n);
-        if (n > (uint64_t(1) << 46)) return report_error(DF11_E_UNSUPPORTED, "tensor %d: %llu elements", t, (unsigned long long)n);
+            return report_error(DF11_E_ARG, "%s: tensor %d: shape does not match %llu elements", who, t,
+                                (unsigned long long)n);
+        if (n > (uint64_t(1) << 46))
+            return report_error(DF11_E_UNSUPPORTED, "%s: tensor %d: %llu elements", who, t, (unsigned long long)n);
         if (((uintptr_t)d_words[t] & 15) || ((uintptr_t)d_outs[t] & 15))
-            return report_error(DF11_E_ARG, "tensor %d: words and output must be 16-byte aligned", t);
+            return report_error(DF11_E_ARG, "%s: tensor %d: words and output must be 16-byte aligned", who, t);
         if (out_caps[t] < df11_container_bound(n))
-            return report_error(DF11_E_ARG, "tensor %d: %llu bytes of output, below df11_container_bound (%llu)", t,
-                                (unsigned long long)out_caps[t], (unsigned long long)df11_container_bound(n));
+            return report_error(DF11_E_ARG, "%s: tensor %d: %llu bytes of output, below df11_container_bound (%llu)",
+                                who, t, (unsigned long long)out_caps[t], (unsigned long long)df11_container_bound(n));
     }
-    if (n_tensors == 0) return DF11_OK;
-    int prev = -1;
-    if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(hip_device) != hipSuccess)
-        return report_error(DF11_E_HIP, "df11_encode_device: device %d", hip_device);
-    struct Restore {
-        int d;
-        ~Restore() { if (d >= 0) (void)hipSetDevice(d); }
-    } restore{prev};
-    auto hip_fail = [](hipError_t e, const char *what) {
-        return report_error(DF11_E_HIP, "df11_encode_device: %s: %s", what, hipGetErrorString(e));
-    };
-    hipError_t e;
+    return DF11_OK;
+}
 
-    // 1. every tensor's histogram, back to the host in one copy
-    std::vector<uint64_t> freq((size_t)n_tensors * 256, 0);
-    unsigned long long *hist = nullptr;
-    const size_t hist_bytes = (size_t)n_tensors * 256 * sizeof(unsigned long long);
-    if ((e = hipMallocAsync((void **)&hist, hist_bytes, stream)) != hipSuccess) return hip_fail(e, "hipMallocAsync");
+// Makes hip_device current for the caller's scope and puts the previous one
+// back.
+struct DeviceScope {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceScope(int dev) {
+        ok = hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceScope() {
+        if (ok && prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+df11_status hip_fail(const char *who, hipError_t e, const char *what) {
+    return report_error(DF11_E_HIP, "%s: %s: %s", who, what, hipGetErrorString(e));
+}
+
+// 1. every tensor's exponent histogram into hist (256 counters per tensor,
+// cleared here), then back to the host (freq) in one copy; waits for it.
+hipError_t histograms(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                      unsigned long long *hist, uint64_t *freq, int hip_device, hipStream_t stream) {
+    const uint64_t n_ctr = (uint64_t)n_tensors * 256;
+    hipLaunchKernelGGL(enc_clear, dim3((unsigned)((n_ctr + kEncThreads - 1) / kEncThreads)), dim3(kEncThreads), 0,
+                       stream, (GLOBAL unsigned long long *)hist, n_ctr);
+    hipError_t e = hipGetLastError();
     int n_cu = 0;
     (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device);
-    e = hipMemsetAsync(hist, 0, hist_bytes, stream);
     for (int t = 0; t < n_tensors && e == hipSuccess; ++t) {
         if (!n_elems[t]) continue;
         const uint64_t need = (n_elems[t] + kEncThreads * 8 - 1) / (kEncThreads * 8);
@@ -377,17 +416,20 @@ extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const
                            n_elems[t], (GLOBAL unsigned long long *)(hist + 256 * (size_t)t));
         e = hipGetLastError();
     }
-    if (e == hipSuccess) e = hipMemcpyAsync(freq.data(), hist, hist_bytes, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(freq, hist, n_ctr * sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
-    const hipError_t ef = hipFreeAsync(hist, stream);
-    if (e != hipSuccess) return hip_fail(e, "histogram");
-    if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync");
+    return e;
+}
 
-    // 2.-4. per tensor: the code, layout and header on the host; the header,
-    // chunk bits, chunk index and packing enqueued (nothing waits for them)
+// 2.-4. per tensor: the code, layout and header on the host; the header,
+// chunk bits, chunk index and packing enqueued (nothing waits for them).
+df11_status pack_batch(const char *who, int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                       const int *ndims, const uint64_t *dims, void *const *d_outs, uint64_t *out_bytes,
+                       const uint64_t *freq, hipStream_t stream) {
+    hipError_t e;
     for (int t = 0; t < n_tensors; ++t) {
         const uint64_t n = n_elems[t];
-        const uint64_t *f = freq.data() + 256 * (size_t)t;
+        const uint64_t *f = freq + 256 * (size_t)t;
         CodeTable T;
         build_code(f, T.len, T.code);
         uint64_t total_bits = 0;
@@ -396,7 +438,7 @@ extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const
         Header h;
         write_header(reinterpret_cast<uint8_t *>(h.w), n, ndims[t], dims + 8 * t, L, T.len);
         uint8_t *out = static_cast<uint8_t *>(d_outs[t]);
-        if ((e = hipMemsetAsync(out, 0, L.total, stream)) != hipSuccess) return hip_fail(e, "hipMemsetAsync");
+        if ((e = hipMemsetAsync(out, 0, L.total, stream)) != hipSuccess) return hip_fail(who, e, "hipMemsetAsync");
         hipLaunchKernelGGL(enc_header, dim3(1), dim3(kHeader / 4), 0, stream, h, (GLOBAL uint32_t *)out);
         if (n) {
             const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
@@ -407,10 +449,60 @@ extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const
                         (GLOBAL uint8_t *)(out + L.off_raw)};
             hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, pa, T);
         }
-        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "launch");
+        if ((e = hipGetLastError()) != hipSuccess) return hip_fail(who, e, "launch");
         out_bytes[t] = L.total;
     }
     return DF11_OK;
+}
+
+}  // namespace
+
+}  // namespace df11
+
+using namespace df11;
+
+extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
+                                                const int *ndims, const uint64_t *dims, void *const *d_outs,
+                                                const uint64_t *out_caps, uint64_t *out_bytes, int hip_device,
+                                                hipStream_t stream) {
+    const char *who = "df11_encode_device_batch";
+    df11_status st = check_batch(who, n_tensors, d_words, n_elems, ndims, dims, d_outs, out_caps, out_bytes);
+    if (st != DF11_OK || n_tensors == 0) return st;
+    DeviceScope scope(hip_device);
+    if (!scope.ok) return report_error(DF11_E_HIP, "%s: device %d", who, hip_device);
+    std::vector<uint64_t> freq((size_t)n_tensors * 256, 0);
+    unsigned long long *hist = nullptr;
+    hipError_t e = hipMallocAsync((void **)&hist, (size_t)n_tensors * 256 * sizeof(unsigned long long), stream);
+    if (e != hipSuccess) return hip_fail(who, e, "hipMallocAsync");
+    e = histograms(n_tensors, d_words, n_elems, hist, freq.data(), hip_device, stream);
+    const hipError_t ef = hipFreeAsync(hist, stream);
+    if (e != hipSuccess) return hip_fail(who, e, "histogram");
+    if (ef != hipSuccess) return hip_fail(who, ef, "hipFreeAsync");
+    return pack_batch(who, n_tensors, d_words, n_elems, ndims, dims, d_outs, out_bytes, freq.data(), stream);
+}
+
+extern "C" df11_status df11_encode_device_batch_noalloc(int n_tensors, const void *const *d_words,
+                                                        const uint64_t *n_elems, const int *ndims,
+                                                        const uint64_t *dims, void *const *d_outs,
+                                                        const uint64_t *out_caps, uint64_t *out_bytes,
+                                                        int hip_device, hipStream_t stream) {
+    const char *who = "df11_encode_device_batch_noalloc";
+    if (n_tensors > kNoAllocTensors)
+        return report_error(DF11_E_UNSUPPORTED, "%s: %d tensors, at most %d per call", who, n_tensors,
+                            kNoAllocTensors);
+    if (hip_device < 0 || hip_device >= kMaxDevices)
+        return report_error(DF11_E_ARG, "%s: device %d", who, hip_device);
+    df11_status st = check_batch(who, n_tensors, d_words, n_elems, ndims, dims, d_outs, out_caps, out_bytes);
+    if (st != DF11_OK || n_tensors == 0) return st;
+    DeviceScope scope(hip_device);
+    if (!scope.ok) return report_error(DF11_E_HIP, "%s: device %d", who, hip_device);
+    std::lock_guard<std::mutex> hold(g_scratch_mu);
+    unsigned long long *hist = nullptr;
+    hipError_t e = scratch_on(hip_device, &hist);
+    if (e != hipSuccess) return hip_fail(who, e, "hipGetSymbolAddress");
+    if ((e = histograms(n_tensors, d_words, n_elems, hist, g_freq, hip_device, stream)) != hipSuccess)
+        return hip_fail(who, e, "histogram");
+    return pack_batch(who, n_tensors, d_words, n_elems, ndims, dims, d_outs, out_bytes, g_freq, stream);
 }
 
 extern "C" df11_status df11_encode_device(const void *d_words, uint64_t n, int ndim, const uint64_t *dims,

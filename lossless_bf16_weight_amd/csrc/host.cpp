@@ -27,7 +27,8 @@ using namespace df11;
 
 // ------------------------------------------------------------ error text --
 
-static thread_local std::string g_error = "no error";
+// (a fixed buffer: reporting an error allocates nothing)
+static thread_local char g_error[640] = "no error";
 
 df11_status df11::report_error(df11_status st, const char *fmt, ...) {
     char buf[512];
@@ -35,7 +36,7 @@ df11_status df11::report_error(df11_status st, const char *fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    g_error = std::string(df11_status_str(st)) + ": " + buf;
+    snprintf(g_error, sizeof g_error, "%s: %s", df11_status_str(st), buf);
     return st;
 }
 
@@ -64,7 +65,7 @@ extern "C" const char *df11_status_str(df11_status s) {
     return "DF11_E_UNKNOWN";
 }
 
-extern "C" const char *df11_last_error(void) { return g_error.c_str(); }
+extern "C" const char *df11_last_error(void) { return g_error; }
 extern "C" int df11_abi_version(void) { return DF11_ABI_VERSION; }
 
 // ------------------------------------------------------------ the layout --
@@ -424,7 +425,8 @@ extern "C" df11_status df11_plan(const void *const *host_meta, const size_t *hos
     for (int t = 0; t < n_tensors; ++t) {
         df11_status st = parse_and_validate((const uint8_t *)host_meta[t], host_meta_bytes[t], p->meta[t]);
         if (st) {
-            g_error += " (tensor " + std::to_string(t) + ")";
+            const size_t used = strlen(g_error);
+            snprintf(g_error + used, sizeof g_error - used, " (tensor %d)", t);
             delete p;
             return st;
         }
