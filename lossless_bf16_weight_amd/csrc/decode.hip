@@ -24,8 +24,8 @@
 //      independent dependency chains; 512 chains per workgroup).  A chain
 //      keeps the two code words around its position in registers; a
 //      look-up funnel-shifts them, reads one first-level table entry (up to
-//      three codes of <= 10 bits; codes of 11..16 bits use a second-level
-//      table, longer ones the canonical limits) together with the next code
+//      three codes of <= 10 bits; codes of 11..16 bits use a subtable the
+//      entry names, longer ones the canonical limits) together with the next code
 //      word, and ORs the exponent bytes (rotated, see rot_exp) into a 32 KiB
 //      LDS tile at their chunk positions.  A counted loop with no per-lane
 //      control flow runs while no window of the wave can run out (each
@@ -172,17 +172,14 @@ struct GlobalCodes {
     }
 };
 
-// The second-level table's first prefix and size, per item in scalar
-// registers.
-struct L2Bounds {
-    uint32_t base, size;
-};
-
 // First-level style entry of one code of `len` bits and rotated exponent
 // byte `sym`.
 __device__ __forceinline__ uint32_t one_code(uint32_t sym, uint32_t len) {
     return sym | (len << kEntLenShift) | (1u << kEntCountShift);
 }
+
+// A first-level entry that names a second-level subtable (its count is 0).
+__device__ __forceinline__ bool is_long(uint32_t ent) { return ent < (1u << kEntCountShift); }
 
 // Entry for a code longer than kL2Bits from the canonical limits; msb = the
 // next 30 stream bits, first bit highest.  A prefix no valid stream holds
@@ -199,27 +196,30 @@ __device__ __forceinline__ uint32_t limits_entry(const LutRecord &T, uint32_t ms
 }
 
 // Entries for codes longer than kL1Bits, for both chains at once (ea / eb
-// are replaced where they are 0; ta / tb are the peeked words, the code from
-// bit 2 on).  The two second-level reads are issued together, one LDS round
-// trip for the pair; a code longer than kL2Bits then takes the canonical
-// limits.
-__device__ __forceinline__ void long_pair(const LutRecord &T, L2Bounds l2, uint32_t ta, uint32_t tb,
-                                          uint32_t &ea, uint32_t &eb, uint32_t &bad) {
-    const uint32_t ma = __builtin_bitreverse32(ta >> 2);   // next 30 bits, first bit highest
-    const uint32_t mb = __builtin_bitreverse32(tb >> 2);
-    const uint32_t ia = (ma >> (32 - kL2Bits)) - l2.base;
-    const uint32_t ib = (mb >> (32 - kL2Bits)) - l2.base;
-    // (indexes clamped into the table, so that both reads are unconditional)
-    const uint32_t ra = T.l2[min(ia, (uint32_t)kL2Max - 1u)];
-    const uint32_t rb = T.l2[min(ib, (uint32_t)kL2Max - 1u)];
-    const bool la = ea == 0, lb = eb == 0;
-    const uint32_t e2a = (la && ia < l2.size) ? ra : 0u;
-    const uint32_t e2b = (lb && ib < l2.size) ? rb : 0u;
-    ea = la ? one_code(e2a & 0xFFu, e2a >> 8) : ea;
-    eb = lb ? one_code(e2b & 0xFFu, e2b >> 8) : eb;
-    if (__builtin_expect((la && e2a == 0) | (lb && e2b == 0), 0)) {
-        if (la && e2a == 0) ea = limits_entry(T, ma, bad);
-        if (lb && e2b == 0) eb = limits_entry(T, mb, bad);
+// are replaced where they name a subtable; ta / tb are the peeked words,
+// the code from bit 2 on).  The subtable entry's byte address is
+// l2 - 2 + F + bfe(peek, 11, k + 1) with F << 16 | (k + 1) the first-level
+// entry: the k + 1 bits from the prefix's last bit on are twice the index
+// plus that bit, which F takes off again.  Both chains' reads go out
+// together, one LDS round trip for the pair, and the u16 entry becomes a
+// first-level entry with one byte permute.  A code longer than kL2Bits then
+// takes the canonical limits.
+__device__ __forceinline__ void long_pair(const LutRecord &T, uint32_t ta, uint32_t tb, uint32_t &ea, uint32_t &eb,
+                                          uint32_t &bad) {
+    const bool la = is_long(ea), lb = is_long(eb);
+    const uint8_t *l2 = reinterpret_cast<const uint8_t *>(T.l2) - 2;
+    // (a chain with a short code reads entry 0, so that both reads are
+    // unconditional and inside the table)
+    const uint32_t ia = la ? (ea >> 16) + __builtin_amdgcn_ubfe(ta, 11, ea) : 2u;
+    const uint32_t ib = lb ? (eb >> 16) + __builtin_amdgcn_ubfe(tb, 11, eb) : 2u;
+    const uint32_t ra = *reinterpret_cast<const uint16_t *>(l2 + ia);
+    const uint32_t rb = *reinterpret_cast<const uint16_t *>(l2 + ib);
+    // byte 0 stays, byte 1 (length | 1 << 5) moves to byte 3
+    ea = la ? __builtin_amdgcn_perm(0u, ra, 0x010C0C00u) : ea;
+    eb = lb ? __builtin_amdgcn_perm(0u, rb, 0x010C0C00u) : eb;
+    if (__builtin_expect((la && ra == 0) | (lb && rb == 0), 0)) {
+        if (la && ra == 0) ea = limits_entry(T, __builtin_bitreverse32(ta >> 2), bad);
+        if (lb && rb == 0) eb = limits_entry(T, __builtin_bitreverse32(tb >> 2), bad);
     }
 }
 
@@ -230,7 +230,7 @@ __device__ __forceinline__ uint32_t ent_bits(uint32_t ent) { return (ent >> kEnt
 // global memory (chunks whose codes are not staged in LDS).  kClamp: clamp
 // the positions to the source.
 template <bool kClamp>
-__device__ __forceinline__ void entries(const Lds &L, L2Bounds l2, const GlobalCodes &src, uint32_t pa,
+__device__ __forceinline__ void entries(const Lds &L, const GlobalCodes &src, uint32_t pa,
                                         uint32_t pb, uint32_t &ea, uint32_t &eb, uint32_t &bad) {
     if (kClamp) {
         pa = min(pa, src.pmax);
@@ -241,7 +241,7 @@ __device__ __forceinline__ void entries(const Lds &L, L2Bounds l2, const GlobalC
     const uint32_t tb = src.peek(pb);
     ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
     eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
-    if (__builtin_expect((ea == 0) | (eb == 0), 0)) long_pair(L.lut, l2, ta, tb, ea, eb, bad);
+    if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
 }
 
 // One window's decoder.  The tile is cleared before the decode, and every
@@ -287,13 +287,13 @@ __device__ __forceinline__ void step(Lds &L, Chain &c, uint32_t ent) {
 __device__ __forceinline__ uint32_t out_pos(const Chain &c) { return c.p8 >> 3; }
 
 // The masked phase for a source in global memory (see masked_window_tail).
-__device__ __forceinline__ void masked_tail(Lds &L, L2Bounds l2, const GlobalCodes &src, Chain &A, Chain &B, int32_t &ra,
+__device__ __forceinline__ void masked_tail(Lds &L, const GlobalCodes &src, Chain &A, Chain &B, int32_t &ra,
                                             int32_t &rb, uint32_t &ea_r, uint32_t &eb_r, uint32_t &bad) {
     uint32_t ea, eb;
     bool any = __ballot((ra > 0) | (rb > 0)) != 0;
     while (any) {
         const bool aa = ra > 0, ab = rb > 0;
-        entries<true>(L, l2, src, A.P, B.P, ea, eb, bad);
+        entries<true>(L, src, A.P, B.P, ea, eb, bad);
         ea = aa ? ea : 0u;
         eb = ab ? eb : 0u;
         ea_r = aa ? ea : ea_r;
@@ -329,7 +329,7 @@ __device__ __forceinline__ Window window_at(const uint32_t *w, uint32_t P) {
 }
 
 // One counted look-up of both chains from their register windows.
-__device__ __forceinline__ void window_step(Lds &L, L2Bounds l2, Chain &A, Chain &B, Window &wa, Window &wb,
+__device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &wa, Window &wb,
                                             uint32_t &bad) {
     const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
     const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
@@ -339,7 +339,7 @@ __device__ __forceinline__ void window_step(Lds &L, L2Bounds l2, Chain &A, Chain
     const uint32_t na = L.codes[(A.P >> 5) + 2];
     const uint32_t nb = L.codes[(B.P >> 5) + 2];
     __builtin_amdgcn_sched_barrier(0);
-    if (__builtin_expect((ea == 0) | (eb == 0), 0)) long_pair(L.lut, l2, ta, tb, ea, eb, bad);
+    if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
     // a look-up takes fewer than 32 bits, so it moves a chain at most one word
     const bool ca = (A.P | 31u) < A.P + ent_bits(ea);
     const bool cb = (B.P | 31u) < B.P + ent_bits(eb);
@@ -355,7 +355,7 @@ __device__ __forceinline__ void window_step(Lds &L, L2Bounds l2, Chain &A, Chain
 // whose windows still have codes (the others take a zero entry and keep
 // their state).  The next-word reads are clamped to the staged words, so a
 // container whose index disagrees with its stream reads inside them.
-__device__ __forceinline__ void masked_window_tail(Lds &L, L2Bounds l2, uint32_t kmax, Chain &A, Chain &B, Window &wa,
+__device__ __forceinline__ void masked_window_tail(Lds &L, uint32_t kmax, Chain &A, Chain &B, Window &wa,
                                                    Window &wb, int32_t &ra, int32_t &rb, uint32_t &ea_r,
                                                    uint32_t &eb_r, uint32_t &bad) {
     const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
@@ -369,7 +369,7 @@ __device__ __forceinline__ void masked_window_tail(Lds &L, L2Bounds l2, uint32_t
         const uint32_t na = L.codes[min(A.P >> 5, kmax) + 2];
         const uint32_t nb = L.codes[min(B.P >> 5, kmax) + 2];
         __builtin_amdgcn_sched_barrier(0);
-        if (__builtin_expect((ea == 0) | (eb == 0), 0)) long_pair(L.lut, l2, ta, tb, ea, eb, bad);
+        if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
         ea = aa ? ea : 0u;
         eb = ab ? eb : 0u;
         ea_r = aa ? ea : ea_r;
@@ -392,7 +392,7 @@ __device__ __forceinline__ void masked_window_tail(Lds &L, L2Bounds l2, uint32_t
 // the wave has run out of codes.  On return A.P / B.P hold the stream
 // positions (plus kPosBias) where the windows' last codes end.
 template <class Src>
-__device__ __forceinline__ void decode_pair(Lds &L, L2Bounds l2, const Src &src, Chain &A, Chain &B, uint32_t T,
+__device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Chain &B, uint32_t T,
                                             uint32_t &bad) {
     uint32_t ea, eb;
     int32_t ra, rb;
@@ -405,19 +405,19 @@ __device__ __forceinline__ void decode_pair(Lds &L, L2Bounds l2, const Src &src,
         Window wa = window_at(src.w, A.P), wb = window_at(src.w, B.P);
         // (the loop then starts with no LDS read in flight)
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        for (uint32_t t = 0; t < T; ++t) window_step(L, l2, A, B, wa, wb, bad);
+        for (uint32_t t = 0; t < T; ++t) window_step(L, A, B, wa, wb, bad);
         ra = (int32_t)(A.qe - out_pos(A));
         rb = (int32_t)(B.qe - out_pos(B));
-        masked_window_tail(L, l2, src.pmax >> 5, A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
+        masked_window_tail(L, src.pmax >> 5, A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
     } else {
         for (uint32_t t = 0; t < T; ++t) {
-            entries<false>(L, l2, src, A.P, B.P, ea, eb, bad);
+            entries<false>(L, src, A.P, B.P, ea, eb, bad);
             step(L, A, ea);
             step(L, B, eb);
         }
         ra = (int32_t)(A.qe - out_pos(A));
         rb = (int32_t)(B.qe - out_pos(B));
-        masked_tail(L, l2, src, A, B, ra, rb, ea_r, eb_r, bad);
+        masked_tail(L, src, A, B, ra, rb, ea_r, eb_r, bad);
     }
     // the last entry took -r codes past the window's end
     A.P -= trailing_bits(L, ea_r, (uint32_t)(-ra));
@@ -679,17 +679,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         const uint32_t T =
             __builtin_amdgcn_readfirstlane(wave_min(min(m >= 1 ? (m - 1) / kMaxPerLookup : 0u, room)));
         Chain A{pa + kPosBias, qa << 3, qa + na};
-        const L2Bounds l2{(uint32_t)__builtin_amdgcn_readfirstlane(L.lut.l2_base),
-                          (uint32_t)__builtin_amdgcn_readfirstlane(L.lut.l2_size)};
         Chain B{pb + kPosBias, qb << 3, qb + nb};
         if (it.staged) {
             // code-word reads: codes[k .. k+2] with k = P / 32 <= kCodeWords - 1
             const LdsCodes src{L.codes, pmax + kPosBias};
-            decode_pair(L, l2, src, A, B, T, bad);
+            decode_pair(L, src, A, B, T, bad);
         } else {
             // peeks read words k-1 and k of the stream from s0, k < n_words
             const GlobalCodes src{reinterpret_cast<const GLOBAL uint32_t *>(it.stream) - 1, pmax + kPosBias};
-            decode_pair(L, l2, src, A, B, T, bad);
+            decode_pair(L, src, A, B, T, bad);
         }
         const uint32_t ea = A.P - kPosBias;
         const uint32_t eb = B.P - kPosBias;

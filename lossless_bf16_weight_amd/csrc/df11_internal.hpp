@@ -45,16 +45,22 @@ DF11_HD constexpr uint32_t window_edge(uint32_t nbits, uint32_t i) {
 // the first of them the lowest index bit.
 // Entry: bits 0..23 up to three rotated exponent bytes (first code in the
 // low byte), bits 24..28 how many stream bits they use, bits 29..30 how many
-// codes (1..3).  Entry 0: the next code is longer than kL1Bits (or no code
-// matches: a prefix no valid stream holds).
+// codes (1..3).  An entry with count 0 names the second-level subtable of a
+// prefix whose first code is longer than kL1Bits (or that no valid stream
+// holds): F << 16 | (k + 1), below.
 constexpr int kL1Bits = 10;
 constexpr int kL1Size = 1 << kL1Bits;
 constexpr int kMaxPerLookup = 3;
 constexpr uint32_t kEntLenShift = 24;
 constexpr uint32_t kEntCountShift = 29;
-// Second-level table for codes of kL1Bits+1 .. kL2Bits bits, indexed by the
-// next kL2Bits bits minus l2_base (= the first such prefix); entry
-// (length << 8) | rot(e), 0 when the code is longer than kL2Bits.
+// Second level: one subtable per such prefix, indexed by its next k stream
+// bits (first bit lowest), k = min(longest code under the prefix, kL2Bits) -
+// kL1Bits, in canonical order from entry 2 on; entry rot(e) | (len | 1 << 5)
+// << 8 (its high byte moved to bits 24..31 gives a one-code first-level
+// entry), 0 for a code longer than kL2Bits (the canonical limits take it).
+// Entries 0 and 1 stay 0: the subtable of the prefixes no valid stream holds
+// and of those left over when the table is full.  F = 2 + (the subtable's
+// byte offset) - (the prefix's last stream bit).
 constexpr int kL2Bits = 16;
 constexpr int kL2Max = 512;
 
@@ -72,11 +78,12 @@ struct alignas(16) LutRecord {
     uint8_t sorted[256];
     // code length by rotated exponent byte (0 = absent)
     uint8_t len[256];
-    uint32_t l2_base;
-    uint32_t l2_size;
-    uint32_t pad[2];
+    uint32_t pad[4];
 };
 static_assert(sizeof(LutRecord) == 5904, "LUT record size");
+
+// Builds a tensor's decode tables from its code lengths (host.cpp).
+void build_lut(const uint8_t *len, LutRecord &R);
 
 // Staged code bytes per chunk: chunks whose codes (plus 127 bits of slack,
 // rounded out to 16 bytes) fit go through LDS, the others are read from

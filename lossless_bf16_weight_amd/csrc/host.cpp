@@ -139,56 +139,6 @@ inline int lookup(const Canon &C, int l, uint32_t code) {
     return C.sorted[C.offset[l] + code - C.first[l]];
 }
 
-void build_lut(const uint8_t *len, LutRecord &R) {
-    memset(&R, 0, sizeof R);
-    Canon C = canonical(len);
-    for (int i = 0; i < C.n_sym; ++i) R.sorted[i] = rot_exp(C.sorted[i]);
-    for (int s = 0; s < 256; ++s) R.len[rot_exp(s)] = len[s];
-    for (int l = 0; l < 32; ++l) { R.lim[l] = 0xFFFFFFFFu; R.base[l] = 0; }
-    R.lim[0] = 0;
-    for (int l = 1; l <= kMaxLen; ++l) {
-        R.lim[l] = (C.first[l] + C.count[l]) << (kMaxLen - l);
-        R.base[l] = (int32_t)C.offset[l] - (int32_t)C.first[l];
-    }
-    // First level: greedily resolve up to three whole codes inside the next
-    // kL1Bits bits.  A prefix that starts with no code of <= kL1Bits bits
-    // keeps entry 0 (also every prefix no valid stream holds).
-    for (uint32_t v = 0; v < (uint32_t)kL1Size; ++v) {
-        int pos = 0, n = 0;
-        uint32_t syms = 0;
-        while (n < kMaxPerLookup) {
-            int found = -1, flen = 0;
-            for (int l = 1; l <= kL1Bits - pos && found < 0; ++l) {
-                uint32_t code = (v >> (kL1Bits - pos - l)) & ((1u << l) - 1);
-                found = lookup(C, l, code);
-                flen = l;
-            }
-            if (found < 0) break;
-            syms |= (uint32_t)rot_exp((unsigned)found) << (8 * n);
-            pos += flen;
-            ++n;
-        }
-        // indexed by the 10 bits in stream order, first bit lowest (the
-        // decoder reads its code words least significant bit first)
-        const uint32_t rv = __builtin_bitreverse32(v) >> (32 - kL1Bits);
-        R.l1[rv] = n ? (syms | ((uint32_t)pos << kEntLenShift) | ((uint32_t)n << kEntCountShift)) : 0u;
-    }
-    // Second level: 16-bit prefixes from the first one no code of <= kL1Bits
-    // bits covers.
-    R.l2_base = R.lim[kL1Bits] >> (kMaxLen - kL2Bits);
-    R.l2_size = std::min<uint32_t>((1u << kL2Bits) - R.l2_base, kL2Max);
-    for (uint32_t i = 0; i < R.l2_size; ++i) {
-        const uint32_t v = R.l2_base + i;
-        for (int l = kL1Bits + 1; l <= kL2Bits; ++l) {
-            const int s = lookup(C, l, v >> (kL2Bits - l));
-            if (s >= 0) {
-                R.l2[i] = (uint16_t)((l << 8) | rot_exp((unsigned)s));
-                break;
-            }
-        }
-    }
-}
-
 // Validate a metadata prefix held in host memory.
 df11_status parse_and_validate(const uint8_t *c, size_t bytes, Meta &M) {
     if (!c) return fail(DF11_E_ARG, "container pointer is NULL");
@@ -306,6 +256,76 @@ void fill_info(const Meta &M, df11_tensor_info *info) {
 }
 
 }  // namespace
+
+void df11::build_lut(const uint8_t *len, LutRecord &R) {
+    memset(&R, 0, sizeof R);
+    Canon C = canonical(len);
+    for (int i = 0; i < C.n_sym; ++i) R.sorted[i] = rot_exp(C.sorted[i]);
+    for (int s = 0; s < 256; ++s) R.len[rot_exp(s)] = len[s];
+    for (int l = 0; l < 32; ++l) { R.lim[l] = 0xFFFFFFFFu; R.base[l] = 0; }
+    R.lim[0] = 0;
+    for (int l = 1; l <= kMaxLen; ++l) {
+        R.lim[l] = (C.first[l] + C.count[l]) << (kMaxLen - l);
+        R.base[l] = (int32_t)C.offset[l] - (int32_t)C.first[l];
+    }
+    // First level: greedily resolve up to three whole codes inside the next
+    // kL1Bits bits.  A prefix that starts with no code of <= kL1Bits bits
+    // (or that no valid stream holds) gets a subtable entry below.
+    for (uint32_t v = 0; v < (uint32_t)kL1Size; ++v) {
+        int pos = 0, n = 0;
+        uint32_t syms = 0;
+        while (n < kMaxPerLookup) {
+            int found = -1, flen = 0;
+            for (int l = 1; l <= kL1Bits - pos && found < 0; ++l) {
+                uint32_t code = (v >> (kL1Bits - pos - l)) & ((1u << l) - 1);
+                found = lookup(C, l, code);
+                flen = l;
+            }
+            if (found < 0) break;
+            syms |= (uint32_t)rot_exp((unsigned)found) << (8 * n);
+            pos += flen;
+            ++n;
+        }
+        // indexed by the 10 bits in stream order, first bit lowest (the
+        // decoder reads its code words least significant bit first)
+        const uint32_t rv = __builtin_bitreverse32(v) >> (32 - kL1Bits);
+        R.l1[rv] = n ? (syms | ((uint32_t)pos << kEntLenShift) | ((uint32_t)n << kEntCountShift)) : 0u;
+    }
+    // Second level: a subtable per prefix whose first code is longer than
+    // kL1Bits (layout in df11_internal.hpp), in canonical order, so that the
+    // shorter and more frequent long codes get a subtable first.
+    uint32_t used = 2;
+    for (uint32_t v = 0; v < (uint32_t)kL1Size; ++v) {
+        const uint32_t rv = __builtin_bitreverse32(v) >> (32 - kL1Bits);
+        if (R.l1[rv]) continue;
+        uint32_t maxlen = 0;
+        for (int l = kL1Bits + 1; l <= kMaxLen; ++l) {
+            const uint64_t lo = (uint64_t)v << (l - kL1Bits), hi = (uint64_t)(v + 1) << (l - kL1Bits);
+            if (C.count[l] && lo < (uint64_t)C.first[l] + C.count[l] && hi > C.first[l]) maxlen = (uint32_t)l;
+        }
+        const uint32_t k = maxlen ? std::min<uint32_t>(maxlen, kL2Bits) - kL1Bits : 1u;
+        uint32_t off = 0;
+        if (maxlen && used + (1u << k) <= (uint32_t)kL2Max) {
+            off = used;
+            used += 1u << k;
+            for (uint32_t j = 0; j < (1u << k); ++j) {
+                // j's bits in stream order, first bit lowest
+                for (uint32_t l = kL1Bits + 1; l <= kL1Bits + k; ++l) {
+                    const uint32_t ext = l - kL1Bits;
+                    const uint32_t tail = __builtin_bitreverse32(j & ((1u << ext) - 1u)) >> (32 - ext);
+                    const int s = lookup(C, (int)l, (v << ext) | tail);
+                    if (s >= 0) {
+                        R.l2[off + j] = (uint16_t)(rot_exp((unsigned)s) | ((l | 32u) << 8));
+                        break;
+                    }
+                }
+            }
+        }
+        const uint32_t last_bit = (rv >> (kL1Bits - 1)) & 1u;
+        const uint32_t F = 2u + 2u * off - last_bit;
+        R.l1[rv] = (F << 16) | (k + 1u);
+    }
+}
 
 extern "C" df11_status df11_validate(const void *host_meta, size_t bytes, df11_tensor_info *info) {
     Meta M;

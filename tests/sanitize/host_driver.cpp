@@ -1,7 +1,9 @@
 // Sanitizer driver for the host code of libdf11 (validation, encoders, SHA-256,
-// NF12 host code), built with g++ -fsanitize=address,undefined on the CPU.
+// NF12 host code), built with clang++ -fsanitize=address,undefined on the CPU.
 //
 // Reads a manifest of "<kind> <path>" lines:
+//   slots -                 the decode's ticket-counter slots (SlotTable)
+//   luts  -                 the decode tables against the kernel's look-up arithmetic
 //   df11  <container file>  df11_validate on the whole file and on prefixes
 //   nf12  <container file>  df11_nf12_validate on the whole file and on prefixes
 //   words <16-bit words>    df11_encode (1 and 4 threads), df11_encode_ex with the
@@ -141,6 +143,84 @@ static int check_slots() {
     return 0;
 }
 
+// The decode tables (build_lut) against the kernel's look-up arithmetic, on
+// random streams for many codes: a first-level entry by the next 10 bits,
+// a subtable entry at l2 - 2 + F + bfe(peek, 11, k + 1) for a prefix whose
+// first code is longer, the canonical limits for codes longer than 16 bits.
+// Every look-up must give the next codes' exponents and bits as the
+// canonical code (from the encoder's own construction) has them.
+static uint64_t lcg(uint64_t &x) {
+    x = x * 6364136223846793005ull + 1442695040888963407ull;
+    return x >> 33;
+}
+
+static int check_luts() {
+    using namespace df11;
+    uint64_t rng = 12345;
+    for (int trial = 0; trial < 400; ++trial) {
+        uint64_t freq[256] = {};
+        const int kind = trial % 5;
+        const int nsym = kind == 3 ? 1 + trial % 3 : 1 + (int)(lcg(rng) % 256);
+        for (int i = 0; i < nsym; ++i) {
+            const int sym = (int)(lcg(rng) % 256);
+            uint64_t f = 1;
+            if (kind == 0) f = 1 + (uint64_t)(1e9 / (1.0 + (double)i * i));     // peaked
+            if (kind == 1) f = (uint64_t)1 << (i % 40);                         // up to the 24-bit cap
+            if (kind == 2) f = 1 + lcg(rng) % 1000;                             // flat
+            if (kind == 4) f = i < 6 ? 1000000000ull : 1 + lcg(rng) % 3;        // heavy tail
+            freq[sym] += f;
+        }
+        uint8_t len[256];
+        uint32_t code[256];
+        build_code(freq, len, code);
+        LutRecord R;
+        build_lut(len, R);
+        int syms[256], n = 0;
+        for (int e = 0; e < 256; ++e)
+            if (len[e]) syms[n++] = e;
+        // a stream of 3000 codes, symbols drawn uniformly (long codes often)
+        std::vector<uint8_t> bits = {0, 0};   // two bits before the stream
+        std::vector<int> seq;
+        for (int i = 0; i < 3000; ++i) {
+            const int e = syms[lcg(rng) % (uint64_t)n];
+            seq.push_back(e);
+            for (int b = len[e] - 1; b >= 0; --b) bits.push_back((uint8_t)((code[e] >> b) & 1));
+        }
+        for (int i = 0; i < 64; ++i) bits.push_back((uint8_t)(lcg(rng) & 1));
+        size_t p = 2, i = 0;
+        while (i < seq.size()) {
+            uint32_t ta = 0;
+            for (int b = 0; b < 32; ++b) ta |= (uint32_t)bits[p - 2 + b] << b;
+            uint32_t ent = R.l1[(ta >> 2) & (kL1Size - 1)];
+            if ((ent >> kEntCountShift) == 0) {
+                const uint32_t w = ent & 31u;
+                const uint32_t ia = (ent >> 16) + ((ta >> 11) & ((1u << w) - 1u));
+                if (ia < 2 || (ia & 1u) || (ia - 2) / 2 >= (uint32_t)kL2Max) return 30;
+                const uint32_t ra = R.l2[(ia - 2) / 2];
+                if (ra) {
+                    ent = (ra & 0xFFu) | ((ra >> 8) << 24);
+                } else {
+                    const uint32_t v = __builtin_bitreverse32(ta >> 2) >> (32 - kMaxLen);
+                    uint32_t l = kL1Bits + 1;
+                    while (l <= (uint32_t)kMaxLen && v >= R.lim[l]) ++l;
+                    if (l > (uint32_t)kMaxLen) return 31;
+                    ent = R.sorted[(int)(v >> (kMaxLen - l)) + R.base[l]] | (l << kEntLenShift) | (1u << kEntCountShift);
+                }
+            }
+            const uint32_t cnt = ent >> kEntCountShift, nb = (ent >> kEntLenShift) & 31u;
+            if (cnt == 0 || cnt > (uint32_t)kMaxPerLookup) return 32;
+            uint32_t used = 0;
+            for (uint32_t j = 0; j < cnt && i < seq.size(); ++j, ++i) {
+                if (((ent >> (8 * j)) & 0xFFu) != rot_exp((unsigned)seq[i])) return 33;
+                used += len[seq[i]];
+            }
+            if (i < seq.size() && used != nb) return 34;
+            p += nb;
+        }
+    }
+    return 0;
+}
+
 int main(int argc, char **argv) {
     if (argc != 2) {
         fprintf(stderr, "usage: %s MANIFEST\n", argv[0]);
@@ -170,6 +250,12 @@ int main(int argc, char **argv) {
             const int r = check_slots();
             if (r) {
                 fprintf(stderr, "slot table check %d failed\n", r);
+                return 3;
+            }
+        } else if (!strcmp(kind, "luts")) {
+            const int r = check_luts();
+            if (r) {
+                fprintf(stderr, "decode table check %d failed\n", r);
                 return 3;
             }
         } else if (!strcmp(kind, "words")) {

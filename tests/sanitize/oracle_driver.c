@@ -93,7 +93,7 @@ int main(int argc, char **argv) {
             prefixes(c, n, kind[0] == 'n');
             free(c);
             ++counts[kind[0] == 'n' ? 2 : 1];
-        } else if (strcmp(kind, "slots") != 0) {   /* (the host driver's own check) */
+        } else if (strcmp(kind, "slots") != 0 && strcmp(kind, "luts") != 0) {   /* (the host driver's own checks) */
             return 2;
         }
     }

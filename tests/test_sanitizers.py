@@ -9,9 +9,12 @@ containers and word files, and a few thousand containers broken on purpose
 flips, truncations).  Every validation must return a status without a
 sanitizer report, every word file must round-trip, and the sanitized encoder
 must write the bytes the normal build writes.  The host side of the
-decode's ticket-counter slots is checked in the same driver: a slot is not
+decode's ticket-counter slots is checked in the same driver (a slot is not
 given out again before the device reports its launch finished, and a
-captured launch keeps its slot."""
+captured launch keeps its slot), and so are the decode tables: every look-up
+the kernel's arithmetic makes on them (first level, subtables, canonical
+limits) gives the codes the canonical code has, on random streams for 400
+codes."""
 import os
 import shutil
 import subprocess
@@ -142,7 +145,7 @@ def _run(exe, manifest):
 def test_host_code_and_oracle_under_sanitizers(drivers, tmp_path):
     host, orc = drivers
     rng = np.random.default_rng(2024)
-    lines = ["slots -"]
+    lines = ["slots -", "luts -"]
     words = _word_sets()
     for name, w in words.items():
         p = tmp_path / f"{name}.u16"
