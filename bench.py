@@ -355,7 +355,7 @@ def stack_loop(passes: int, warmup: int):
         sys.exit(1)
 
 
-def workload_table(rounds: int = 3):
+def workload_table(rounds: int = 3, names=None):
     """DF11 decode time of every single-decode workload: one batched call
     over the workload's tensors per rep.  "warm": back-to-back reps between
     two events, per round (after 400 warm-up reps, as the part runs slower
@@ -379,7 +379,7 @@ def workload_table(rounds: int = 3):
     sink = torch.empty(16, dtype=torch.uint8, device=dev)
     threads = max(1, min(16, os.cpu_count() or 1))
     rows = []
-    for name in ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
+    for name in names or ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
         specs = W.WORKLOADS[name]()
         words = [s.make(threads=threads).reshape(-1) for s in specs]
         n = sum(w.size for w in words)
@@ -469,7 +469,7 @@ def nf12_compare(reps: int = 100, warmup: int = 200):
         return a.elapsed_time(b) / reps
 
     rows = []
-    for name in ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
+    for name in names or ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
         specs = W.WORKLOADS[name]()
         words = [s.make().reshape(-1) for s in specs]
         n = sum(w.size for w in words)
@@ -522,8 +522,9 @@ def main():
                     help="only compare the NF12 format with DF11 on the workloads")
     ap.add_argument("--jit-overlap", action="store_true",
                     help="only measure the just-in-time layer loop against its consumer")
-    ap.add_argument("--workloads", action="store_true",
-                    help="only time the DF11 decode of every single-decode workload, warm and flushed")
+    ap.add_argument("--workloads", nargs="*", default=None, metavar="NAME",
+                    help="only time the DF11 decode of the single-decode workloads (all four, or the "
+                         "ones named), warm and flushed")
     ap.add_argument("--stack", action="store_true",
                     help="only measure the layer loop over the resident 32-layer stack")
     args = ap.parse_args()
@@ -547,8 +548,8 @@ def main():
         stack_loop(passes=20, warmup=10)
         return
 
-    if args.workloads:
-        workload_table()
+    if args.workloads is not None:
+        workload_table(names=args.workloads or None)
         return
 
     if args.copy_calibration:
