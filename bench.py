@@ -145,9 +145,10 @@ def jit_overlap(n_layers: int, token_counts, reps: int):
     computes x @ W^T for the layer's seven tensors (BF16 products by the
     vendor library), and the next layer decodes on its own stream meanwhile.
     Per token count: ms per layer for the consumer alone (weights already
-    decoded), the decode alone, and the overlapped loop; the overhead is the
-    loop's time over the consumer's, minus one (the quantity the mlx-dfloat
-    page reports per denoising step)."""
+    decoded), the decode alone, and the overlapped loop, with the decode's
+    workgroups per compute unit as many as fit and capped at two; the
+    overhead is the loop's time over the consumer's, minus one (the quantity
+    the mlx-dfloat page reports per denoising step)."""
     import numpy as np
     import torch
     import lossless_bf16_weight_amd as df11
@@ -189,14 +190,22 @@ def jit_overlap(n_layers: int, token_counts, reps: int):
                 F.linear(x2 if w.shape[1] == x2.shape[1] else x, w)
 
         consumer_ms = timed(lambda: [consume(l, resident) for l in range(n_layers)])
-        decode_ms = timed(lambda: [loop.decode_into(l, l & 1, stream) for l in range(n_layers)])
-        loop_ms = timed(lambda: loop.run(consume))
         flops = 2.0 * T * sum(w.numel() for w in resident)
-        rows.append({"tokens": T, "consumer_ms_per_layer": round(consumer_ms, 4),
-                     "decode_ms_per_layer": round(decode_ms, 4), "jit_loop_ms_per_layer": round(loop_ms, 4),
-                     "overhead": round(loop_ms / consumer_ms - 1.0, 4),
-                     "decode_hidden": round((consumer_ms + decode_ms - loop_ms) / decode_ms, 4),
-                     "consumer_tflops": round(flops / (consumer_ms * 1e-3) / 1e12, 1)})
+        row = {"tokens": T, "consumer_ms_per_layer": round(consumer_ms, 4),
+               "consumer_tflops": round(flops / (consumer_ms * 1e-3) / 1e12, 1)}
+        # the decode with as many workgroups per compute unit as fit, and
+        # capped at two (room for the consumer's kernels beside it)
+        for cap in (0, 2):
+            loop.set_decode_wgs_per_cu(cap)
+            decode_ms = timed(lambda: [loop.decode_into(l, l & 1, stream) for l in range(n_layers)])
+            loop_ms = timed(lambda: loop.run(consume))
+            key = "" if cap == 0 else f"_wgs{cap}"
+            row.update({f"decode_ms_per_layer{key}": round(decode_ms, 4),
+                        f"jit_loop_ms_per_layer{key}": round(loop_ms, 4),
+                        f"overhead{key}": round(loop_ms / consumer_ms - 1.0, 4),
+                        f"decode_hidden{key}": round((consumer_ms + decode_ms - loop_ms) / decode_ms, 4)})
+        loop.set_decode_wgs_per_cu(0)
+        rows.append(row)
     print(json.dumps({"metric": "just-in-time layer loop: overhead of decoding one layer ahead of a BF16 consumer",
                       "config": {"workload": "llama8b_block layers", "layers": n_layers,
                                  "consumer": "x @ W^T for the 7 tensors of each layer (torch.nn.functional.linear)"},

@@ -226,6 +226,18 @@ void df11_plan_destroy(df11_plan_t plan);
 
 df11_status df11_plan_info(df11_plan_t plan, int tensor, df11_tensor_info *info);
 
+/* How many decode workgroups the plan's later launches may place on one
+ * compute unit: 0 (the default) for as many as fit (three on gfx950), or 1
+ * to that number.  For a decode that runs next to the model's own kernels
+ * (the mlx-dfloat page, introduction: each block is decoded as the model
+ * runs; "Measured numbers": the overhead that adds to a step), a smaller
+ * number leaves LDS and wave slots on every compute unit for the other
+ * kernel, so that the two can run at once; a decode alone is fastest with
+ * the default.  Returns DF11_E_ARG for a NULL plan or a negative number;
+ * numbers above the limit act as 0.  Set it before the plan's decodes are
+ * issued from other threads: it is read, not locked, at each launch. */
+df11_status df11_plan_set_wgs_per_cu(df11_plan_t plan, int wgs_per_cu);
+
 /* ------------------------------------------------------------------ decode */
 
 /* Decode tensor `tensor` of the plan: rebuild every BF16 word from its raw

@@ -59,7 +59,7 @@ _lib = None
 EXPORTS = [
     "df11_validate", "df11_container_bound", "df11_encode", "df11_encode_ex", "df11_encode_device", "df11_encode_device_batch",
     "df11_encode_device_batch_noalloc", "df11_sha256",
-    "df11_verify_words", "df11_plan", "df11_plan_destroy",
+    "df11_verify_words", "df11_plan", "df11_plan_destroy", "df11_plan_set_wgs_per_cu",
     "df11_plan_info", "df11_decode", "df11_decode_batch", "df11_check", "df11_last_error",
     "df11_status_str", "df11_abi_version", "df11_bw_control",
     "df11_nf12_bound", "df11_nf12_encode", "df11_nf12_validate", "df11_nf12_decode",
@@ -105,6 +105,8 @@ def lib():
     L.df11_plan.restype = ctypes.c_int
     L.df11_plan_destroy.argtypes = [vp]
     L.df11_plan_destroy.restype = None
+    L.df11_plan_set_wgs_per_cu.argtypes = [vp, ctypes.c_int]
+    L.df11_plan_set_wgs_per_cu.restype = ctypes.c_int
     L.df11_plan_info.argtypes = [vp, ctypes.c_int, ctypes.POINTER(TensorInfo)]
     L.df11_plan_info.restype = ctypes.c_int
     L.df11_decode.argtypes = [vp, ctypes.c_int, vp, vp, vp]
@@ -297,6 +299,11 @@ class Plan:
         info = TensorInfo()
         _raise(lib().df11_plan_info(self._h, t, ctypes.byref(info)))
         return info.as_dict()
+
+    def set_wgs_per_cu(self, n: int) -> None:
+        """Decode workgroups per compute unit for this plan's later
+        launches: 0 for as many as fit, else a cap (df11_plan_set_wgs_per_cu)."""
+        _raise(lib().df11_plan_set_wgs_per_cu(self._h, int(n)))
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

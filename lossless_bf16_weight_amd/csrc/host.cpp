@@ -369,6 +369,7 @@ struct df11_plan_s {
     uint32_t *d_work = nullptr;              // kWorkSlots ticket counters
     uint32_t *h_fin = nullptr;               // kWorkSlots completion words (pinned host memory)
     uint32_t *d_fin = nullptr;               // the same words, as the device addresses them
+    int wgs_cap = 0;                         // decode workgroups per CU (0: as many as fit)
     std::mutex slot_mu;
     SlotTable slots;
 };
@@ -424,7 +425,9 @@ void give_back_slot(df11_plan_s *p, int slot) {
 }
 
 int grid_for(const df11_plan_s *p, uint64_t items) {
-    const uint64_t resident = (uint64_t)p->n_cu * (uint64_t)decode_wgs_per_cu();
+    uint64_t per_cu = (uint64_t)decode_wgs_per_cu();
+    if (p->wgs_cap > 0) per_cu = std::min<uint64_t>(per_cu, (uint64_t)p->wgs_cap);
+    const uint64_t resident = (uint64_t)p->n_cu * per_cu;
     return (int)std::max<uint64_t>(1, std::min<uint64_t>(items, resident));
 }
 
@@ -539,6 +542,12 @@ extern "C" void df11_plan_destroy(df11_plan_t p) {
 extern "C" df11_status df11_plan_info(df11_plan_t p, int tensor, df11_tensor_info *info) {
     if (!p || !info || tensor < 0 || tensor >= p->n_tensors) return fail(DF11_E_ARG, "plan_info arguments");
     fill_info(p->meta[tensor], info);
+    return DF11_OK;
+}
+
+extern "C" df11_status df11_plan_set_wgs_per_cu(df11_plan_t p, int wgs_per_cu) {
+    if (!p || wgs_per_cu < 0) return fail(DF11_E_ARG, "df11_plan_set_wgs_per_cu arguments");
+    p->wgs_cap = wgs_per_cu;
     return DF11_OK;
 }
 

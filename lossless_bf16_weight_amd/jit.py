@@ -20,6 +20,11 @@ from ._lib import Plan, decode_batch
 class LayerLoop:
     """Decode layer l+1 while `consumer(l, weights)` runs layer l.
 
+    decode_wgs_per_cu caps the decode's workgroups per compute unit for every
+    layer's plan (0: as many as fit): with 2, the decode shares the compute
+    units with a small consumer (one token's matrix-vector products) instead
+    of running after it; with large consumers the default is faster.
+
     plans[l] is the plan of layer l and containers[l] its device containers
     (uint8 tensors, one per planned tensor).  Every layer has the same number
     of tensors; buffer t of each of the two buffer sets is sized for the
@@ -27,7 +32,7 @@ class LayerLoop:
     with the tensor's shape (dtype bfloat16)."""
 
     def __init__(self, plans: Sequence[Plan], containers: Sequence[Sequence[torch.Tensor]],
-                 device: str = "cuda"):
+                 device: str = "cuda", decode_wgs_per_cu: int = 0):
         if len(plans) == 0 or len(plans) != len(containers):
             raise ValueError("one plan and one container list per layer")
         n_t = plans[0].n_tensors
@@ -35,6 +40,10 @@ class LayerLoop:
             if p.n_tensors != n_t or len(cs) != n_t:
                 raise ValueError("every layer needs the same number of tensors")
         self.plans = list(plans)
+        # decode workgroups per compute unit (0: as many as fit).  Fewer leave
+        # room on every compute unit for the consumer's kernels, so that the
+        # next layer's decode runs beside them instead of after them.
+        self.set_decode_wgs_per_cu(decode_wgs_per_cu)
         self.containers = [list(cs) for cs in containers]
         self.shapes = [[tuple(int(d) for d in p.infos[t]["dims"]) or (1,) for t in range(n_t)]
                        for p in self.plans]
@@ -43,6 +52,12 @@ class LayerLoop:
         self.buffers = [[torch.empty(max(b, 1), dtype=torch.bfloat16, device=device) for b in biggest]
                         for _ in range(2)]
         self.decode_stream = torch.cuda.Stream(device=device)
+
+    def set_decode_wgs_per_cu(self, n: int) -> None:
+        """Cap the decode's workgroups per compute unit (0: as many as fit)."""
+        self.decode_wgs_per_cu = int(n)
+        for p in self.plans:
+            p.set_wgs_per_cu(self.decode_wgs_per_cu)
 
     def __len__(self) -> int:
         return len(self.plans)

@@ -20,17 +20,23 @@ from gpu_util import log, to_device_u8
 pytestmark = pytest.mark.gpu
 
 
-def test_layer_loop_feeds_a_consumer_bit_exact():
+@pytest.mark.parametrize("wgs_per_cu", [0, 2, 1])
+def test_layer_loop_feeds_a_consumer_bit_exact(wgs_per_cu):
+    """Also with the decode capped at two and at one workgroup per compute
+    unit (the launch then has fewer workgroups than the chunks need rounds
+    of, and they share the compute units with the consumer's kernels)."""
     import torch
     from lossless_bf16_weight_amd.jit import LayerLoop
     F = torch.nn.functional
 
     n_layers, T = 3, 64
-    log(f"jit loop: {n_layers} Llama-8B-shaped layers, {T} tokens")
+    log(f"jit loop: {n_layers} Llama-8B-shaped layers, {T} tokens, decode workgroups per CU {wgs_per_cu}")
     groups = [W.llama8b_block(l) for l in range(n_layers)]
     words = [[s.make().reshape(-1) for s in g] for g in groups]
     conts = [[df11.encode(w, shape=s.shape) for w, s in zip(ws, g)] for ws, g in zip(words, groups)]
-    loop = LayerLoop([df11.Plan(cs) for cs in conts], [[to_device_u8(c) for c in cs] for cs in conts])
+    loop = LayerLoop([df11.Plan(cs) for cs in conts], [[to_device_u8(c) for c in cs] for cs in conts],
+                     decode_wgs_per_cu=wgs_per_cu)
+    assert all(p.infos for p in loop.plans)
     assert len(loop) == n_layers
 
     gen = torch.Generator(device="cuda").manual_seed(0)
@@ -66,3 +72,13 @@ def test_layer_loop_rejects_mismatched_layers():
         LayerLoop([p1, p2], [[d], [d, d]])
     with pytest.raises(ValueError):
         LayerLoop([p1], [[d], [d]])
+
+
+def test_plan_workgroups_per_cu_argument():
+    import torch  # noqa: F401
+    w = W.normal_bf16((5000,), seed=1)
+    p = df11.Plan([df11.encode(w)])
+    with pytest.raises(df11.DF11Error):
+        p.set_wgs_per_cu(-1)
+    p.set_wgs_per_cu(0)
+    p.set_wgs_per_cu(64)   # above the limit: as many as fit
