@@ -786,7 +786,13 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     if (tid == 0 && atomicAdd(a.work + 1, 1u) == gridDim.x - 1) {
         atomicExch(a.work, 0u);
         atomicExch(a.work + 1, 0u);
-        __hip_atomic_store(a.fin, a.launch_id, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        // The host may give the slot to a new launch once it reads the id,
+        // so the two resets must be done first: wait for them (vmcnt counts
+        // them until they are performed), then store the id.  A release at
+        // system scope would order them too, but it writes back the whole
+        // L2 first, at the end of every launch.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        __hip_atomic_store(a.fin, a.launch_id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
 }
 
