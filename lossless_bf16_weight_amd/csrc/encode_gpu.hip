@@ -12,12 +12,17 @@
 //      from the total bit count sum(f * len), and the header;
 //   2. per-chunk bit counts, written where the chunk index goes;
 //   3. one workgroup turns them into start bits (the chunk index);
-//   4. one workgroup per chunk: every lane packs the codes of 128 consecutive
-//      elements into 32-bit words of the stream (whole words with plain
-//      stores, the two it may share with its neighbours with an atomic OR
-//      into the zeroed section), counts the codes that start in each of the
-//      chunk's 512 windows and the offset of each window's first code (in
-//      LDS), and writes the elements' raw bytes.
+//   4. one 512-lane workgroup per chunk: every lane packs the codes of 64
+//      consecutive elements into 32-bit words of the stream (whole words
+//      with plain stores, the two it may share with its neighbours with an
+//      atomic OR into the zeroed section), counts the codes that start in
+//      each of the chunk's 512 windows and the offset of each window's first
+//      code (in LDS), and writes the elements' raw bytes.  (512 lanes of 64
+//      elements measured 7% faster for the whole encoder than 256 of 128,
+//      and 3% faster than 1024 of 32.)
+//
+// Only the bytes no kernel writes are cleared first: the stream section
+// (packed with ORs) and the padding between and after the sections.
 //
 // Bound by HBM traffic: the words are read three times (2 bytes each) and
 // about 1.36 bytes per element are written.
@@ -46,7 +51,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #define GLOBAL __attribute__((address_space(1)))
 
 constexpr int kEncThreads = 256;
-constexpr int kPerLane = kChunk / kEncThreads;   // 128 elements per lane
+constexpr int kPackThreads = 512;                    // lanes per chunk in the packing kernel
+constexpr int kPerLane = kChunk / kPackThreads;      // 64 elements per packing lane
 constexpr int kHistCopies = 16;                  // LDS copies of the histogram (lane % 16 picks one)
 
 struct CodeTable {
@@ -114,18 +120,19 @@ __device__ __forceinline__ void for_each_word(const GLOBAL uint16_t *w, LaneRang
 
 // Exclusive prefix sum over the workgroup's 256 lanes (LDS, both buffers of
 // `s` used in turn); also returns the total.
-__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t (&s)[2][kEncThreads], uint32_t &total) {
+template <int N>
+__device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t (&s)[2][N], uint32_t &total) {
     const uint32_t tid = threadIdx.x;
     s[0][tid] = v;
     __syncthreads();
     int src = 0;
-    for (uint32_t d = 1; d < kEncThreads; d <<= 1) {
+    for (uint32_t d = 1; d < (uint32_t)N; d <<= 1) {
         const uint32_t x = s[src][tid] + (tid >= d ? s[src][tid - d] : 0u);
         s[src ^ 1][tid] = x;
         src ^= 1;
         __syncthreads();
     }
-    total = s[src][kEncThreads - 1];
+    total = s[src][N - 1];
     return s[src][tid] - v;
 }
 
@@ -229,18 +236,21 @@ struct LaneWords {
 };
 
 // 4. one chunk: codes into the stream, the window index, the raw bytes
-__global__ __launch_bounds__(kEncThreads) void enc_pack(PackArgs a, CodeTable T) {
+__global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T) {
     __shared__ uint32_t code[256];
     __shared__ uint8_t len[256];
     __shared__ uint32_t cnt[kWindows], gap[kWindows];
-    __shared__ uint32_t s[2][kEncThreads];
-    __shared__ uint8_t last_len[kEncThreads];
+    __shared__ uint32_t s[2][kPackThreads];
+    __shared__ uint8_t last_len[kPackThreads];
     const uint32_t tid = threadIdx.x;
     const uint64_t c = blockIdx.x;
-    code[tid] = T.code[tid];
-    len[tid] = T.len[tid];
-    cnt[tid] = cnt[tid + kEncThreads] = 0;
-    gap[tid] = gap[tid + kEncThreads] = 0;
+    if (tid < 256) {
+        code[tid] = T.code[tid];
+        len[tid] = T.len[tid];
+    }
+    static_assert(kPackThreads == kWindows, "one window entry per packing lane");
+    cnt[tid] = 0;
+    gap[tid] = 0;
     __syncthreads();
 
     const LaneRange r = lane_range(c, tid, a.n);
@@ -314,10 +324,13 @@ __global__ __launch_bounds__(kEncThreads) void enc_pack(PackArgs a, CodeTable T)
         if (r.m & 3) *reinterpret_cast<GLOBAL uint32_t *>(rb + (r.m & ~3u)) = acc;   // inside the 16-byte padding
     }
     __syncthreads();
-    // the 512 window entries, cnt | gap << kWinGapShift, two per lane
-    const uint32_t e0 = cnt[2 * tid] | (gap[2 * tid] << kWinGapShift);
-    const uint32_t e1 = cnt[2 * tid + 1] | (gap[2 * tid + 1] << kWinGapShift);
-    a.win[c * (kWindows / 2) + tid] = e0 | (e1 << 16);
+    // the 512 window entries, cnt | gap << kWinGapShift, two per lane of the
+    // first 256
+    if (tid < kWindows / 2) {
+        const uint32_t e0 = cnt[2 * tid] | (gap[2 * tid] << kWinGapShift);
+        const uint32_t e1 = cnt[2 * tid + 1] | (gap[2 * tid + 1] << kWinGapShift);
+        a.win[c * (kWindows / 2) + tid] = e0 | (e1 << 16);
+    }
 }
 
 // The 512-byte header, from a kernel argument (so that no host buffer has to
@@ -438,7 +451,19 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
         Header h;
         write_header(reinterpret_cast<uint8_t *>(h.w), n, ndims[t], dims + 8 * t, L, T.len);
         uint8_t *out = static_cast<uint8_t *>(d_outs[t]);
-        if ((e = hipMemsetAsync(out, 0, L.total, stream)) != hipSuccess) return hip_fail(who, e, "hipMemsetAsync");
+        // the kernels write the header, the chunk index, the window entries
+        // and the raw bytes (up to the dword holding element n - 1); clear the
+        // rest: the gaps after the chunk index and the window entries, the
+        // stream section (whose words are ORed together), and the raw
+        // section's tail padding
+        // (an empty tensor runs no kernel but the header's: all of it is cleared)
+        const uint64_t ci_end = n ? L.off_ci + (L.n_chunks + 1) * 16 : kHeader;
+        const uint64_t win_end = L.off_win + L.n_chunks * kWindows * 2;
+        const uint64_t raw_set = L.off_raw + (n & ~uint64_t(3));
+        if ((e = hipMemsetAsync(out + ci_end, 0, L.off_win - ci_end, stream)) != hipSuccess ||
+            (e = hipMemsetAsync(out + win_end, 0, L.off_raw - win_end, stream)) != hipSuccess ||
+            (e = hipMemsetAsync(out + raw_set, 0, L.total - raw_set, stream)) != hipSuccess)
+            return hip_fail(who, e, "hipMemsetAsync");
         hipLaunchKernelGGL(enc_header, dim3(1), dim3(kHeader / 4), 0, stream, h, (GLOBAL uint32_t *)out);
         if (n) {
             const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
@@ -447,7 +472,7 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
             hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n);
             PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
                         (GLOBAL uint8_t *)(out + L.off_raw)};
-            hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, pa, T);
+            hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kPackThreads), 0, stream, pa, T);
         }
         if ((e = hipGetLastError()) != hipSuccess) return hip_fail(who, e, "launch");
         out_bytes[t] = L.total;
