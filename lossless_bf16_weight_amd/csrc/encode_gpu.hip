@@ -7,10 +7,12 @@
 // makes compression time the cost to cut; here the element-wise passes run
 // on the GPU and only the 256-symbol code is built on the host:
 //
-//   1. histogram of the exponent byte (one read of the words);
+//   1. histogram of the exponent byte per chunk (one read of the words),
+//      kept where the chunk's window entries go later, and summed per tensor;
 //   -- the host builds the code (package-merge, canonical values), the layout
 //      from the total bit count sum(f * len), and the header;
-//   2. per-chunk bit counts, written where the chunk index goes;
+//   2. per-chunk bit counts from the chunk histograms, written where the
+//      chunk index goes;
 //   3. one workgroup turns them into start bits (the chunk index);
 //   4. one 512-lane workgroup per chunk: every lane packs the codes of 64
 //      consecutive elements into 32-bit words of the stream (whole words
@@ -24,8 +26,8 @@
 // Only the bytes no kernel writes are cleared first: the stream section
 // (packed with ORs) and the padding between and after the sections.
 //
-// Bound by HBM traffic: the words are read three times (2 bytes each) and
-// about 1.36 bytes per element are written.
+// Bound by HBM traffic: the words are read twice (2 bytes each) and about
+// 1.36 bytes per element are written.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,8 +70,11 @@ __device__ __forceinline__ uint32_t word_of(const u32x4 &v, int i) {
     return (i & 1) ? d >> 16 : d & 0xFFFFu;
 }
 
-// 1. exponent histogram (u32 counters per workgroup, summed into u64)
+// 1. exponent histogram, one workgroup per chunk: the chunk's 256 counts go
+// to chunk_hist (u32 each, in the space the chunk's window entries take
+// later) and are added into the tensor's u64 totals
 __global__ __launch_bounds__(kEncThreads) void enc_hist(const GLOBAL uint16_t *w, uint64_t n,
+                                                        GLOBAL uint32_t *chunk_hist,
                                                         GLOBAL unsigned long long *hist) {
     // (each copy is one entry longer than the 256 bins, so that the copies of
     // a bin fall in different LDS banks; one copy per lane measured slower)
@@ -77,19 +82,22 @@ __global__ __launch_bounds__(kEncThreads) void enc_hist(const GLOBAL uint16_t *w
     for (int i = threadIdx.x; i < kHistCopies * 257; i += kEncThreads) (&h[0][0])[i] = 0;
     __syncthreads();
     uint32_t *mine = h[threadIdx.x % kHistCopies];
-    const uint64_t stride = (uint64_t)gridDim.x * kEncThreads * 8;
-    for (uint64_t j = ((uint64_t)blockIdx.x * kEncThreads + threadIdx.x) * 8; j < n; j += stride) {
-        if (j + 8 <= n) {
+    const uint64_t c = blockIdx.x;
+    const uint64_t c0 = c * kChunk;
+    const uint64_t cend = min(n, c0 + kChunk);
+    for (uint64_t j = c0 + 8 * threadIdx.x; j < cend; j += 8 * kEncThreads) {
+        if (j + 8 <= cend) {
             const u32x4 v = *reinterpret_cast<const GLOBAL u32x4 *>(w + j);
 #pragma unroll
             for (int i = 0; i < 8; ++i) atomicAdd(&mine[(word_of(v, i) >> 7) & 0xFFu], 1u);
         } else {
-            for (uint64_t k = j; k < n; ++k) atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
+            for (uint64_t k = j; k < cend; ++k) atomicAdd(&mine[(w[k] >> 7) & 0xFFu], 1u);
         }
     }
     __syncthreads();
     uint32_t sum = 0;
-    for (int c = 0; c < kHistCopies; ++c) sum += h[(c + threadIdx.x) % kHistCopies][threadIdx.x];
+    for (int k = 0; k < kHistCopies; ++k) sum += h[(k + threadIdx.x) % kHistCopies][threadIdx.x];
+    chunk_hist[c * 256 + threadIdx.x] = sum;
     if (sum) __hip_atomic_fetch_add(&hist[threadIdx.x], (unsigned long long)sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -136,30 +144,17 @@ __device__ __forceinline__ uint32_t block_exclusive(uint32_t v, uint32_t (&s)[2]
     return s[src][tid] - v;
 }
 
-// 2. bits of each chunk, into the chunk index's start-bit slots
-__global__ __launch_bounds__(kEncThreads) void enc_chunk_bits(const GLOBAL uint16_t *w, uint64_t n, CodeTable T,
+// 2. bits of each chunk, into the chunk index's start-bit slots: the sum of
+// count x code length over the chunk's histogram (no second read of the
+// words)
+__global__ __launch_bounds__(kEncThreads) void enc_chunk_bits(const GLOBAL uint32_t *chunk_hist, CodeTable T,
                                                               GLOBAL uint64_t *ci) {
-    __shared__ uint8_t len[256];
     __shared__ uint32_t s[2][kEncThreads];
-    len[threadIdx.x] = T.len[threadIdx.x];
-    __syncthreads();
-    // (the order does not matter for a sum: each load instruction covers 4 KiB
-    // of consecutive words across the workgroup)
-    uint32_t bits = 0;
-    const uint64_t c0 = (uint64_t)blockIdx.x * kChunk;
-    const uint64_t cend = min(n, c0 + kChunk);
-    for (uint64_t j = c0 + 8 * threadIdx.x; j < cend; j += 8 * kEncThreads) {
-        if (j + 8 <= cend) {
-            const u32x4 v = *reinterpret_cast<const GLOBAL u32x4 *>(w + j);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bits += len[(word_of(v, i) >> 7) & 0xFFu];
-        } else {
-            for (uint64_t k = j; k < cend; ++k) bits += len[(w[k] >> 7) & 0xFFu];
-        }
-    }
+    const uint64_t c = blockIdx.x;
+    const uint32_t bits = chunk_hist[c * 256 + threadIdx.x] * (uint32_t)T.len[threadIdx.x];
     uint32_t total;
     block_exclusive(bits, s, total);
-    if (threadIdx.x == 0) ci[2 * (uint64_t)blockIdx.x] = total;
+    if (threadIdx.x == 0) ci[2 * c] = total;
 }
 
 // 3. start bits: exclusive prefix sum of the chunk bit counts, in place,
@@ -413,20 +408,27 @@ df11_status hip_fail(const char *who, hipError_t e, const char *what) {
 
 // 1. every tensor's exponent histogram into hist (256 counters per tensor,
 // cleared here), then back to the host (freq) in one copy; waits for it.
-hipError_t histograms(int n_tensors, const void *const *d_words, const uint64_t *n_elems,
-                      unsigned long long *hist, uint64_t *freq, int hip_device, hipStream_t stream) {
+// Where a tensor's per-chunk histograms wait between the histogram and the
+// chunk bits: the container's window section, n_chunks x 1 KiB (the packing
+// overwrites it), whose offset depends on the element count only.
+GLOBAL uint32_t *chunk_hist_of(void *d_out, uint64_t n) {
+    const EncodeLayout L = encode_layout(n, 0);
+    return (GLOBAL uint32_t *)(static_cast<uint8_t *>(d_out) + L.off_win);
+}
+static_assert(kWindows * 2 == 256 * sizeof(uint32_t), "a chunk's histogram fills its window entries");
+
+hipError_t histograms(int n_tensors, const void *const *d_words, const uint64_t *n_elems, void *const *d_outs,
+                      unsigned long long *hist, uint64_t *freq, hipStream_t stream) {
     const uint64_t n_ctr = (uint64_t)n_tensors * 256;
     hipLaunchKernelGGL(enc_clear, dim3((unsigned)((n_ctr + kEncThreads - 1) / kEncThreads)), dim3(kEncThreads), 0,
                        stream, (GLOBAL unsigned long long *)hist, n_ctr);
     hipError_t e = hipGetLastError();
-    int n_cu = 0;
-    (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device);
     for (int t = 0; t < n_tensors && e == hipSuccess; ++t) {
         if (!n_elems[t]) continue;
-        const uint64_t need = (n_elems[t] + kEncThreads * 8 - 1) / (kEncThreads * 8);
-        const int grid = (int)std::min<uint64_t>(need, (uint64_t)std::max(1, n_cu) * 8);
-        hipLaunchKernelGGL(enc_hist, dim3(grid), dim3(kEncThreads), 0, stream, (const GLOBAL uint16_t *)d_words[t],
-                           n_elems[t], (GLOBAL unsigned long long *)(hist + 256 * (size_t)t));
+        const uint64_t n_chunks = (n_elems[t] + kChunk - 1) / kChunk;
+        hipLaunchKernelGGL(enc_hist, dim3((unsigned)n_chunks), dim3(kEncThreads), 0, stream,
+                           (const GLOBAL uint16_t *)d_words[t], n_elems[t], chunk_hist_of(d_outs[t], n_elems[t]),
+                           (GLOBAL unsigned long long *)(hist + 256 * (size_t)t));
         e = hipGetLastError();
     }
     if (e == hipSuccess) e = hipMemcpyAsync(freq, hist, n_ctr * sizeof(unsigned long long), hipMemcpyDeviceToHost, stream);
@@ -468,7 +470,8 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
         if (n) {
             const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
             GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
-            hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream, w, n, T, ci);
+            hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream,
+                               (const GLOBAL uint32_t *)chunk_hist_of(out, n), T, ci);
             hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n);
             PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
                         (GLOBAL uint8_t *)(out + L.off_raw)};
@@ -499,7 +502,7 @@ extern "C" df11_status df11_encode_device_batch(int n_tensors, const void *const
     unsigned long long *hist = nullptr;
     hipError_t e = hipMallocAsync((void **)&hist, (size_t)n_tensors * 256 * sizeof(unsigned long long), stream);
     if (e != hipSuccess) return hip_fail(who, e, "hipMallocAsync");
-    e = histograms(n_tensors, d_words, n_elems, hist, freq.data(), hip_device, stream);
+    e = histograms(n_tensors, d_words, n_elems, d_outs, hist, freq.data(), stream);
     const hipError_t ef = hipFreeAsync(hist, stream);
     if (e != hipSuccess) return hip_fail(who, e, "histogram");
     if (ef != hipSuccess) return hip_fail(who, ef, "hipFreeAsync");
@@ -525,7 +528,7 @@ extern "C" df11_status df11_encode_device_batch_noalloc(int n_tensors, const voi
     unsigned long long *hist = nullptr;
     hipError_t e = scratch_on(hip_device, &hist);
     if (e != hipSuccess) return hip_fail(who, e, "hipGetSymbolAddress");
-    if ((e = histograms(n_tensors, d_words, n_elems, hist, g_freq, hip_device, stream)) != hipSuccess)
+    if ((e = histograms(n_tensors, d_words, n_elems, d_outs, hist, g_freq, stream)) != hipSuccess)
         return hip_fail(who, e, "histogram");
     return pack_batch(who, n_tensors, d_words, n_elems, ndims, dims, d_outs, out_bytes, g_freq, stream);
 }
