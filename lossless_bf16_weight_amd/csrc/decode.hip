@@ -36,8 +36,8 @@
 //      first code starts (or at the chunk end); otherwise the plan's flag is
 //      set;
 //   5. assemble: per 2048 elements, each lane joins 8 tile bytes with 8 raw
-//      bytes into BF16 words (two byte permutes and one bitfield insert per
-//      two words) and writes them with one 16-byte store, contiguous across
+//      bytes into BF16 words (two bitfield inserts and two byte permutes
+//      per four words) and writes them with one 16-byte store, contiguous across
 //      the wave (1 KiB per store instruction); the next chunk's code bytes,
 //      tables and raw bytes are requested meanwhile.
 //
@@ -55,12 +55,13 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kTileBytes = kChunk;                 // one exponent byte per element
 constexpr uint32_t kTilePadded = kTileBytes + kTileBytes / 32;   // 4 pad bytes per 128
 // LDS per workgroup: 13 KiB staged codes + 33 KiB tile + 5.8 KiB tables +
-// 160 bytes of records and wave totals = 52 KiB, so that three workgroups
+// tickets and wave totals = 52 KiB, so that three workgroups
 // fit in a compute unit's 160 KiB.
 constexpr int kCodeWords = kCodeCap / 4;
 constexpr int kCodeLoads = (kCodeCap + 16 * kThreads - 1) / (16 * kThreads);
 constexpr int kBlockElems = 8 * kThreads;          // elements per store block
 constexpr int kBlocks = kChunk / kBlockElems;
+static_assert(kBlockElems == 2048 && kThreads == 256, "block tile stride 2112");
 static_assert(2 * kThreads == kWindows, "two windows per lane");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -76,6 +77,17 @@ __device__ __forceinline__ GLOBAL T *global(T *p) {
     return (GLOBAL T *)p;
 }
 
+// A pointer that is the same for all lanes, made a scalar value, so that an
+// access through it plus a lane offset uses the scalar base + vector offset
+// address form (no 64-bit vector address per access).
+template <class T>
+__device__ __forceinline__ GLOBAL T *uniform(GLOBAL T *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (GLOBAL T *)((uint64_t)hi << 32 | lo);
+}
+
 // LDS of one workgroup.  Staged code word k (first stream bit lowest) sits
 // in codes[k + 1], with codes[1] 16-byte aligned; the 12 bytes in front keep
 // codes[0] inside the struct.  The tile's and the tables' bases fold into
@@ -85,10 +97,8 @@ struct Lds {
     uint32_t codes[kCodeWords + 9];   // 12 + 4 * (kCodeWords + 9) = 0 mod 16
     uint8_t tile[kTilePadded + 16];
     LutRecord lut;
-    // the chunk records of the current and the next work item (slot =
-    // iteration parity), copied in by wave 0 before the assembly, and their item
-    // numbers (n_items or more: no item; the record is then item n_items-1's)
-    uint32_t rec[2][16];
+    // the next work item's ticket (slot = iteration parity), written by wave
+    // 0 before the barrier that ends the decode (n_items or more: no item)
     uint32_t rec_id[2];
     // per wave: bit offset from the chunk start of the first code of its
     // first non-empty window (~0: all its windows are empty), and the number
@@ -96,7 +106,7 @@ struct Lds {
     uint32_t wave_first[kWaves];
     uint32_t wave_total[kWaves];
 };
-static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0 && offsetof(Lds, rec) % 16 == 0,
+static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0,
               "LDS alignment");
 static_assert(sizeof(Lds) <= 53248, "three workgroups per compute unit");
 
@@ -122,21 +132,18 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
     return x;
 }
 
-// Two BF16 words from two rotated exponent bytes (t) and two raw bytes (r):
-// word = [r & 0x80 | t & 0x7F] [t & 0x80 | r & 0x7F].
-__device__ __forceinline__ uint32_t join2(uint32_t t, uint32_t r, uint32_t sel_p, uint32_t sel_q) {
-    const uint32_t p = __builtin_amdgcn_perm(t, r, sel_p);   // [r1 t1 r0 t0]
-    const uint32_t q = __builtin_amdgcn_perm(t, r, sel_q);   // [t1 r1 t0 r0]
-    return (p & 0x80808080u) | (q & 0x7F7F7F7Fu);
+// Four BF16 words from four rotated exponent bytes t and four raw bytes r:
+// the high bytes (sign | e >> 1) and the low bytes (e & 1 | fraction) of all
+// four with one bitfield insert each, then interleaved by two byte permutes.
+__device__ __forceinline__ u32x2 join4(uint32_t t, uint32_t r) {
+    const uint32_t hi = (r & 0x80808080u) | (t & 0x7F7F7F7Fu);
+    const uint32_t lo = (t & 0x80808080u) | (r & 0x7F7F7F7Fu);
+    return u32x2{__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u)};
 }
 
 __device__ __forceinline__ u32x4 join8(u32x2 t8, u32x2 r8) {
-    u32x4 o;
-    o.x = join2(t8.x, r8.x, 0x01050004u, 0x05010400u);
-    o.y = join2(t8.x, r8.x, 0x03070206u, 0x07030602u);
-    o.z = join2(t8.y, r8.y, 0x01050004u, 0x05010400u);
-    o.w = join2(t8.y, r8.y, 0x03070206u, 0x07030602u);
-    return o;
+    const u32x2 a = join4(t8.x, r8.x), b = join4(t8.y, r8.y);
+    return u32x4{a.x, a.y, b.x, b.y};
 }
 
 // ---- code sources ---------------------------------------------------------
@@ -325,11 +332,12 @@ __device__ __forceinline__ uint32_t trailing_bits(const Lds &L, uint32_t ent, ui
 // word together) instead of two in a row.
 struct Window {
     uint32_t w0, w1;
+    uint32_t kb;   // 4 (P / 32): byte offset of word k from codes[0]
 };
 
 __device__ __forceinline__ Window window_at(const uint32_t *w, uint32_t P) {
     const uint32_t k = P >> 5;
-    return Window{w[k], w[k + 1]};
+    return Window{w[k], w[k + 1], (P >> 3) & ~3u};
 }
 
 // One counted look-up of both chains from their register windows.
@@ -340,13 +348,19 @@ __device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &
     const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
     uint32_t ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
     uint32_t eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
-    const uint32_t na = L.codes[(A.P >> 5) + 2];
-    const uint32_t nb = L.codes[(B.P >> 5) + 2];
+    const uint8_t *cw = reinterpret_cast<const uint8_t *>(L.codes);
+    const uint32_t na = *reinterpret_cast<const uint32_t *>(cw + wa.kb + 8);
+    const uint32_t nb = *reinterpret_cast<const uint32_t *>(cw + wb.kb + 8);
     __builtin_amdgcn_sched_barrier(0);
     if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
-    // a look-up takes fewer than 32 bits, so it moves a chain at most one word
-    const bool ca = (A.P | 31u) < A.P + ent_bits(ea);
-    const bool cb = (B.P | 31u) < B.P + ent_bits(eb);
+    // a look-up takes fewer than 32 bits, so it moves a chain at most one
+    // word: it does when the new position's word offset differs
+    const uint32_t ka = ((A.P + ent_bits(ea)) >> 3) & ~3u;
+    const uint32_t kb = ((B.P + ent_bits(eb)) >> 3) & ~3u;
+    const bool ca = ka != wa.kb;
+    const bool cb = kb != wb.kb;
+    wa.kb = ka;
+    wb.kb = kb;
     wa.w0 = ca ? wa.w1 : wa.w0;
     wa.w1 = ca ? na : wa.w1;
     wb.w0 = cb ? wb.w1 : wb.w0;
@@ -409,7 +423,12 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
         Window wa = window_at(src.w, A.P), wb = window_at(src.w, B.P);
         // (the loop then starts with no LDS read in flight)
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        for (uint32_t t = 0; t < T; ++t) window_step(L, A, B, wa, wb, bad);
+        uint32_t t = 0;
+        for (; t + 1 < T; t += 2) {
+            window_step(L, A, B, wa, wb, bad);
+            window_step(L, A, B, wa, wb, bad);
+        }
+        if (t < T) window_step(L, A, B, wa, wb, bad);
         ra = (int32_t)(A.qe - out_pos(A));
         rb = (int32_t)(B.qe - out_pos(B));
         masked_window_tail(L, src.pmax >> 5, A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
@@ -459,23 +478,14 @@ struct Item {
     uint32_t lut;            // plan tensor index
 };
 
-// A chunk record from its LDS slot: every field is the same for all lanes
-// (the reads broadcast), and goes to a scalar register.
-__device__ __forceinline__ Item item_at(const DecodeArgs &a, const Lds &L, uint32_t slot) {
-    const u32x4 *q = reinterpret_cast<const u32x4 *>(L.rec[slot]);
-    uint32_t f[16];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const u32x4 v = q[k];
-        f[4 * k + 0] = __builtin_amdgcn_readfirstlane(v.x);
-        f[4 * k + 1] = __builtin_amdgcn_readfirstlane(v.y);
-        f[4 * k + 2] = __builtin_amdgcn_readfirstlane(v.z);
-        f[4 * k + 3] = __builtin_amdgcn_readfirstlane(v.w);
-    }
-    // fields in ChunkRec order
-    const uint64_t stream_off = f[0] | (uint64_t)f[1] << 32, raw_off = f[2] | (uint64_t)f[3] << 32;
-    const uint64_t win_off = f[4] | (uint64_t)f[5] << 32;
-    const uint32_t tensor = f[14], chunk = f[15];
+// A chunk record (id is the same for all lanes): one scalar load of its 64
+// bytes through the constant address space, so every field is in a scalar
+// register and no workgroup barrier is needed to share it.
+#define CONSTANT __attribute__((address_space(4)))
+__device__ __forceinline__ Item item_at(const DecodeArgs &a, uint32_t id) {
+    const CONSTANT ChunkRec *r = (const CONSTANT ChunkRec *)a.recs + id;
+    const uint64_t stream_off = r->stream_off, raw_off = r->raw_off, win_off = r->win_off;
+    const uint32_t tensor = r->tensor, chunk = r->chunk;
     const uint32_t tl = tensor - a.tensor_base;
     const GLOBAL uint8_t *C = global(a.containers[tl]);
     Item it;
@@ -483,27 +493,18 @@ __device__ __forceinline__ Item item_at(const DecodeArgs &a, const Lds &L, uint3
     it.raw = C + raw_off;
     it.win = C + win_off;
     it.out = global(a.outs[tl]) + (uint64_t)chunk * kChunk;
-    it.rel0 = f[8];
-    it.nbits = f[9];
-    it.s_len = f[10] & ~kStagedBit;
-    it.staged = f[10] >> 31;
-    it.nc = f[11];
-    it.raw_left = f[12];
-    it.n_words = f[13];
+    it.rel0 = r->rel0;
+    it.nbits = r->nbits;
+    const uint32_t sl = r->s_len;
+    it.s_len = sl & ~kStagedBit;
+    it.staged = sl >> 31;
+    it.nc = r->nc;
+    it.raw_left = r->raw_left;
+    it.n_words = r->n_words;
     it.lut = tensor;
     return it;
 }
 static_assert(offsetof(ChunkRec, rel0) == 32 && offsetof(ChunkRec, tensor) == 56, "record layout");
-
-// Wave 0 fetches a chunk record (lanes 0..3: 16 bytes each) ...
-__device__ __forceinline__ u32x4 fetch_rec(const DecodeArgs &a, uint32_t item, uint32_t lane) {
-    return reinterpret_cast<const GLOBAL u32x4 *>(global(a.recs) + item)[lane & 3u];
-}
-// ... and later puts it in its LDS slot.
-__device__ __forceinline__ void put_rec(Lds &L, uint32_t slot, u32x4 v, uint32_t id, uint32_t lane) {
-    if (lane < 4u) reinterpret_cast<u32x4 *>(L.rec[slot])[lane] = v;
-    if (lane == 0) L.rec_id[slot] = id;
-}
 
 // Wave 0: the next ticket of the launch (lane 0 takes it, every lane gets
 // it).  Tickets count on from gridDim.x: workgroup w's first item is w.
@@ -545,10 +546,17 @@ __device__ __forceinline__ void load_codes(const Item &it, uint32_t tid, u32x4 (
 // Raw bytes of store block b (elements 2048b + 8 tid .. +8) of an item; a
 // partial chunk reads inside its (16-byte padded) raw bytes only.
 __device__ __forceinline__ u32x2 load_raw(const Item &it, uint32_t tid, int b) {
-    uint32_t j = kBlockElems * b + 8u * tid;
-    if (it.nc != (uint32_t)kChunk) j = min(j, (it.raw_left - 8u) & ~7u);
+    // a block base shared by the wave and a lane offset, both clamped for a
+    // partial chunk to the last whole 8 bytes
+    uint32_t base = kBlockElems * b, lim = ~0u;
+    if (it.nc != (uint32_t)kChunk) {
+        const uint32_t last = (it.raw_left - 8u) & ~7u;
+        base = min(base, last);
+        lim = last - base;
+    }
+    const GLOBAL uint8_t *rb = uniform(it.raw + base);
     // (a plain load: the non-temporal hint measured about 8% slower here)
-    return *reinterpret_cast<const GLOBAL u32x2 *>(it.raw + j);
+    return *reinterpret_cast<const GLOBAL u32x2 *>(rb + min(8u * tid, lim));
 }
 
 // The index entries of this lane's windows 2 tid (low half) and 2 tid + 1
@@ -574,20 +582,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     u32x2 rw[kBlocks];
     u32x4 lr[kLutLoads];
     uint32_t win;
-    // the second item's ticket, taken at once (its round trip overlaps the
-    // first record's): at the end of the first decode every workgroup would
-    // otherwise wait for the ticket counter at the same time
-    if (wave == 0) {
-        const uint32_t i0 = blockIdx.x;
-        const u32x4 r0 = fetch_rec(a, min(i0, n - 1), lane);
-        put_rec(L, 0, r0, i0, lane);
-    }
-    __syncthreads();
+    // The current item (the first is the workgroup's number).  Every wave
+    // reads an item's record itself, with one scalar load, so records need
+    // no LDS slot and no barrier of their own.
+    uint32_t cur = blockIdx.x;
     {
         // (in the order the loop issues them: windows, codes, tables, raw
         // bytes; the compiler's wait counts assume the same order on every
         // path)
-        const Item it = item_at(a, L, 0);
+        const Item it = item_at(a, min(cur, n - 1));
         win = load_windows(it, tid);
         load_codes(it, tid, cw);
         load_lut(a, it.lut, tid, lr);
@@ -603,22 +606,25 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
 
     for (uint32_t k = 0;; ++k) {
         // ---- the previous item's tile and staged words are no longer
-        //      read; this item's record and tables are in LDS
+        //      read; this item's tables are in LDS
         __syncthreads();
         const uint32_t sl = k & 1u;
-        if (__builtin_amdgcn_readfirstlane(L.rec_id[sl]) >= n) break;
+        if (cur >= n) break;
         // The next chunk's ticket is taken once this chunk is decoded, so
         // that at the end of the launch no workgroup holds a chunk in reserve
         // while others have run out (about 3% faster than taking it one chunk
         // ahead); only a workgroup's first chunk takes it before decoding,
-        // when every workgroup would otherwise wait for it at once.  (A
-        // ticket of n or above: no item; its record is then item n-1's, so
-        // that the next item's loads stay unconditional and the compiler can
-        // count them and wait for the oldest ones only.)
+        // when every workgroup would otherwise wait for it at once.  Wave 0
+        // takes it and leaves it in LDS for the barrier that ends the decode.
+        // (A ticket of n or above: no item; the next item's loads then read
+        // item n-1's bytes, so that they stay unconditional and the compiler
+        // can count them and wait for the oldest ones only.)
         const bool late = k != 0;
-        const Item it = item_at(a, L, sl);
-        uint32_t t1 = n;
-        if (wave == 0 && !late) t1 = take_ticket(a, lane);
+        const Item it = item_at(a, cur);
+        if (wave == 0 && !late) {
+            const uint32_t t1 = take_ticket(a, lane);
+            if (lane == 0) L.rec_id[sl ^ 1u] = t1;
+        }
 
         // ---- the tile cleared (the decode ORs its bytes in), and the staged
         //      words to LDS
@@ -655,8 +661,6 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         if (lane == 0) L.wave_first[wave] = mask ? wf : 0xFFFFFFFFu;
         __syncthreads();
 
-        u32x4 r1;
-        if (wave == 0 && !late) r1 = fetch_rec(a, min(t1, n - 1), lane);
         uint32_t base = 0;
         for (uint32_t w = 0; w < wave; ++w) base += L.wave_total[w];
         const uint32_t qa = base + incl - na - nb;
@@ -699,14 +703,13 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         }
         const uint32_t ea = A.P - kPosBias;
         const uint32_t eb = B.P - kPosBias;
-        if (wave == 0 && !late) put_rec(L, sl ^ 1u, r1, t1, lane);
         // (the ticket's round trip overlaps the wait for the other waves)
-        if (wave == 0 && late) t1 = take_ticket(a, lane);
-        __syncthreads();
-        if (late) {
-            if (wave == 0) put_rec(L, sl ^ 1u, fetch_rec(a, min(t1, n - 1), lane), t1, lane);
-            __syncthreads();
+        if (wave == 0 && late) {
+            const uint32_t t1 = take_ticket(a, lane);
+            if (lane == 0) L.rec_id[sl ^ 1u] = t1;
         }
+        __syncthreads();
+        const uint32_t nid = __builtin_amdgcn_readfirstlane(L.rec_id[sl ^ 1u]);
 
         // ---- every non-empty window ends where the next non-empty window's
         //      first code starts; the last one at the chunk end
@@ -740,20 +743,23 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // that the compute unit's other waves' decodes do not hold back its
         // loads and stores; about 1% faster)
         __builtin_amdgcn_s_setprio(3);
-        const Item nx = item_at(a, L, sl ^ 1u);
+        const Item nx = item_at(a, min(nid, n - 1));
         const uint32_t win_nx = load_windows(nx, tid);
         load_codes(nx, tid, cw);
         load_lut(a, nx.lut, tid, lr);
         GLOBAL uint16_t *o = it.out;
         const uint32_t full = nc / kBlockElems;
-        // lanes whose first dword opens a 32-dword group (tid % 16 == 0)
+        // the tile offset of this lane's two dwords in block 0; block b's are
+        // tile_off(512 b + 2 tid) = 2112 b + that
+        const uint32_t tb0 = tile_off(2u * tid);
         const uint32_t pad_mask = (tid & 15u) ? 0u : ~0u;
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
-                const uint32_t j = kBlockElems * b + 8 * tid;
-                const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
-                __builtin_nontemporal_store(join8(t8, rw[b]), reinterpret_cast<GLOBAL u32x4 *>(o + j));
+                const uint32_t *tp = reinterpret_cast<const uint32_t *>(L.tile + tb0 + 2112u * b);
+                const u32x2 t8{tp[0], tp[1]};
+                GLOBAL u32x4 *ob = uniform(reinterpret_cast<GLOBAL u32x4 *>(o + kBlockElems * b));
+                __builtin_nontemporal_store(join8(t8, rw[b]), ob + tid);
             }
             rw[b] = load_raw(nx, tid, b);
         }
@@ -777,6 +783,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // the next item's tables (nothing reads them during the assembly)
         put_lut(L, tid, lr);
         win = win_nx;
+        cur = nid;
         __builtin_amdgcn_s_setprio(0);
     }
     if (__ballot(bad_any) && lane == 0) atomicOr(a.status, 1u);

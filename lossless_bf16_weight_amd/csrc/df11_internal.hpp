@@ -23,8 +23,8 @@ static_assert((24u * kChunk + kWindows - 1) / kWindows <= kWinCntMask, "window c
 // Exponent bytes are handled rotated right by one bit inside the decoder,
 // rot(e) = (e >> 1) | (e & 1) << 7, so that a BF16 word splits into the two
 // bytes [sign | e >> 1] and [e & 1 | fraction]: the decode tables hold rot(e)
-// and the join of tile bytes with raw bytes is two byte permutes and one
-// bitfield insert per pair of words.
+// and the join of tile bytes with raw bytes is two bitfield inserts and two
+// byte permutes per four words.
 #if defined(__HIPCC__)
 #define DF11_HD __host__ __device__
 #else
