@@ -8,38 +8,41 @@
 // One workgroup = four wave64s (256 lanes) decodes whole chunks of 32768
 // elements (64 KiB of BF16 output), one after the other; a launch's
 // workgroups take its chunks from a ticket counter as they finish decoding
-// the previous one.  Per chunk:
+// the previous one.  A chunk takes two workgroup barriers: one before its
+// decode, one after.  Per chunk:
 //
-//   1. stage: the tile is cleared; the chunk's code bytes, requested with
-//      coalesced 16-byte loads while the previous chunk was assembled, go
-//      to LDS as 32-bit words with the stream's first bit lowest; the
-//      chunk's raw bytes wait in registers (8 bytes per lane per 2048
-//      elements) until step 4;
-//   2. index: the chunk's N bits form 512 windows (window i starts
+//   1. index: the chunk's N bits form 512 windows (window i starts
 //      floor(i*N/512) bits in); lane i takes windows 2i and 2i+1.  A DPP
 //      prefix sum over each wave's lane totals of the window code counts,
-//      plus the totals of the waves below (through LDS), gives each window
-//      the chunk position of its first code;
-//   3. decode: each lane walks its two windows side by side (two
+//      plus the totals of the waves below (through LDS, written at the end
+//      of the previous chunk's assembly), gives each window the chunk
+//      position of its first code;
+//   2. decode: each lane walks its two windows side by side (two
 //      independent dependency chains; 512 chains per workgroup).  A chain
 //      keeps the two code words around its position in registers; a
 //      look-up funnel-shifts them, reads one first-level table entry (up to
 //      three codes of <= 10 bits; codes of 11..16 bits use a subtable the
-//      entry names, longer ones the canonical limits) together with the next code
-//      word, and ORs the exponent bytes (rotated, see rot_exp) into a 32 KiB
-//      LDS tile at their chunk positions.  A counted loop with no per-lane
-//      control flow runs while no window of the wave can run out (each
-//      look-up takes at most three codes) and no peek can pass the end of
-//      the staged words (each moves a window at most 24 bits); a masked
-//      loop finishes;
-//   4. check: a window must end exactly where the next non-empty window's
+//      entry names, longer ones the canonical limits) together with the next
+//      code word, and ORs the exponent bytes (rotated, see rot_exp) into a
+//      32 KiB LDS tile, zero beforehand, at their chunk positions.  A counted
+//      loop with no per-lane control flow runs while no window of the wave
+//      can run out before its last counted look-up (each look-up takes at
+//      most three codes) and no peek can pass the end of the staged words
+//      (each moves a window at most 24 bits); a masked loop finishes;
+//   3. check: a window must end exactly where the next non-empty window's
 //      first code starts (or at the chunk end); otherwise the plan's flag is
 //      set;
-//   5. assemble: per 2048 elements, each lane joins 8 tile bytes with 8 raw
-//      bytes into BF16 words (two bitfield inserts and two byte permutes
-//      per four words) and writes them with one 16-byte store, contiguous across
-//      the wave (1 KiB per store instruction); the next chunk's code bytes,
-//      tables and raw bytes are requested meanwhile.
+//   4. assemble: per 2048 elements, each lane joins 8 tile bytes with 8 raw
+//      bytes into BF16 words (two bitfield inserts and two byte permutes per
+//      four words), writes them with one 16-byte store, contiguous across the
+//      wave (1 KiB per store instruction), and clears the tile bytes it read;
+//      the next chunk's window entries, code bytes, tables and raw bytes are
+//      requested meanwhile;
+//   5. stage: at the end of its assembly each wave puts the next chunk's
+//      code bytes in LDS as 32-bit words with the stream's first bit lowest,
+//      writes its tables, and scans its windows (step 1 for the next chunk).
+//      The raw bytes wait in registers (8 bytes per lane per 2048 elements)
+//      until that chunk's assembly.
 //
 // There is no matrix arithmetic here: the path is bound by HBM traffic
 // (about 1.37 bytes read and 2 bytes written per element), with the look-up
@@ -103,8 +106,8 @@ struct Lds {
     // per wave: bit offset from the chunk start of the first code of its
     // first non-empty window (~0: all its windows are empty), and the number
     // of codes its windows hold
-    uint32_t wave_first[kWaves];
-    uint32_t wave_total[kWaves];
+    uint32_t wave_first[2][kWaves];
+    uint32_t wave_total[2][kWaves];
 };
 static_assert(offsetof(Lds, tile) % 16 == 0 && offsetof(Lds, lut) % 16 == 0,
               "LDS alignment");
@@ -342,7 +345,7 @@ __device__ __forceinline__ Window window_at(const uint32_t *w, uint32_t P) {
 
 // One counted look-up of both chains from their register windows.
 __device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &wa, Window &wb,
-                                            uint32_t &bad) {
+                                            uint32_t &bad, uint32_t &ea_o, uint32_t &eb_o) {
     const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
     const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
     const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
@@ -367,48 +370,69 @@ __device__ __forceinline__ void window_step(Lds &L, Chain &A, Chain &B, Window &
     wb.w1 = cb ? nb : wb.w1;
     step(L, A, ea);
     step(L, B, eb);
+    ea_o = ea;
+    eb_o = eb;
 }
 
-// The masked phase from register windows: as window_step, for the chains
-// whose windows still have codes (the others take a zero entry and keep
-// their state).  The next-word reads are clamped to the staged words, so a
-// container whose index disagrees with its stream reads inside them.
-__device__ __forceinline__ void masked_window_tail(Lds &L, uint32_t kmax, Chain &A, Chain &B, Window &wa,
+// One look-up of the masked phase from register windows: as window_step,
+// for the chains whose windows still have codes (aa / ab; the others take a
+// zero entry and keep their state).  The next-word reads are clamped to the
+// staged words, so a container whose index disagrees with its stream reads
+// inside them.  aa / ab come back for the next look-up.
+__device__ __forceinline__ void masked_window_step(Lds &L, uint32_t kmax4, Chain &A, Chain &B, Window &wa,
+                                                   Window &wb, int32_t &ra, int32_t &rb, uint32_t &ea_r,
+                                                   uint32_t &eb_r, uint32_t &bad, bool &aa, bool &ab) {
+    const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
+    const uint8_t *cw = reinterpret_cast<const uint8_t *>(L.codes);
+    const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
+    const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
+    uint32_t ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
+    uint32_t eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
+    const uint32_t na = *reinterpret_cast<const uint32_t *>(cw + min(wa.kb, kmax4) + 8);
+    const uint32_t nb = *reinterpret_cast<const uint32_t *>(cw + min(wb.kb, kmax4) + 8);
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
+    ea = aa ? ea : 0u;
+    eb = ab ? eb : 0u;
+    ea_r = aa ? ea : ea_r;
+    eb_r = ab ? eb : eb_r;
+    ra -= (int32_t)ent_count(ea);
+    rb -= (int32_t)ent_count(eb);
+    const uint32_t ka = ((A.P + ent_bits(ea)) >> 3) & ~3u;
+    const uint32_t kb = ((B.P + ent_bits(eb)) >> 3) & ~3u;
+    const bool ca = ka != wa.kb;
+    const bool cb = kb != wb.kb;
+    wa.kb = ka;
+    wb.kb = kb;
+    wa.w0 = ca ? wa.w1 : wa.w0;
+    wa.w1 = ca ? na : wa.w1;
+    wb.w0 = cb ? wb.w1 : wb.w0;
+    wb.w1 = cb ? nb : wb.w1;
+    step(L, A, ea);
+    step(L, B, eb);
+    aa = ra > 0;
+    ab = rb > 0;
+}
+
+// The masked phase: look-ups while any window of the wave has codes left
+// (two per loop iteration, so that the loop-carried registers need no
+// copies).
+__device__ __forceinline__ void masked_window_tail(Lds &L, uint32_t kmax4, Chain &A, Chain &B, Window &wa,
                                                    Window &wb, int32_t &ra, int32_t &rb, uint32_t &ea_r,
                                                    uint32_t &eb_r, uint32_t &bad) {
-    const uint8_t *l1 = reinterpret_cast<const uint8_t *>(L.lut.l1);
-    bool any = __ballot((ra > 0) | (rb > 0)) != 0;
-    while (any) {
-        const bool aa = ra > 0, ab = rb > 0;
-        const uint32_t ta = __builtin_amdgcn_alignbit(wa.w1, wa.w0, A.P);
-        const uint32_t tb = __builtin_amdgcn_alignbit(wb.w1, wb.w0, B.P);
-        uint32_t ea = *reinterpret_cast<const uint32_t *>(l1 + (ta & ((kL1Size - 1) << 2)));
-        uint32_t eb = *reinterpret_cast<const uint32_t *>(l1 + (tb & ((kL1Size - 1) << 2)));
-        const uint32_t na = L.codes[min(A.P >> 5, kmax) + 2];
-        const uint32_t nb = L.codes[min(B.P >> 5, kmax) + 2];
-        __builtin_amdgcn_sched_barrier(0);
-        if (__builtin_expect(is_long(ea) | is_long(eb), 0)) long_pair(L.lut, ta, tb, ea, eb, bad);
-        ea = aa ? ea : 0u;
-        eb = ab ? eb : 0u;
-        ea_r = aa ? ea : ea_r;
-        eb_r = ab ? eb : eb_r;
-        ra -= (int32_t)ent_count(ea);
-        rb -= (int32_t)ent_count(eb);
-        const bool ca = (A.P | 31u) < A.P + ent_bits(ea);
-        const bool cb = (B.P | 31u) < B.P + ent_bits(eb);
-        wa.w0 = ca ? wa.w1 : wa.w0;
-        wa.w1 = ca ? na : wa.w1;
-        wb.w0 = cb ? wb.w1 : wb.w0;
-        wb.w1 = cb ? nb : wb.w1;
-        step(L, A, ea);
-        step(L, B, eb);
-        any = __ballot((ra > 0) | (rb > 0)) != 0;
-    }
+    bool aa = ra > 0, ab = rb > 0;
+    if (__ballot(aa | ab) == 0) return;
+    do {
+        masked_window_step(L, kmax4, A, B, wa, wb, ra, rb, ea_r, eb_r, bad, aa, ab);
+        if (__ballot(aa | ab) == 0) break;
+        masked_window_step(L, kmax4, A, B, wa, wb, ra, rb, ea_r, eb_r, bad, aa, ab);
+    } while (__ballot(aa | ab) != 0);
 }
 
-// Decode both windows of this lane.  T: look-ups after which no window of
-// the wave has run out of codes.  On return A.P / B.P hold the stream
-// positions (plus kPosBias) where the windows' last codes end.
+// Decode both windows of this lane.  T: look-ups before whose last one no
+// window of the wave has run out of codes (codes in global memory: after
+// whose last one).  On return A.P / B.P hold the stream positions (plus
+// kPosBias) where the windows' last codes end.
 template <class Src>
 __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Chain &B, uint32_t T,
                                             uint32_t &bad) {
@@ -425,13 +449,15 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
         __builtin_amdgcn_s_waitcnt(0xC07F);
         uint32_t t = 0;
         for (; t + 1 < T; t += 2) {
-            window_step(L, A, B, wa, wb, bad);
-            window_step(L, A, B, wa, wb, bad);
+            window_step(L, A, B, wa, wb, bad, ea_r, eb_r);
+            window_step(L, A, B, wa, wb, bad, ea_r, eb_r);
         }
-        if (t < T) window_step(L, A, B, wa, wb, bad);
+        if (t < T) window_step(L, A, B, wa, wb, bad, ea_r, eb_r);
+        // (a window may have run out during the last counted look-up: its
+        // last entry is then that look-up's)
         ra = (int32_t)(A.qe - out_pos(A));
         rb = (int32_t)(B.qe - out_pos(B));
-        masked_window_tail(L, src.pmax >> 5, A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
+        masked_window_tail(L, 4u * (src.pmax >> 5), A, B, wa, wb, ra, rb, ea_r, eb_r, bad);
     } else {
         for (uint32_t t = 0; t < T; ++t) {
             entries<false>(L, src, A.P, B.P, ea, eb, bad);
@@ -566,6 +592,45 @@ __device__ __forceinline__ uint32_t load_windows(const Item &it, uint32_t tid) {
     return __builtin_nontemporal_load(reinterpret_cast<const GLOBAL uint32_t *>(it.win) + tid);
 }
 
+// The staged code bytes of an item to LDS, first stream bit lowest.
+__device__ __forceinline__ void stage_codes(Lds &L, uint32_t tid, const u32x4 (&cw)[kCodeLoads]) {
+#pragma unroll
+    for (int q = 0; q < kCodeLoads; ++q) {
+        if (16u * kThreads * q + 16u * tid < (uint32_t)kCodeCap) {
+            u32x4 v = cw[q];
+            v.x = lsb_first(v.x);
+            v.y = lsb_first(v.y);
+            v.z = lsb_first(v.z);
+            v.w = lsb_first(v.w);
+            reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * q + tid] = v;
+        }
+    }
+}
+
+// Windows 2 tid (a) and 2 tid + 1 (b) of an item: code counts, first code
+// starts (bit offsets from the staged first byte) and the wave's inclusive
+// count sum; the wave's total and first code go to LDS slot `slot` for the
+// waves above it.
+struct WinScan {
+    uint32_t na, nb, sa, sb, incl, first;
+    uint64_t mask;   // lanes with a code
+};
+__device__ __forceinline__ WinScan scan_windows(Lds &L, const Item &it, uint32_t win, uint32_t tid, uint32_t lane,
+                                                uint32_t wave, uint32_t slot) {
+    WinScan w;
+    w.na = win & kWinCntMask;
+    w.nb = (win >> 16) & kWinCntMask;
+    w.incl = wave_inclusive_sum(w.na + w.nb);
+    w.sa = it.rel0 + window_edge(it.nbits, 2 * tid) + ((win >> kWinGapShift) & 31u);
+    w.sb = it.rel0 + window_edge(it.nbits, 2 * tid + 1) + (win >> (16 + kWinGapShift));
+    w.mask = __ballot(w.na + w.nb != 0);
+    w.first = w.na ? w.sa : w.sb;
+    const uint32_t wf = __shfl(w.first, w.mask ? (int)__builtin_ctzll(w.mask) : 0);
+    if (lane == 63) L.wave_total[slot][wave] = w.incl;
+    if (lane == 0) L.wave_first[slot][wave] = w.mask ? wf : 0xFFFFFFFFu;
+    return w;
+}
+
 __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     __shared__ Lds L;
     const uint32_t tid = threadIdx.x;
@@ -574,24 +639,25 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
     uint32_t bad_any = 0;
 
     // Software pipeline over the workgroup's items: while item i is
-    // assembled, the code bytes and decode tables of item i+1 are in flight,
-    // and its raw bytes are requested block by block as item i's assembly
-    // frees the registers.  Items come from the launch's ticket counter, so
-    // that workgroups that run faster take more of them.
+    // assembled, the code bytes, window entries and decode tables of item
+    // i+1 are in flight, and its raw bytes are requested block by block as
+    // item i's assembly frees the registers.  At the end of its assembly a
+    // wave stages item i+1's code bytes, puts its tables in LDS and scans its
+    // windows, and the assembly leaves the tile zero behind it, so that
+    // after the next barrier the decode starts at once.  Items come from the
+    // launch's ticket counter, so that workgroups that run faster take more
+    // of them.
     u32x4 cw[kCodeLoads];
     u32x2 rw[kBlocks];
     u32x4 lr[kLutLoads];
-    uint32_t win;
     // The current item (the first is the workgroup's number).  Every wave
     // reads an item's record itself, with one scalar load, so records need
     // no LDS slot and no barrier of their own.
     uint32_t cur = blockIdx.x;
+    WinScan sc;
     {
-        // (in the order the loop issues them: windows, codes, tables, raw
-        // bytes; the compiler's wait counts assume the same order on every
-        // path)
         const Item it = item_at(a, min(cur, n - 1));
-        win = load_windows(it, tid);
+        const uint32_t win = load_windows(it, tid);
         load_codes(it, tid, cw);
         load_lut(a, it.lut, tid, lr);
         // At the start every workgroup requests its first chunk at once: the
@@ -601,12 +667,18 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) rw[b] = load_raw(it, tid, b);
+        // the tile starts zero; from then on each assembly clears what it read
+#pragma unroll
+        for (uint32_t i = 0; i < sizeof(L.tile) / 16; i += kThreads)
+            if (i + tid < sizeof(L.tile) / 16) reinterpret_cast<u32x4 *>(L.tile)[i + tid] = u32x4{0u, 0u, 0u, 0u};
+        if (it.staged) stage_codes(L, tid, cw);
         put_lut(L, tid, lr);
+        sc = scan_windows(L, it, win, tid, lane, wave, 0);
     }
 
     for (uint32_t k = 0;; ++k) {
-        // ---- the previous item's tile and staged words are no longer
-        //      read; this item's tables are in LDS
+        // ---- the previous item's tile is read and cleared; this item's
+        //      code bytes, tables and wave totals are in LDS
         __syncthreads();
         const uint32_t sl = k & 1u;
         if (cur >= n) break;
@@ -626,44 +698,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             if (lane == 0) L.rec_id[sl ^ 1u] = t1;
         }
 
-        // ---- the tile cleared (the decode ORs its bytes in), and the staged
-        //      words to LDS
-#pragma unroll
-        for (uint32_t i = 0; i < sizeof(L.tile) / 16; i += kThreads)
-            if (i + tid < sizeof(L.tile) / 16) reinterpret_cast<u32x4 *>(L.tile)[i + tid] = u32x4{0u, 0u, 0u, 0u};
-        if (it.staged) {
-#pragma unroll
-            for (int q = 0; q < kCodeLoads; ++q) {
-                if (16u * kThreads * q + 16u * tid < (uint32_t)kCodeCap) {
-                    u32x4 v = cw[q];
-                    v.x = lsb_first(v.x);
-                    v.y = lsb_first(v.y);
-                    v.z = lsb_first(v.z);
-                    v.w = lsb_first(v.w);
-                    reinterpret_cast<u32x4 *>(L.codes + 1)[kThreads * q + tid] = v;
-                }
-            }
-        }
-
-        // ---- windows 2*tid (a) and 2*tid+1 (b): starts and output positions.
-        //      Stream positions are bit offsets from the staged first byte.
-        const uint32_t b0 = it.rel0, b1 = it.rel0 + it.nbits;
+        // ---- windows 2*tid (a) and 2*tid+1 (b): output positions
+        const uint32_t b1 = it.rel0 + it.nbits;
         const uint32_t nc = it.nc;
-        uint32_t na = win & kWinCntMask, nb = (win >> 16) & kWinCntMask;
-        const uint32_t incl = wave_inclusive_sum(na + nb);
-        const uint32_t sa = b0 + window_edge(it.nbits, 2 * tid) + ((win >> kWinGapShift) & 31u);
-        const uint32_t sb = b0 + window_edge(it.nbits, 2 * tid + 1) + (win >> (16 + kWinGapShift));
-        // the wave's code total and first code, for the waves above it
-        const uint64_t mask = __ballot(na + nb != 0);
-        const uint32_t first = na ? sa : sb;          // this lane's first code
-        const uint32_t wf = __shfl(first, mask ? (int)__builtin_ctzll(mask) : 0);
-        if (lane == 63) L.wave_total[wave] = incl;
-        if (lane == 0) L.wave_first[wave] = mask ? wf : 0xFFFFFFFFu;
-        __syncthreads();
-
+        uint32_t na = sc.na, nb = sc.nb;
+        const uint32_t sa = sc.sa, sb = sc.sb;
         uint32_t base = 0;
-        for (uint32_t w = 0; w < wave; ++w) base += L.wave_total[w];
-        const uint32_t qa = base + incl - na - nb;
+        for (uint32_t w = 0; w < wave; ++w) base += L.wave_total[sl][w];
+        const uint32_t qa = base + sc.incl - na - nb;
         const uint32_t qb = qa + na;
         // never write past the chunk, whatever the device bytes say
         uint32_t bad = 0;
@@ -682,14 +724,16 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         bad |= (sa > pmax) | (sb > pmax);
         const uint32_t pa = min(sa, pmax), pb = min(sb, pmax);
         // T counted look-ups: while no window of the wave can run out of
-        // codes (a look-up takes at most three) and no peek can pass pmax (a
-        // look-up moves a window at most 24 bits; a bound on T alone, 24 T
-        // below pmax for every start, would move the valid starts of chunks
-        // that end near pmax)
+        // codes before its last counted look-up (a look-up takes at most
+        // three) and no peek can pass pmax (a look-up moves a window at most
+        // 24 bits; a bound on T alone, 24 T below pmax for every start, would
+        // move the valid starts of chunks that end near pmax)
         const uint32_t room = (pmax - max(pa, pb)) / 24u;
         const uint32_t m = min(na, nb);
-        const uint32_t T =
-            __builtin_amdgcn_readfirstlane(wave_min(min(m >= 1 ? (m - 1) / kMaxPerLookup : 0u, room)));
+        // (staged codes: the last counted look-up may take a window's last
+        // codes, since its entry is kept; codes in global memory: it may not)
+        const uint32_t Tm = m == 0 ? 0u : it.staged ? (m - 1) / kMaxPerLookup + 1 : (m - 1) / kMaxPerLookup;
+        const uint32_t T = __builtin_amdgcn_readfirstlane(wave_min(min(Tm, room)));
         Chain A{pa + kPosBias, qa << 3, qa + na, 0u};
         Chain B{pb + kPosBias, qb << 3, qb + nb, 0u};
         if (it.staged) {
@@ -714,15 +758,15 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // ---- every non-empty window ends where the next non-empty window's
         //      first code starts; the last one at the chunk end
         {
-            const uint64_t above = lane == 63 ? 0 : (mask >> (lane + 1));
+            const uint64_t above = lane == 63 ? 0 : (sc.mask >> (lane + 1));
             const uint32_t nxt_lane = above ? lane + 1 + (uint32_t)__builtin_ctzll(above) : lane;
-            const uint32_t nxt_first = __shfl(first, (int)nxt_lane);
+            const uint32_t nxt_first = __shfl(sc.first, (int)nxt_lane);
             uint32_t after_b = b1;
             if (above) {
                 after_b = nxt_first;
             } else {
                 for (uint32_t w = wave + 1; w < (uint32_t)kWaves; ++w) {
-                    const uint32_t f = L.wave_first[w];
+                    const uint32_t f = L.wave_first[sl][w];
                     if (f != 0xFFFFFFFFu) {
                         after_b = f;
                         break;
@@ -734,10 +778,11 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
             bad_any |= bad;
         }
 
-        // ---- assemble and store the whole 2048-element blocks; each block's
-        //      raw registers take the next item's bytes right after use.
-        //      The next item's window entries, code bytes and tables are
-        //      requested first: they are needed first.
+        // ---- assemble and store the whole 2048-element blocks, clearing
+        //      the tile dwords read; each block's raw registers take the next
+        //      item's bytes right after use.  The next item's window entries,
+        //      code bytes and tables are requested first: they are needed
+        //      first.
         // (the assembly issues all of the kernel's memory traffic, the
         // decode only VALU and LDS work: a wave assembling goes first, so
         // that the compute unit's other waves' decodes do not hold back its
@@ -752,23 +797,27 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
         // the tile offset of this lane's two dwords in block 0; block b's are
         // tile_off(512 b + 2 tid) = 2112 b + that
         const uint32_t tb0 = tile_off(2u * tid);
-        const uint32_t pad_mask = (tid & 15u) ? 0u : ~0u;
 #pragma unroll
         for (int b = 0; b < kBlocks; ++b) {
             if ((uint32_t)b < full) {
-                const uint32_t *tp = reinterpret_cast<const uint32_t *>(L.tile + tb0 + 2112u * b);
+                uint32_t *tp = reinterpret_cast<uint32_t *>(L.tile + tb0 + 2112u * b);
                 const u32x2 t8{tp[0], tp[1]};
+                tp[0] = 0u;
+                tp[1] = 0u;
                 GLOBAL u32x4 *ob = uniform(reinterpret_cast<GLOBAL u32x4 *>(o + kBlockElems * b));
                 __builtin_nontemporal_store(join8(t8, rw[b]), ob + tid);
             }
             rw[b] = load_raw(nx, tid, b);
         }
-        // ---- the ragged last block of a tensor (raw bytes fetched again)
-        if (full * kBlockElems < nc) {
+        if (nc < (uint32_t)kChunk) {
+            // ---- the ragged last block of a tensor (raw bytes fetched again)
             const uint32_t j = full * kBlockElems + 8 * tid;
             if (j < nc) {
                 const u32x2 r8 = *reinterpret_cast<const GLOBAL u32x2 *>(it.raw + j);   // j + 8 <= raw bytes
-                const u32x2 t8 = tile_pair(L, j >> 2, pad_mask);
+                uint32_t *tp = reinterpret_cast<uint32_t *>(L.tile + tile_off(j >> 2));   // j/4 even: +4 is dword j/4 + 1
+                const u32x2 t8{tp[0], tp[1]};
+                tp[0] = 0u;
+                tp[1] = 0u;
                 const u32x4 v = join8(t8, r8);
                 if (j + 8 <= nc) {
                     *reinterpret_cast<GLOBAL u32x4 *>(o + j) = v;
@@ -779,10 +828,18 @@ __global__ __launch_bounds__(kThreads, 3) void decode_kernel(DecodeArgs a) {
                     }
                 }
             }
+            // a window's last look-up and spill reach at most 6 elements past
+            // the chunk's end: clear the dwords the ragged block did not
+            if (tid < 3u) {
+                const uint32_t d = ((nc + 7u) >> 3) * 2u + tid;
+                *reinterpret_cast<uint32_t *>(L.tile + tile_off(d)) = 0u;
+            }
         }
-        // the next item's tables (nothing reads them during the assembly)
+        // the next item: its tables and staged code bytes (nothing reads
+        // them after the decode) and its window scan
         put_lut(L, tid, lr);
-        win = win_nx;
+        if (nx.staged) stage_codes(L, tid, cw);
+        sc = scan_windows(L, nx, win_nx, tid, lane, wave, sl ^ 1u);
         cur = nid;
         __builtin_amdgcn_s_setprio(0);
     }
