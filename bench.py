@@ -454,7 +454,7 @@ def workload_table(rounds: int = 3, names=None):
         sys.exit(1)
 
 
-def nf12_compare(reps: int = 100, warmup: int = 200):
+def nf12_compare(reps: int = 100, warmup: int = 200, names=None):
     """NF12 (fixed-rate 12-bit groups with an escape buffer) next to DF11 on
     the workloads that fit one decode: container size relative to BF16 and
     decode rate (BF16 GB/s and HBM GB/s of the bytes each decode moves)."""
