@@ -129,6 +129,35 @@ def test_batched_mixed_sizes_one_call():
         assert (host[:32] == 0x5A5A).all() and (host[32 + n:] == 0x5A5A).all()
 
 
+def test_tiles_reused_after_partial_chunks():
+    """A workgroup decodes several chunks in turn into one LDS tile, which
+    its assembly clears behind itself; a partial chunk's last windows run a
+    few codes past the chunk's end, and those tile bytes are cleared
+    separately.  Forty tensors of 20 whole chunks plus a partial one (every
+    residue mod 8, a few near a store block's end), more chunks than the
+    launch has workgroups, two launches in a row: every word exact."""
+    torch = _torch()
+    log("tiles reused after partial chunks")
+    residues = [1, 2, 3, 4, 5, 6, 7, 8, 9, 13, 15, 17, 2047, 2049, 4095, 30001, 32767]
+    sizes = [20 * 32768 + residues[i % len(residues)] for i in range(40)]
+    mixes = list(ENTROPY_MIXES)
+    ws = [W.normal_bf16((n,), seed=7000 + i) if i % 3 else entropy_mix_words(mixes[i % len(mixes)], n)
+          for i, n in enumerate(sizes)]
+    cs = oracle_encode_many(ws)
+    plan = df11.Plan(cs)
+    assert sum(i["n_chunks"] for i in plan.infos) > 768
+    dcs = [to_device_u8(c) for c in cs]
+    for rep in range(2):
+        bufs = [empty_words(n, guard=16) for n in sizes]
+        df11.decode_batch(plan, dcs, [o for _, o in bufs])
+        df11.check(plan)
+        torch.cuda.synchronize()
+        for w, (buf, _), n in zip(ws, bufs, sizes):
+            host = buf.cpu().numpy().view(np.uint16)
+            assert (host[16:16 + n] == w).all(), (rep, n)
+            assert (host[:16] == 0x5A5A).all() and (host[16 + n:] == 0x5A5A).all()
+
+
 def test_more_tensors_than_one_launch():
     """70 tensors: the batch is split into launches of 64."""
     torch = _torch()
