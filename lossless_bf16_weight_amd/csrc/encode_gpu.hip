@@ -230,13 +230,22 @@ struct LaneWords {
     }
 };
 
-// 4. one chunk: codes into the stream, the window index, the raw bytes
+// 4. one chunk: codes into the stream, the window index, the raw bytes.
+// The chunk's stream words are put together in LDS (a lane's words with
+// plain writes, the two it may share with its neighbours with an LDS OR)
+// and then written out by the whole workgroup, consecutive words across
+// lanes; only the chunk's first and last words, which it may share with the
+// chunks before and after it, take an atomic OR in global memory.  A chunk
+// of more than kStageWords words (above 8 bits per element) ORs its words
+// into global memory directly.
+constexpr uint32_t kStageWords = 8192;
 __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T) {
     __shared__ uint32_t code[256];
     __shared__ uint8_t len[256];
     __shared__ uint32_t cnt[kWindows], gap[kWindows];
     __shared__ uint32_t s[2][kPackThreads];
     __shared__ uint8_t last_len[kPackThreads];
+    __shared__ uint32_t sw[kStageWords];
     const uint32_t tid = threadIdx.x;
     const uint64_t c = blockIdx.x;
     if (tid < 256) {
@@ -246,6 +255,13 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
     static_assert(kPackThreads == kWindows, "one window entry per packing lane");
     cnt[tid] = 0;
     gap[tid] = 0;
+    const uint64_t b0 = a.ci[2 * c];
+    const uint32_t N = (uint32_t)(a.ci[2 * c + 2] - b0);   // the chunk's bits
+    const uint64_t k0 = b0 >> 5;                            // its first stream word
+    const uint32_t nw = N ? (uint32_t)(((b0 + N - 1) >> 5) - k0 + 1) : 0u;
+    const bool staged = nw <= kStageWords;
+    if (staged)
+        for (uint32_t i = tid; i < nw; i += kPackThreads) sw[i] = 0u;
     __syncthreads();
 
     const LaneRange r = lane_range(c, tid, a.n);
@@ -260,8 +276,6 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
     uint32_t nbits_scan;
     const uint32_t p0 = block_exclusive(bits, s, nbits_scan);   // (its barriers publish last_len)
 
-    const uint64_t b0 = a.ci[2 * c];
-    const uint32_t N = (uint32_t)(a.ci[2 * c + 2] - b0);   // the chunk's bits (= nbits_scan)
     if (r.m) {
         uint64_t G = b0 + p0;            // stream position of the next code
         uint64_t k = G >> 5;             // its word
@@ -274,6 +288,17 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
         // before it (windows start at floor(i N / 512)); then moved forward
         uint32_t wi = min((uint32_t)kWindows - 1u, (kWindows * (p0 + 1u) - 1u) / N);
         uint32_t run_w = ~0u, run = 0;
+        // a finished stream word: to LDS (or global memory), ORed where a
+        // neighbouring lane may have bits in it
+        auto put = [&](uint64_t kk, uint32_t v, bool shared) {
+            if (staged) {
+                if (shared) atomicOr(&sw[kk - k0], v);
+                else sw[kk - k0] = v;
+            } else {
+                if (shared) __hip_atomic_fetch_or(&a.stream[kk], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                else a.stream[kk] = v;
+            }
+        };
         words.each([&](uint32_t, uint32_t x) {
             const uint32_t e = (x >> 7) & 0xFFu;
             const uint32_t L = len[e];
@@ -290,9 +315,7 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
             const uint64_t v = (uint64_t)code[e] << (64u - o - L);
             cur |= (uint32_t)(v >> 32);
             if (o + L >= 32) {
-                if (first_word)   // (may hold the lane before's bits)
-                    __hip_atomic_fetch_or(&a.stream[k], bswap32(cur), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else a.stream[k] = bswap32(cur);
+                put(k, bswap32(cur), first_word);   // (the first may hold the lane before's bits)
                 first_word = false;
                 ++k;
                 cur = (uint32_t)v;
@@ -303,22 +326,38 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
             pos += L;
             prev_len = L;
         });
-        if (o)   // (may hold the next lane's bits)
-            __hip_atomic_fetch_or(&a.stream[k], bswap32(cur), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (o) put(k, bswap32(cur), true);   // (may hold the next lane's bits)
         if (run) atomicAdd(&cnt[run_w], run);
-        // raw bytes: (sign << 7) | fraction
+        // raw bytes: (sign << 7) | fraction, 16 at a time (a partial last
+        // group inside the section's 16-byte padding, its missing bytes zero)
         GLOBAL uint8_t *rb = a.raw + r.j0;
-        uint32_t acc = 0;
+        u32x4 acc{0u, 0u, 0u, 0u};
         words.each([&](uint32_t i, uint32_t x) {
-            acc |= (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (i & 3));
-            if ((i & 3) == 3) {
-                *reinterpret_cast<GLOBAL uint32_t *>(rb + (i & ~3u)) = acc;
-                acc = 0;
+            const uint32_t b = (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (i & 3));
+            const uint32_t q = (i >> 2) & 3u;
+            acc.x |= q == 0 ? b : 0u;
+            acc.y |= q == 1 ? b : 0u;
+            acc.z |= q == 2 ? b : 0u;
+            acc.w |= q == 3 ? b : 0u;
+            if ((i & 15) == 15) {
+                *reinterpret_cast<GLOBAL u32x4 *>(rb + (i & ~15u)) = acc;
+                acc = u32x4{0u, 0u, 0u, 0u};
             }
         });
-        if (r.m & 3) *reinterpret_cast<GLOBAL uint32_t *>(rb + (r.m & ~3u)) = acc;   // inside the 16-byte padding
+        if (r.m & 15) *reinterpret_cast<GLOBAL u32x4 *>(rb + (r.m & ~15u)) = acc;
     }
     __syncthreads();
+    // the staged words, consecutive across lanes; the chunk's first and last
+    // words are ORed (the chunks before and after may have bits in them)
+    if (staged) {
+        for (uint32_t i = tid; i < nw; i += kPackThreads) {
+            const uint32_t v = sw[i];
+            if (i == 0 || i == nw - 1)
+                __hip_atomic_fetch_or(&a.stream[k0 + i], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            else
+                a.stream[k0 + i] = v;
+        }
+    }
     // the 512 window entries, cnt | gap << kWinGapShift, two per lane of the
     // first 256
     if (tid < kWindows / 2) {
