@@ -158,9 +158,14 @@ __global__ __launch_bounds__(kEncThreads) void enc_chunk_bits(const GLOBAL uint3
 }
 
 // 3. start bits: exclusive prefix sum of the chunk bit counts, in place,
-// with each chunk's first element and the sentinel {total bits, n}
+// with each chunk's first element and the sentinel {total bits, n}.  Then
+// the stream words the packing ORs into are cleared (every other stream
+// word it writes whole): each chunk's first and last word, which it may
+// share with the chunks before and after it, and the section's padding
+// after the last code (stream_words: the section's length in words).
 constexpr int kScanThreads = 1024;
-__global__ __launch_bounds__(kScanThreads) void enc_scan(GLOBAL uint64_t *ci, uint64_t n_chunks, uint64_t n) {
+__global__ __launch_bounds__(kScanThreads) void enc_scan(GLOBAL uint64_t *ci, uint64_t n_chunks, uint64_t n,
+                                                         GLOBAL uint32_t *stream, uint64_t stream_words) {
     __shared__ uint64_t s[2][kScanThreads];
     __shared__ uint64_t carry;
     const uint32_t tid = threadIdx.x;
@@ -190,6 +195,15 @@ __global__ __launch_bounds__(kScanThreads) void enc_scan(GLOBAL uint64_t *ci, ui
         ci[2 * n_chunks] = carry;
         ci[2 * n_chunks + 1] = n;
     }
+    // (every start bit was written before the last barrier; the total is in LDS)
+    for (uint64_t c = tid; c < n_chunks; c += kScanThreads) {
+        const uint64_t b = ci[2 * c], e = c + 1 < n_chunks ? ci[2 * c + 2] : carry;
+        if (e > b) {
+            stream[b >> 5] = 0u;
+            stream[(e - 1) >> 5] = 0u;
+        }
+    }
+    for (uint64_t k = ((carry + 31) >> 5) + tid; k < stream_words; k += kScanThreads) stream[k] = 0u;
 }
 
 struct PackArgs {
@@ -368,12 +382,20 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
 }
 
 // The 512-byte header, from a kernel argument (so that no host buffer has to
-// outlive the call).
+// outlive the call), and the bytes no other kernel writes: three ranges,
+// 16-byte aligned, each a multiple of 16 bytes (the gaps after the chunk
+// index and after the window entries, and the raw section's tail from the
+// last group of 16 bytes the packing writes on).
 struct Header {
     uint32_t w[kHeader / 4];
+    uint64_t zero_at[3], zero_bytes[3];
 };
 __global__ __launch_bounds__(kHeader / 4) void enc_header(Header h, GLOBAL uint32_t *out) {
     out[threadIdx.x] = h.w[threadIdx.x];
+    for (int r = 0; r < 3; ++r) {
+        GLOBAL u32x4 *z = reinterpret_cast<GLOBAL u32x4 *>(reinterpret_cast<GLOBAL uint8_t *>(out) + h.zero_at[r]);
+        for (uint64_t i = threadIdx.x; i < h.zero_bytes[r] / 16; i += kHeader / 4) z[i] = u32x4{0u, 0u, 0u, 0u};
+    }
 }
 
 // Zeroes n counters (the histograms, before they are counted).
@@ -492,26 +514,30 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
         Header h;
         write_header(reinterpret_cast<uint8_t *>(h.w), n, ndims[t], dims + 8 * t, L, T.len);
         uint8_t *out = static_cast<uint8_t *>(d_outs[t]);
-        // the kernels write the header, the chunk index, the window entries
-        // and the raw bytes (up to the dword holding element n - 1); clear the
-        // rest: the gaps after the chunk index and the window entries, the
-        // stream section (whose words are ORed together), and the raw
+        // the kernels write the header, the chunk index, the window entries,
+        // the stream (clearing the words they OR into themselves) and the raw
+        // bytes (up to the 16 bytes holding element n - 1); clear the rest:
+        // the gaps after the chunk index and the window entries, and the raw
         // section's tail padding
         // (an empty tensor runs no kernel but the header's: all of it is cleared)
         const uint64_t ci_end = n ? L.off_ci + (L.n_chunks + 1) * 16 : kHeader;
         const uint64_t win_end = L.off_win + L.n_chunks * kWindows * 2;
-        const uint64_t raw_set = L.off_raw + (n & ~uint64_t(3));
-        if ((e = hipMemsetAsync(out + ci_end, 0, L.off_win - ci_end, stream)) != hipSuccess ||
-            (e = hipMemsetAsync(out + win_end, 0, L.off_raw - win_end, stream)) != hipSuccess ||
-            (e = hipMemsetAsync(out + raw_set, 0, L.total - raw_set, stream)) != hipSuccess)
-            return hip_fail(who, e, "hipMemsetAsync");
+        const uint64_t stream_at = n ? L.off_stream : L.off_raw;
+        const uint64_t raw_set = L.off_raw + (n & ~uint64_t(15));
+        h.zero_at[0] = ci_end;
+        h.zero_bytes[0] = L.off_win - ci_end;
+        h.zero_at[1] = win_end;
+        h.zero_bytes[1] = stream_at - win_end;
+        h.zero_at[2] = raw_set;
+        h.zero_bytes[2] = L.total - raw_set;
         hipLaunchKernelGGL(enc_header, dim3(1), dim3(kHeader / 4), 0, stream, h, (GLOBAL uint32_t *)out);
         if (n) {
             const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
             GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
             hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream,
                                (const GLOBAL uint32_t *)chunk_hist_of(out, n), T, ci);
-            hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n);
+            hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n,
+                               (GLOBAL uint32_t *)(out + L.off_stream), (L.off_raw - L.off_stream) / 4);
             PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
                         (GLOBAL uint8_t *)(out + L.off_raw)};
             hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kPackThreads), 0, stream, pa, T);
