@@ -105,3 +105,33 @@ def test_batch_of_mixed_tensors_matches_single_calls():
         want = oracle.encode(w)
         got = c.cpu().numpy()
         assert got.size == want.size and (got == want).all(), w.shape
+
+
+@pytest.mark.parametrize("fill", ["random", "ones"])
+def test_containers_into_dirty_buffers_match_oracle_bytes(fill):
+    """No byte of a container is cleared before the kernels run: each is
+    written by exactly one kernel (stream words shared by two chunks are
+    cleared by the scan kernel before the packing ORs into them).  Output
+    buffers full of random bytes, or of 0xFF, must still come back as the
+    oracle's bytes: long codes, chunks whose code words do not fit the
+    packing kernel's LDS array (every 16-bit word: 8 bits per code), many
+    chunks sharing stream words, and ragged tails."""
+    import torch
+    log(f"gpu encode into {fill} buffers")
+    ws = [W.heavy_tail_bf16((5 * 32768 + 4097,), seed=21), W.exhaustive_words(),
+          entropy_mix_words(sorted(ENTROPY_MIXES)[0], 9 * 32768 + 11), W.normal_bf16((33,), seed=22),
+          W.normal_bf16((700001,), seed=23)]
+    ts = [torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to("cuda") for w in ws]
+    if fill == "random":
+        g = torch.Generator(device="cuda").manual_seed(31)
+        outs = [torch.randint(0, 256, (df11.container_bound(t.numel()),), dtype=torch.uint8, device="cuda",
+                              generator=g) for t in ts]
+    else:
+        outs = [torch.full((df11.container_bound(t.numel()),), 0xFF, dtype=torch.uint8, device="cuda")
+                for t in ts]
+    cs = df11.encode_device_batch(ts, outs=outs)
+    torch.cuda.synchronize()
+    for w, c in zip(ws, cs):
+        want = oracle.encode(w)
+        got = c.cpu().numpy()
+        assert got.size == want.size and (got == want).all(), w.size
