@@ -49,9 +49,12 @@
  * floor(N/512) or ceil(N/512) bits.  cnt[c][i] counts the codes that START in
  * window i (at most 1536, a window's largest bit count, so 11 bits); gap[c][i]
  * is the offset of the first of them from the window start (always < 24, 5
- * bits), and 0 when cnt is 0.  One 16-bit entry per window holds both: a
- * smaller block index in the spirit of the df11pack page's experimental 8-bit
- * index ("Beyond the official format").  The first code of window i is
+ * bits), and 0 when cnt is 0.  One 16-bit entry per window holds both, 1024
+ * bytes per chunk.  (The df11pack page's experimental 8-bit block index,
+ * "Beyond the official format", halves that with windows of equal code
+ * counts; such windows decode slower on this kernel, whose lanes run
+ * windows side by side and wait for the one with the most look-ups, so the
+ * windows here have equal bit counts instead.)  The first code of window i is
  * element out_elem[c] + (cnt[c][0] + ... + cnt[c][i-1]) -- a prefix sum over
  * the windows.  The decoder gives one 256-lane workgroup to a chunk and two
  * neighbouring windows to each lane, and forms the prefix sum with one

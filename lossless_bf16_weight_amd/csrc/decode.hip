@@ -502,19 +502,6 @@ __device__ __forceinline__ void decode_pair(Lds &L, const Src &src, Chain &A, Ch
     B.P -= trailing_bits(L, eb_r, (uint32_t)(-rb));
 }
 
-// Tile dwords dw and dw+1 (dw even) for the assembly.  The lanes whose dw
-// opens a 32-dword group also OR in the (zero) pad before it: the look-ups
-// no longer spill into the pads, but the same code without that read
-// measured 0.6% slower (the compiler then keeps one address register per
-// store block).  (Dword 0 ORs itself.)
-__device__ __forceinline__ u32x2 tile_pair(const Lds &L, uint32_t dw, uint32_t pad_mask) {
-    const uint32_t ta = tile_off(dw);
-    const uint32_t tp = ta ? ta - 4u : 0u;
-    const uint32_t pad = *reinterpret_cast<const uint32_t *>(L.tile + tp) & pad_mask;
-    return u32x2{*reinterpret_cast<const uint32_t *>(L.tile + ta) | pad,
-                 *reinterpret_cast<const uint32_t *>(L.tile + ta + 4)};
-}
-
 // One work item (a chunk of a tensor) and where its bytes are.
 struct Item {
     const GLOBAL uint8_t *stream;   // the staged stream bytes
