@@ -107,6 +107,24 @@ def test_batch_of_mixed_tensors_matches_single_calls():
         assert got.size == want.size and (got == want).all(), w.shape
 
 
+def _chunks_above_the_lds_array():
+    """One exponent at probability 1/2 (a 1-bit code) and 255 uniform (9-bit
+    codes), the whole tensor's words sorted by code length: the second half's
+    chunks need about 9,200 stream words, more than the packing kernel's LDS
+    array (8,192), so they are packed in global memory, and most of them
+    start inside a word.  Returns the words and the oracle's container."""
+    w = W.exponent_mix_bf16(32768 * 8 + 777, seed=24, probs=[255.0] + [1.0] * 255, e0=0)
+    code_len = oracle.header(oracle.encode(w))["code_len"].astype(np.int64)
+    w = w[np.argsort(code_len[(w >> 7) & 0xFF], kind="stable")]
+    c = oracle.encode(w)
+    h = oracle.header(c)
+    ci = c[h["off_chunk_index"]:h["off_chunk_index"] + 16 * (h["n_chunks"] + 1)].view(np.uint64).reshape(-1, 2)
+    b0, b1 = ci[:-1, 0].astype(np.int64), ci[1:, 0].astype(np.int64)
+    nw = ((b1 - 1) >> 5) - (b0 >> 5) + 1
+    assert ((nw > 8192) & (b0 % 32 != 0)).sum() >= 3
+    return w, c
+
+
 @pytest.mark.parametrize("fill", ["random", "ones"])
 def test_containers_into_dirty_buffers_match_oracle_bytes(fill):
     """No byte of a container is cleared before the kernels run: each is
@@ -114,13 +132,14 @@ def test_containers_into_dirty_buffers_match_oracle_bytes(fill):
     cleared by the scan kernel before the packing ORs into them).  Output
     buffers full of random bytes, or of 0xFF, must still come back as the
     oracle's bytes: long codes, chunks whose code words do not fit the
-    packing kernel's LDS array (every 16-bit word: 8 bits per code), many
-    chunks sharing stream words, and ragged tails."""
+    packing kernel's LDS array (packed in global memory, with the words two
+    lanes share ORed there), many chunks sharing stream words, and ragged
+    tails."""
     import torch
     log(f"gpu encode into {fill} buffers")
     ws = [W.heavy_tail_bf16((5 * 32768 + 4097,), seed=21), W.exhaustive_words(),
           entropy_mix_words(sorted(ENTROPY_MIXES)[0], 9 * 32768 + 11), W.normal_bf16((33,), seed=22),
-          W.normal_bf16((700001,), seed=23)]
+          W.normal_bf16((700001,), seed=23), _chunks_above_the_lds_array()[0]]
     ts = [torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to("cuda") for w in ws]
     if fill == "random":
         g = torch.Generator(device="cuda").manual_seed(31)
