@@ -257,20 +257,90 @@ struct LaneWords {
 // of more than kStageWords words (above 8 bits per element) is packed into
 // global memory directly, with the same plain writes and ORs.
 constexpr uint32_t kStageWords = 8192;
+
+// A lane's codes into 32-bit stream words, first stream bit highest, its
+// windows' counts and first-code offsets.  The lane's bits start at stream
+// bit g0 (chunk bit p0); the codes go through a 64-bit register that holds
+// the bits not yet written (the first word starts with the g0 % 32 bits of
+// the lane before, as zeros), and every word that fills up is written out:
+// staged chunks OR every word into the zeroed LDS words (the first and last
+// may be shared with the neighbouring lanes), the others write plain words
+// to global memory except the first and last, which they OR there.  A code
+// whose start passes the next window edge takes the slow path: the window
+// count so far goes out, and the new window's first-code offset is set.
+template <bool kStaged>
+__device__ __forceinline__ void pack_lane(const LaneWords &words, const uint32_t *tab, uint32_t *sw,
+                                          GLOBAL uint32_t *stream, uint64_t k0, uint64_t g0, uint32_t p0,
+                                          uint32_t N, uint32_t prev_len, uint32_t *cnt, uint32_t *gap) {
+    uint64_t k = g0 >> 5;                  // the word being filled
+    uint64_t acc = 0;                      // its bits so far, and any after
+    uint32_t nb = (uint32_t)(g0 & 31);     // bits in acc not yet written
+    bool first = true;
+    auto put = [&](uint32_t v, bool shared) {
+        if (kStaged) {
+            atomicOr(&sw[k - k0], bswap32(v));   // (the LDS words start zero)
+        } else if (shared) {
+            __hip_atomic_fetch_or(&stream[k], bswap32(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            stream[k] = bswap32(v);
+        }
+    };
+    // the window of the lane's first code: the last one whose edge is at or
+    // before it (windows start at floor(i N / 512))
+    uint32_t wi = min((uint32_t)kWindows - 1u, (kWindows * (p0 + 1u) - 1u) / N);
+    uint32_t next_edge = wi + 1u < (uint32_t)kWindows ? window_edge(N, wi + 1u) : ~0u;
+    if (p0 == 0 || window_edge(N, wi) > p0 - prev_len) gap[wi] = p0 - window_edge(N, wi);
+    uint32_t run = 0;
+    uint32_t pos = p0;
+    words.each([&](uint32_t, uint32_t x) {
+        const uint32_t ent = tab[(x >> 7) & 0xFFu];
+        const uint32_t L = ent & 0xFFu;
+        if (pos >= next_edge) {
+            // the first code to start in a later window (the windows passed
+            // over hold no code start)
+            atomicAdd(&cnt[wi], run);
+            run = 0;
+            do {
+                ++wi;
+            } while (wi + 1u < (uint32_t)kWindows && window_edge(N, wi + 1u) <= pos);
+            gap[wi] = pos - window_edge(N, wi);
+            next_edge = wi + 1u < (uint32_t)kWindows ? window_edge(N, wi + 1u) : ~0u;
+        }
+        ++run;
+        pos += L;
+        acc = (acc << L) | (ent >> 8);
+        nb += L;
+        if (nb >= 32u) {
+            nb -= 32u;
+            put((uint32_t)(acc >> nb), first);
+            first = false;
+            ++k;
+        }
+    });
+    if (nb) put((uint32_t)(acc << (32u - nb)), true);   // (shared with the lane after)
+    if (run) atomicAdd(&cnt[wi], run);
+}
+
+// The raw bytes, (sign << 7) | fraction, of a lane holding all its words:
+// four at a time from two words of the 16-byte groups (masks, shifts and
+// one byte permute), 16 bytes per store.
+__device__ __forceinline__ uint32_t raw4(uint32_t d0, uint32_t d1) {
+    const uint32_t t0 = (d0 & 0x007F007Fu) | ((d0 >> 8) & 0x00800080u);
+    const uint32_t t1 = (d1 & 0x007F007Fu) | ((d1 >> 8) & 0x00800080u);
+    return __builtin_amdgcn_perm(t1, t0, 0x06040200u);
+}
+
 __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T) {
-    __shared__ uint32_t code[256];
-    __shared__ uint8_t len[256];
+    __shared__ uint32_t tab[256];          // code << 8 | length
     __shared__ uint32_t cnt[kWindows], gap[kWindows];
     __shared__ uint32_t s[2][kPackThreads];
     __shared__ uint8_t last_len[kPackThreads];
     __shared__ uint32_t sw[kStageWords];
     const uint32_t tid = threadIdx.x;
     const uint64_t c = blockIdx.x;
-    if (tid < 256) {
-        code[tid] = T.code[tid];
-        len[tid] = T.len[tid];
-    }
+    if (tid < 256) tab[tid] = (T.code[tid] << 8) | T.len[tid];
     static_assert(kPackThreads == kWindows, "one window entry per packing lane");
+    static_assert(kMaxLen <= 24, "code << 8 fits 32 bits");
     cnt[tid] = 0;
     gap[tid] = 0;
     const uint64_t b0 = a.ci[2 * c];
@@ -287,7 +357,7 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
     // this lane's bits and its last element's code length, for its neighbours
     uint32_t bits = 0, lastl = 0;
     words.each([&](uint32_t, uint32_t x) {
-        lastl = len[(x >> 7) & 0xFFu];
+        lastl = tab[(x >> 7) & 0xFFu] & 0xFFu;
         bits += lastl;
     });
     last_len[tid] = (uint8_t)lastl;
@@ -313,74 +383,37 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
     }
 
     if (r.m) {
-        uint64_t G = b0 + p0;            // stream position of the next code
-        uint64_t k = G >> 5;             // its word
-        uint32_t o = (uint32_t)(G & 31); // its bit in the word, first stream bit highest
-        uint32_t cur = 0;
-        bool first_word = true;
-        uint32_t pos = p0;                                   // chunk-relative start of the next code
-        uint32_t prev_len = tid ? last_len[tid - 1] : 0u;     // the code before it
-        // the window of the lane's first code: the last one that starts at or
-        // before it (windows start at floor(i N / 512)); then moved forward
-        uint32_t wi = min((uint32_t)kWindows - 1u, (kWindows * (p0 + 1u) - 1u) / N);
-        uint32_t run_w = ~0u, run = 0;
-        // a finished stream word: to LDS (or global memory), ORed where a
-        // neighbouring lane may have bits in it
-        auto put = [&](uint64_t kk, uint32_t v, bool shared) {
-            if (staged) {
-                if (shared) atomicOr(&sw[kk - k0], v);
-                else sw[kk - k0] = v;
-            } else {
-                if (shared) __hip_atomic_fetch_or(&a.stream[kk], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else a.stream[kk] = v;
-            }
-        };
-        words.each([&](uint32_t, uint32_t x) {
-            const uint32_t e = (x >> 7) & 0xFFu;
-            const uint32_t L = len[e];
-            while (wi + 1u < (uint32_t)kWindows && window_edge(N, wi + 1u) <= pos) ++wi;
-            const uint32_t edge = window_edge(N, wi);
-            if (pos == 0 || edge > pos - prev_len) gap[wi] = pos - edge;   // the window's first code
-            if (wi != run_w) {
-                if (run) atomicAdd(&cnt[run_w], run);
-                run_w = wi;
-                run = 0;
-            }
-            ++run;
-            // the code, first bit highest, at bit o of word k
-            const uint64_t v = (uint64_t)code[e] << (64u - o - L);
-            cur |= (uint32_t)(v >> 32);
-            if (o + L >= 32) {
-                put(k, bswap32(cur), first_word);   // (the first may hold the lane before's bits)
-                first_word = false;
-                ++k;
-                cur = (uint32_t)v;
-                o = o + L - 32;
-            } else {
-                o += L;
-            }
-            pos += L;
-            prev_len = L;
-        });
-        if (o) put(k, bswap32(cur), true);   // (may hold the next lane's bits)
-        if (run) atomicAdd(&cnt[run_w], run);
+        const uint32_t prev_len = tid ? last_len[tid - 1] : 0u;   // the code before the lane's first
+        if (staged)
+            pack_lane<true>(words, tab, sw, a.stream, k0, b0 + p0, p0, N, prev_len, cnt, gap);
+        else
+            pack_lane<false>(words, tab, sw, a.stream, k0, b0 + p0, p0, N, prev_len, cnt, gap);
         // raw bytes: (sign << 7) | fraction, 16 at a time (a partial last
         // group inside the section's 16-byte padding, its missing bytes zero)
         GLOBAL uint8_t *rb = a.raw + r.j0;
-        u32x4 acc{0u, 0u, 0u, 0u};
-        words.each([&](uint32_t i, uint32_t x) {
-            const uint32_t b = (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (i & 3));
-            const uint32_t q = (i >> 2) & 3u;
-            acc.x |= q == 0 ? b : 0u;
-            acc.y |= q == 1 ? b : 0u;
-            acc.z |= q == 2 ? b : 0u;
-            acc.w |= q == 3 ? b : 0u;
-            if ((i & 15) == 15) {
-                *reinterpret_cast<GLOBAL u32x4 *>(rb + (i & ~15u)) = acc;
-                acc = u32x4{0u, 0u, 0u, 0u};
+        if (words.full) {
+#pragma unroll
+            for (int g = 0; g < kPerLane / 8; g += 2) {
+                const u32x4 &v = words.v[g], &u = words.v[g + 1];
+                *reinterpret_cast<GLOBAL u32x4 *>(rb + 8 * g) =
+                    u32x4{raw4(v.x, v.y), raw4(v.z, v.w), raw4(u.x, u.y), raw4(u.z, u.w)};
             }
-        });
-        if (r.m & 15) *reinterpret_cast<GLOBAL u32x4 *>(rb + (r.m & ~15u)) = acc;
+        } else {
+            u32x4 acc{0u, 0u, 0u, 0u};
+            words.each([&](uint32_t i, uint32_t x) {
+                const uint32_t b = (((x >> 8) & 0x80u) | (x & 0x7Fu)) << (8 * (i & 3));
+                const uint32_t q = (i >> 2) & 3u;
+                acc.x |= q == 0 ? b : 0u;
+                acc.y |= q == 1 ? b : 0u;
+                acc.z |= q == 2 ? b : 0u;
+                acc.w |= q == 3 ? b : 0u;
+                if ((i & 15) == 15) {
+                    *reinterpret_cast<GLOBAL u32x4 *>(rb + (i & ~15u)) = acc;
+                    acc = u32x4{0u, 0u, 0u, 0u};
+                }
+            });
+            if (r.m & 15) *reinterpret_cast<GLOBAL u32x4 *>(rb + (r.m & ~15u)) = acc;
+        }
     }
     __syncthreads();
     // the staged words, consecutive across lanes; the chunk's first and last
