@@ -13,7 +13,8 @@
 //      from the total bit count sum(f * len), and the header;
 //   2. per-chunk bit counts from the chunk histograms, written where the
 //      chunk index goes;
-//   3. one workgroup turns them into start bits (the chunk index);
+//   3. one workgroup turns them into start bits (the chunk index) and
+//      writes the header;
 //   4. one 512-lane workgroup per chunk: every lane packs the codes of 64
 //      consecutive elements into 32-bit stream words, put together in LDS
 //      and written out by the whole workgroup (the words a lane may share
@@ -26,8 +27,8 @@
 // Nothing is cleared before the kernels run: every byte of the container is
 // written by one of them.  The stream words that take ORs in global memory
 // (a chunk's first and last word, shared with the chunks before and after
-// it) are cleared by the kernel of step 3, the header kernel clears the
-// gaps between and after the sections.
+// it) are cleared by the kernel of step 3, which also clears the gaps
+// between and after the sections.
 //
 // The histogram is bound by its LDS atomics, the packing by its serial loop
 // of 64 codes per lane; the words are read twice (2 bytes each) and about
@@ -161,18 +162,36 @@ __global__ __launch_bounds__(kEncThreads) void enc_chunk_bits(const GLOBAL uint3
     if (threadIdx.x == 0) ci[2 * c] = total;
 }
 
+// The 512-byte header, from a kernel argument (so that no host buffer has to
+// outlive the call), and the bytes no kernel writes otherwise: three ranges,
+// 16-byte aligned, each a multiple of 16 bytes (the gaps after the chunk
+// index and after the window entries, and the raw section's tail from the
+// last group of 16 bytes the packing writes on).
+struct Header {
+    uint32_t w[kHeader / 4];
+    uint64_t zero_at[3], zero_bytes[3];
+};
+
 // 3. start bits: exclusive prefix sum of the chunk bit counts, in place,
 // with each chunk's first element and the sentinel {total bits, n}.  Then
 // the stream words the packing ORs into are cleared (every other stream
 // word it writes whole): each chunk's first and last word, which it may
 // share with the chunks before and after it, and the section's padding
-// after the last code (stream_words: the section's length in words).
+// after the last code (stream_words: the section's length in words).  The
+// same workgroup writes the header and clears the gaps no kernel writes.
 constexpr int kScanThreads = 1024;
 __global__ __launch_bounds__(kScanThreads) void enc_scan(GLOBAL uint64_t *ci, uint64_t n_chunks, uint64_t n,
-                                                         GLOBAL uint32_t *stream, uint64_t stream_words) {
+                                                         GLOBAL uint32_t *stream, uint64_t stream_words,
+                                                         Header h, GLOBAL uint32_t *out) {
     __shared__ uint64_t s[2][kScanThreads];
     __shared__ uint64_t carry;
     const uint32_t tid = threadIdx.x;
+    // the header, and the gaps between and after the sections
+    if (tid < kHeader / 4) out[tid] = h.w[tid];
+    for (int r = 0; r < 3; ++r) {
+        GLOBAL u32x4 *z = reinterpret_cast<GLOBAL u32x4 *>(reinterpret_cast<GLOBAL uint8_t *>(out) + h.zero_at[r]);
+        for (uint64_t i = tid; i < h.zero_bytes[r] / 16; i += kScanThreads) z[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (tid == 0) carry = 0;
     for (uint64_t base = 0; base < n_chunks; base += kScanThreads) {
         __syncthreads();
@@ -436,23 +455,6 @@ __global__ __launch_bounds__(kPackThreads) void enc_pack(PackArgs a, CodeTable T
     }
 }
 
-// The 512-byte header, from a kernel argument (so that no host buffer has to
-// outlive the call), and the bytes no other kernel writes: three ranges,
-// 16-byte aligned, each a multiple of 16 bytes (the gaps after the chunk
-// index and after the window entries, and the raw section's tail from the
-// last group of 16 bytes the packing writes on).
-struct Header {
-    uint32_t w[kHeader / 4];
-    uint64_t zero_at[3], zero_bytes[3];
-};
-__global__ __launch_bounds__(kHeader / 4) void enc_header(Header h, GLOBAL uint32_t *out) {
-    out[threadIdx.x] = h.w[threadIdx.x];
-    for (int r = 0; r < 3; ++r) {
-        GLOBAL u32x4 *z = reinterpret_cast<GLOBAL u32x4 *>(reinterpret_cast<GLOBAL uint8_t *>(out) + h.zero_at[r]);
-        for (uint64_t i = threadIdx.x; i < h.zero_bytes[r] / 16; i += kHeader / 4) z[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
 // Zeroes n counters (the histograms, before they are counted).
 __global__ __launch_bounds__(kEncThreads) void enc_clear(GLOBAL unsigned long long *p, uint64_t n) {
     const uint64_t i = (uint64_t)blockIdx.x * kEncThreads + threadIdx.x;
@@ -574,7 +576,7 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
         // bytes (up to the 16 bytes holding element n - 1); clear the rest:
         // the gaps after the chunk index and the window entries, and the raw
         // section's tail padding
-        // (an empty tensor runs no kernel but the header's: all of it is cleared)
+        // (an empty tensor: all of it after the header is cleared)
         const uint64_t ci_end = n ? L.off_ci + (L.n_chunks + 1) * 16 : kHeader;
         const uint64_t win_end = L.off_win + L.n_chunks * kWindows * 2;
         const uint64_t stream_at = n ? L.off_stream : L.off_raw;
@@ -585,14 +587,17 @@ df11_status pack_batch(const char *who, int n_tensors, const void *const *d_word
         h.zero_bytes[1] = stream_at - win_end;
         h.zero_at[2] = raw_set;
         h.zero_bytes[2] = L.total - raw_set;
-        hipLaunchKernelGGL(enc_header, dim3(1), dim3(kHeader / 4), 0, stream, h, (GLOBAL uint32_t *)out);
-        if (n) {
-            const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
-            GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
+        GLOBAL uint64_t *ci = (GLOBAL uint64_t *)(out + L.off_ci);
+        if (n)
             hipLaunchKernelGGL(enc_chunk_bits, dim3((unsigned)L.n_chunks), dim3(kEncThreads), 0, stream,
                                (const GLOBAL uint32_t *)chunk_hist_of(out, n), T, ci);
-            hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n,
-                               (GLOBAL uint32_t *)(out + L.off_stream), (L.off_raw - L.off_stream) / 4);
+        // (an empty tensor: the header and its zero chunk index entry, the
+        // rest cleared)
+        hipLaunchKernelGGL(enc_scan, dim3(1), dim3(kScanThreads), 0, stream, ci, L.n_chunks, n,
+                           (GLOBAL uint32_t *)(out + (n ? L.off_stream : L.off_raw)),
+                           n ? (L.off_raw - L.off_stream) / 4 : 0, h, (GLOBAL uint32_t *)out);
+        if (n) {
+            const GLOBAL uint16_t *w = (const GLOBAL uint16_t *)d_words[t];
             PackArgs pa{w, n, ci, (GLOBAL uint32_t *)(out + L.off_stream), (GLOBAL uint32_t *)(out + L.off_win),
                         (GLOBAL uint8_t *)(out + L.off_raw)};
             hipLaunchKernelGGL(enc_pack, dim3((unsigned)L.n_chunks), dim3(kPackThreads), 0, stream, pa, T);
