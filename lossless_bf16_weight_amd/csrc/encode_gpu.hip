@@ -77,7 +77,8 @@ __device__ __forceinline__ uint32_t word_of(const u32x4 &v, int i) {
 
 // 1. exponent histogram, one workgroup per chunk: the chunk's 256 counts go
 // to chunk_hist (u32 each, in the space the chunk's window entries take
-// later) and are added into the tensor's u64 totals
+// later) and are added into the tensor's u64 totals.  Bound by the LDS
+// atomics once the loads are in flight together.
 __global__ __launch_bounds__(kEncThreads) void enc_hist(const GLOBAL uint16_t *w, uint64_t n,
                                                         GLOBAL uint32_t *chunk_hist,
                                                         GLOBAL unsigned long long *hist) {
@@ -90,6 +91,23 @@ __global__ __launch_bounds__(kEncThreads) void enc_hist(const GLOBAL uint16_t *w
     const uint64_t c = blockIdx.x;
     const uint64_t c0 = c * kChunk;
     const uint64_t cend = min(n, c0 + kChunk);
+    if (cend - c0 == kChunk) {
+        // a whole chunk: all 16 of a lane's 16-byte loads in flight before
+        // their counts (one load, then its 8 counts, left the kernel waiting
+        // on each load: 221 -> 174 us per Llama-8B block call)
+        constexpr int kGroups = kChunk / (8 * kEncThreads);
+        const GLOBAL u32x4 *src = reinterpret_cast<const GLOBAL u32x4 *>(w + c0) + threadIdx.x;
+#pragma unroll
+        for (int g = 0; g < kGroups; g += 16) {
+            u32x4 v[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = src[kEncThreads * (g + k)];
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) atomicAdd(&mine[(word_of(v[k], i) >> 7) & 0xFFu], 1u);
+        }
+    } else
     for (uint64_t j = c0 + 8 * threadIdx.x; j < cend; j += 8 * kEncThreads) {
         if (j + 8 <= cend) {
             const u32x4 v = *reinterpret_cast<const GLOBAL u32x4 *>(w + j);
