@@ -45,7 +45,7 @@
 //      until that chunk's assembly.
 //
 // There is no matrix arithmetic here: the path is bound by HBM traffic
-// (about 1.37 bytes read and 2 bytes written per element), with the look-up
+// (about 1.36 bytes read and 2 bytes written per element), with the look-up
 // chains' latency and integer ALU as the secondary limit.
 #include <hip/hip_runtime.h>
 
