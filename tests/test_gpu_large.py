@@ -3,7 +3,8 @@
 element offsets pass 2^31 and stream bit offsets pass 2^32 (the container
 format allows up to 2^46 elements and 2^24 chunks per tensor).
 
-Checks: the whole output equals the source words (compared on the GPU); the
+Checks: the GPU encoder's container equals the host encoder's byte for
+byte; the whole output equals the source words (compared on the GPU); the
 chunks on either side of element 2^31, the first and the last equal the
 oracle's own chunk decode of the same container; guard words on both sides
 of the output stay untouched; the same tensor decoded again in one batched
@@ -65,6 +66,12 @@ def test_tensor_past_2_31_elements_and_2_32_code_bits():
     dc = to_device_u8(c)
     src = to_device_words(w)
     del w
+    # the GPU encoder on the same words: the same bytes
+    log("large tensor: GPU encoder")
+    g = df11.encode_device(src)
+    torch.cuda.synchronize()
+    assert g.numel() == c.size and torch.equal(g, dc)
+    del g
     buf, out = empty_words(N_BIG, guard=GUARD, fill=CANARY)
     df11.decode(plan, 0, dc, out)
     df11.check(plan)
