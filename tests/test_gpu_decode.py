@@ -10,7 +10,7 @@ import oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from exponent_mixes import ENTROPY_MIXES, entropy_mix_words
+from exponent_mixes import ENTROPY_MIXES, entropy_mix_words, random_exponent_case
 from gpu_util import empty_words, log, oracle_encode_many, to_device_u8, to_device_words
 
 pytestmark = pytest.mark.gpu
@@ -535,3 +535,33 @@ def test_decode_batch_replays_from_a_hip_graph():
             for w, t in zip(ws, o):
                 assert (t.cpu().numpy().view(np.uint16) == w).all(), rep
     df11.check(plan)
+
+
+def test_random_distributions_in_one_batched_launch():
+    """60 seeded random cases (sizes up to 200,000 words, random exponent
+    sets and probabilities, Fibonacci counts that reach the 24-bit cap, an
+    empty tensor possible) in the oracle's containers, decoded by one
+    batched launch (60 tensors, 60 code tables): every output equals its
+    source words, with guard words on both sides untouched; and one batched
+    GPU encoder call over the same words writes the oracle's bytes."""
+    import torch
+    log("random distributions, batched")
+    ws = [random_exponent_case(seed, 200_000) for seed in range(60)]
+    conts = oracle_encode_many(ws)
+    assert max(int(oracle.header(c)["code_len"].max()) for c, w in zip(conts, ws) if w.size) == 24
+    plan = df11.Plan(conts)
+    d_conts = [to_device_u8(c) for c in conts]
+    bufs = [empty_words(w.size, guard=16) for w in ws]
+    df11.decode_batch(plan, d_conts, [o for _, o in bufs])
+    df11.check(plan)
+    torch.cuda.synchronize()
+    for seed, (w, (buf, out)) in enumerate(zip(ws, bufs)):
+        got = buf.cpu().numpy().view(np.uint16)
+        assert (got[16:16 + w.size] == w).all(), seed
+        assert (got[:16] == 0x5A5A).all() and (got[16 + w.size:] == 0x5A5A).all(), seed
+    log("random distributions, GPU encoder")
+    ts = [torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to("cuda") for w in ws]
+    gs = df11.encode_device_batch(ts)
+    torch.cuda.synchronize()
+    for seed, (g, c) in enumerate(zip(gs, conts)):
+        assert g.numel() == c.size and (g.cpu().numpy() == c).all(), seed

@@ -174,3 +174,20 @@ def test_plan_rejects_bad_input_without_a_gpu():
         df11.Plan([c[:64]])
     assert e.value.status == 2
     assert "DF11_E_FORMAT" in str(e.value)
+
+
+def test_encoder_matches_oracle_on_random_distributions():
+    """60 seeded random cases (random sizes up to 200,000 words, random
+    exponent sets and probabilities, some pushing codes to the 24-bit cap):
+    the product encoder's bytes equal the oracle's, on 1 and 4 threads."""
+    from exponent_mixes import random_exponent_case
+    longest = 0
+    for seed in range(60):
+        w = random_exponent_case(seed, 200_000)
+        want = oracle.encode(w)
+        for threads in (1, 4):
+            got = df11.encode(w, threads=threads)
+            assert got.size == want.size and (got == want).all(), (seed, w.size, threads)
+        if w.size:
+            longest = max(longest, int(oracle.header(want)["code_len"].max()))
+    assert longest == 24   # the cases reach the length cap
