@@ -192,6 +192,49 @@ def test_non_default_stream_and_repeats():
         assert (o.cpu().numpy().view(np.uint16) == w).all()
 
 
+def test_one_plan_from_four_host_threads():
+    """Four host threads, each with a stream and outputs of its own, enqueue
+    20 batched decodes of one plan at the same time (the library hands out
+    the plan's ticket counters under a lock, and ctypes calls run without
+    the interpreter lock); every output exact, the flag clear."""
+    import threading
+    torch = _torch()
+    log("one plan, four host threads")
+    sizes = [2 * 32768 + 11, 300001, 7]
+    ws = [W.normal_bf16((n,), seed=80 + i) for i, n in enumerate(sizes)]
+    cs = oracle_encode_many(ws)
+    plan = df11.Plan(cs)
+    dcs = [to_device_u8(c) for c in cs]
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def run(t):
+        try:
+            s = torch.cuda.Stream()
+            outs = []
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    o = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+                    df11.decode_batch(plan, dcs, o, stream=s)
+                    outs.append(o)
+            s.synchronize()
+            results[t] = outs
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    th = [threading.Thread(target=run, args=(t,)) for t in range(4)]
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    assert not errors, errors
+    df11.check(plan)
+    for outs in results:
+        for o in outs:
+            for w, oo in zip(ws, o):
+                assert (oo.cpu().numpy().view(np.uint16) == w).all()
+
+
 def test_ticket_counters_across_many_launches_and_streams():
     """Every launch takes its chunks from one of the plan's ticket counters,
     which its last workgroup clears.  160 launches (single and batched, on
