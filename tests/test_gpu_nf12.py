@@ -10,7 +10,7 @@ from oracle import nf12 as nf12_oracle
 import lossless_bf16_weight_amd as df11
 from lossless_bf16_weight_amd import workloads as W
 
-from exponent_mixes import ENTROPY_MIXES, entropy_mix_words
+from exponent_mixes import ENTROPY_MIXES, entropy_mix_words, random_exponent_case
 from gpu_util import empty_words, log, to_device_u8
 
 pytestmark = pytest.mark.gpu
@@ -159,3 +159,21 @@ def test_batch_of_mixed_sizes_split_over_launches():
         host = buf.cpu().numpy().view(np.uint16)
         assert (host[32:32 + n] == w).all()
         assert (host[:32] == 0x5A5A).all() and (host[32 + max(n, 1):] == 0x5A5A).all()
+
+
+def test_random_distributions_batched():
+    """60 seeded random exponent distributions (random sizes, from no
+    escaped group to all of them) in the NF12 oracle's containers, decoded
+    in one batched call with guard words around every output."""
+    import torch
+    log("nf12 random distributions")
+    ws = [random_exponent_case(seed, 120_000) for seed in range(60)]
+    cs = [nf12_oracle.encode(w) for w in ws]
+    bufs = [empty_words(max(w.size, 1), guard=32) for w in ws]
+    dcs = [to_device_u8(np.pad(c, (0, 16))) for c in cs]
+    df11.nf12_decode_batch([c[:256] for c in cs], dcs, [o for _, o in bufs])
+    torch.cuda.synchronize()
+    for seed, (w, (buf, _)) in enumerate(zip(ws, bufs)):
+        host = buf.cpu().numpy().view(np.uint16)
+        assert (host[32:32 + w.size] == w).all(), seed
+        assert (host[:32] == 0x5A5A).all() and (host[32 + max(w.size, 1):] == 0x5A5A).all(), seed

@@ -64,3 +64,16 @@ def test_validate_rejects_broken_containers():
     assert status(lambda x: x.__setitem__(h["off_prefix"] + 4, x[h["off_prefix"] + 4] ^ 1), cut=256) == 0
     assert status(lambda x: x.__setitem__(24, x[24] ^ 1), cut=256) == E_FORMAT
     assert status(lambda x: None, cut=255) == E_FORMAT
+
+
+def test_encoder_matches_oracle_on_random_distributions():
+    """60 seeded random exponent distributions (random sizes, random
+    exponent sets, so that anything from no group to every group escapes):
+    the product encoder's bytes equal the NF12 oracle's."""
+    from exponent_mixes import random_exponent_case
+    for seed in range(60):
+        w = random_exponent_case(seed, 120_000)
+        a = df11.nf12_encode(w, threads=4)
+        b = nf12_oracle.encode(w)
+        assert a.size == b.size and (a == b).all(), seed
+        assert df11.nf12_validate(a) == w.size
