@@ -454,6 +454,66 @@ def workload_table(rounds: int = 3, names=None):
         sys.exit(1)
 
 
+def control_by_size(reps: int = 300):
+    """The decode against the bandwidth control with the same read and write
+    byte counts, warm (reps launches after as many warm-up launches), for
+    batches of growing size: the Llama-8B block, three of them in one batch,
+    the DiT block, and the DiT block without its 16 vectors."""
+    import numpy as np
+    import torch
+    import lossless_bf16_weight_amd as df11
+    from lossless_bf16_weight_amd import workloads as W
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(reps):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def n_of(s):
+        n = 1
+        for d in s.shape:
+            n *= d
+        return n
+
+    cases = [("llama8b_block", W.llama8b_block()),
+             ("llama8b_block_x3", W.llama8b_block(0) + W.llama8b_block(1) + W.llama8b_block(2)),
+             ("flux_dit_block", W.flux_dit_block()),
+             ("flux_dit_block_without_vectors", [s for s in W.flux_dit_block() if n_of(s) > 100000])]
+    rows = []
+    for name, specs in cases:
+        words = [s.make(threads=16).reshape(-1) for s in specs]
+        conts = [df11.encode(w, shape=s.shape, threads=16) for w, s in zip(words, specs)]
+        plan = df11.Plan(conts, device=0)
+        rd = sum(i["bytes_read_per_decode"] for i in plan.infos)
+        wr = 2 * sum(i["n_elems"] for i in plan.infos)
+        d = [torch.from_numpy(c).to(dev) for c in conts]
+        outs = [torch.empty(i["n_elems"], dtype=torch.int16, device=dev) for i in plan.infos]
+        ms = timed(lambda: df11.decode_batch(plan, d, outs, stream=stream))
+        df11.check(plan, stream=stream)
+        exact = all(torch.equal(torch.from_numpy(w.view(np.int16)).to(dev), o) for w, o in zip(words, outs))
+        src = torch.empty((rd + 15) // 16 * 16, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        dst = torch.empty(wr, dtype=torch.uint8, device=dev)
+        cms = timed(lambda: df11.bw_control(src, dst, stream=stream))
+        rows.append({"batch": name, "tensors": len(specs), "bytes_per_launch": rd + wr,
+                     "decode_ms": round(ms, 4), "control_ms": round(cms, 4),
+                     "decode_TBs": round((rd + wr) / ms / 1e9, 3), "control_TBs": round((rd + wr) / cms / 1e9, 3),
+                     "decode_over_control": round(cms / ms, 3), "bit_exact": bool(exact)})
+        del d, outs, src, dst
+        plan.close()
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "decode against the bandwidth control by batch size", "reps": reps, "results": rows}),
+          flush=True)
+
+
 def nf12_compare(reps: int = 100, warmup: int = 200, names=None):
     """NF12 (fixed-rate 12-bit groups with an escape buffer) next to DF11 on
     the workloads that fit one decode: container size relative to BF16 and
@@ -536,6 +596,8 @@ def main():
                          "ones named), warm and flushed")
     ap.add_argument("--stack", action="store_true",
                     help="only measure the layer loop over the resident 32-layer stack")
+    ap.add_argument("--control-by-size", action="store_true",
+                    help="only time the decode against the bandwidth control for batches of growing size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; this decoder runs on one GPU "
@@ -555,6 +617,10 @@ def main():
 
     if args.stack:
         stack_loop(passes=20, warmup=10)
+        return
+
+    if args.control_by_size:
+        control_by_size()
         return
 
     if args.workloads is not None:
