@@ -38,6 +38,23 @@ def _compile(item):
     return obj
 
 
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "decode_from_c.c")
+
+
+def build_c_example() -> str:
+    """The C program that drives the library through include/df11.h alone
+    (tests/c_abi), built with gcc as C99 against the in-tree libdf11.so."""
+    out = C_EXAMPLE[:-2]
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"), C_EXAMPLE, "-L" + PKG, "-ldf11",
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../lossless_bf16_weight_amd",
+           "-Wl,-rpath,/opt/rocm/lib", "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C example build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(len(SOURCES)) as ex:
@@ -48,8 +65,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    example = build_c_example()
     if verbose:
         print("built", LIB)
+        print("built", example)
     return LIB
 
 

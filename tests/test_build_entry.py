@@ -1,6 +1,7 @@
 """The documented build entry point, run end to end on the CPU: it compiles
-libdf11.so for gfx950 and the oracles with gcc, loads the library and checks
-that its ABI version is the one the Python binding marshals for."""
+libdf11.so for gfx950, the C program over the C ABI and the oracles with
+gcc, loads the library and checks that its ABI version is the one the
+Python binding marshals for."""
 import os
 import shutil
 import subprocess
@@ -19,6 +20,9 @@ def test_graft_entry_build_runs_end_to_end():
     assert r.returncode == 0, (r.stdout[-2000:], r.stderr[-4000:])
     import lossless_bf16_weight_amd as df11
     assert df11.lib().df11_abi_version() == df11.ABI_VERSION
+    # and the C program over the C ABI (run by the GPU tests)
+    example = os.path.join(ROOT, "tests", "c_abi", "decode_from_c")
+    assert os.path.exists(example) and os.access(example, os.X_OK)
 
 
 def test_binding_abi_version_matches_header():
