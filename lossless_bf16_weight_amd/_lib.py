@@ -317,9 +317,34 @@ class Plan:
             pass
 
 
+def _check_device_tensor(x, what: str, min_bytes: int, device: int, words16: bool = False):
+    """What the C ABI cannot check for a device pointer: a contiguous CUDA
+    tensor on the plan's device, at least min_bytes long (and of a 16-bit
+    dtype for decoded words).  Alignment is checked by the library."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{what}: a CUDA tensor is needed")
+    if (x.device.index or 0) != device:
+        raise ValueError(f"{what}: on cuda:{x.device.index}, the decode runs on cuda:{device}")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    if words16 and x.element_size() != 2:
+        raise ValueError(f"{what}: a 16-bit dtype is needed, not {x.dtype}")
+    if x.numel() * x.element_size() < min_bytes:
+        raise ValueError(f"{what}: {x.numel() * x.element_size()} bytes, at least {min_bytes} needed")
+
+
+def _check_decode_args(plan: "Plan", t: int, container, out):
+    if 0 <= t < plan.n_tensors:   # (another tensor number: the library reports it)
+        info = plan.infos[t]
+        _check_device_tensor(container, f"tensor {t}'s container", info["container_bytes"], plan.device)
+        _check_device_tensor(out, f"tensor {t}'s output", 2 * info["n_elems"], plan.device, words16=True)
+
+
 def decode(plan: Plan, t: int, container, out, stream=None):
     """Enqueue the decode of tensor t: container (uint8, device) -> out
     (16-bit dtype, device, n_elems)."""
+    _check_decode_args(plan, t, container, out)
     _raise(lib().df11_decode(plan.handle, t, container.data_ptr(), out.data_ptr(),
                              _stream_handle(stream)))
 
@@ -328,6 +353,8 @@ def decode_batch(plan: Plan, containers: List, outs: List, stream=None):
     n = plan.n_tensors
     if len(containers) != n or len(outs) != n:
         raise ValueError("one container and one output per planned tensor")
+    for t in range(n):
+        _check_decode_args(plan, t, containers[t], outs[t])
     cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in containers])
     op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])
     _raise(lib().df11_decode_batch(plan.handle, cp, op, _stream_handle(stream)))
@@ -369,6 +396,16 @@ def nf12_validate(container) -> int:
     return int(n.value)
 
 
+def _check_nf12_args(h: np.ndarray, container, out, device: int):
+    """The header validated (the library's error for a bad one), then the
+    device tensors against its element count and total size."""
+    _raise(lib().df11_nf12_validate(h.ctypes.data, NF12_HEADER, None))
+    n = int(h[16:24].view(np.uint64)[0])
+    total = int(h[72:80].view(np.uint64)[0])
+    _check_device_tensor(container, "NF12 container", total, device)
+    _check_device_tensor(out, "NF12 output", 2 * n, device, words16=True)
+
+
 def nf12_decode(host_header, container, out, device: int = 0, stream=None):
     """Enqueue the decode of an NF12 container: host_header = host copy of
     (at least) its first 256 bytes, container = the device copy (uint8),
@@ -376,6 +413,7 @@ def nf12_decode(host_header, container, out, device: int = 0, stream=None):
     h = _host_u8(host_header)
     if h.size < NF12_HEADER:
         raise ValueError("the NF12 header is 256 bytes")
+    _check_nf12_args(h, container, out, device)
     _raise(lib().df11_nf12_decode(h.ctypes.data, container.data_ptr(), out.data_ptr(), device,
                                   _stream_handle(stream)))
 
@@ -389,6 +427,8 @@ def nf12_decode_batch(host_headers: List, containers: List, outs: List, device: 
     hs = [_host_u8(h) for h in host_headers]
     if any(h.size < NF12_HEADER for h in hs):
         raise ValueError("the NF12 header is 256 bytes")
+    for h, c, o in zip(hs, containers, outs):
+        _check_nf12_args(h, c, o, device)
     hp = (ctypes.c_void_p * n)(*[h.ctypes.data for h in hs])
     cp = (ctypes.c_void_p * n)(*[c.data_ptr() for c in containers])
     op = (ctypes.c_void_p * n)(*[o.data_ptr() for o in outs])

@@ -477,6 +477,21 @@ def test_bad_arguments_are_rejected():
         df11.decode(plan, 1, dc, o)          # no tensor 1
     with pytest.raises(df11.DF11Error):
         df11.Plan([c[:100]])                 # truncated metadata
+    # what the binding checks before the call (the library cannot see the
+    # size of a device buffer): nothing is enqueued for these
+    with pytest.raises(ValueError):
+        df11.decode(plan, 0, dc, o[:w.size - 8])                 # output too small
+    with pytest.raises(ValueError):
+        df11.decode(plan, 0, dc[:-16], o)                        # container too short
+    with pytest.raises(ValueError):
+        df11.decode(plan, 0, dc, o.view(torch.int32))            # not 16-bit words
+    with pytest.raises(ValueError):
+        df11.decode(plan, 0, dc, o.cpu())                        # not on the GPU
+    with pytest.raises(ValueError):
+        df11.decode_batch(plan, [dc], [o.reshape(-1, 8)[:, :4]])  # not contiguous
+    df11.decode(plan, 0, dc, o[:w.size])
+    df11.check(plan)
+    assert (o[:w.size].cpu().numpy().view(np.uint16) == w).all()
 
 
 def _sampled_oracle_chunks(c, words, n_samples=3):

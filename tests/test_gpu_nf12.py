@@ -127,7 +127,7 @@ def test_bad_arguments_are_rejected():
     w = W.normal_bf16((4096,), seed=1)
     c = df11.nf12_encode(w)
     dc = to_device_u8(c)
-    out = torch.empty(w.size, dtype=torch.int16, device="cuda")
+    out = torch.empty(w.size + 8, dtype=torch.int16, device="cuda")
     with pytest.raises(df11.DF11Error):
         hdr = c[:256].copy()
         hdr[0] = ord("X")
@@ -136,6 +136,14 @@ def test_bad_arguments_are_rejected():
         df11.nf12_decode(c[:256], dc, out[1:])          # misaligned output
     with pytest.raises(ValueError):
         df11.nf12_decode(c[:100], dc, out)
+    # what the binding checks before the call (the library cannot see the
+    # size of a device buffer)
+    with pytest.raises(ValueError):
+        df11.nf12_decode(c[:256], dc, out[:w.size - 8])  # output too small
+    with pytest.raises(ValueError):
+        df11.nf12_decode(c[:256], dc[:-16], out)        # container too short
+    with pytest.raises(ValueError):
+        df11.nf12_decode_batch([c[:256]], [dc], [out.view(torch.int32)])   # not 16-bit words
 
 
 def test_batch_of_mixed_sizes_split_over_launches():
