@@ -173,12 +173,23 @@ def encode(words, shape=None, threads: int = 0, sha256: bool = False) -> np.ndar
     return out[: nbytes.value]
 
 
+def _cuda_words(x, what: str):
+    """A device tensor of 16-bit words (the library reads it on the GPU: a
+    host tensor's pointer must never reach it)."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{what}: a CUDA tensor is needed")
+    if x.element_size() != 2:
+        raise ValueError(f"{what}: a 16-bit dtype is needed, not {x.dtype}")
+    return x.contiguous().view(torch.int16)
+
+
 def encode_device(words, shape=None, stream=None):
     """Encode a 16-bit device tensor (BF16 bit patterns, on a GPU) into a
     version-4 container on the same device (uint8 tensor): the bytes
     encode() writes for the same words, computed by the GPU kernels."""
     import torch
-    w = words.contiguous().view(torch.int16).reshape(-1)
+    w = _cuda_words(words, "words").reshape(-1)
     shape = tuple(words.shape) if shape is None else tuple(shape)
     dims = (ctypes.c_uint64 * max(1, len(shape)))(*shape)
     out = torch.empty(container_bound(w.numel()), dtype=torch.uint8, device=w.device)
@@ -197,13 +208,23 @@ def encode_device_batch(tensors, stream=None, outs=None, noalloc=False):
     df11_encode_device_batch_noalloc (at most 64 tensors), which allocates
     nothing for its histograms."""
     import torch
-    ws = [t.contiguous().view(torch.int16) for t in tensors]
+    ws = [_cuda_words(t, f"tensor {i}") for i, t in enumerate(tensors)]
     k = len(ws)
     if k == 0:
         return []
     dev = ws[0].device
+    for i, w in enumerate(ws):
+        if w.device != dev:
+            raise ValueError(f"tensor {i}: on {w.device}, tensor 0 on {dev}")
+        if w.dim() > 8:
+            raise ValueError(f"tensor {i}: {w.dim()} dimensions, at most 8")
     if outs is None:
         outs = [torch.empty(container_bound(w.numel()), dtype=torch.uint8, device=dev) for w in ws]
+    elif len(outs) != k:
+        raise ValueError("one output buffer per tensor")
+    else:
+        for i, o in enumerate(outs):
+            _check_device_tensor(o, f"output {i}", 0, dev.index or 0)
     dims = (ctypes.c_uint64 * (8 * k))()
     for t, w in enumerate(ws):
         for i, d in enumerate(w.shape):
@@ -213,9 +234,10 @@ def encode_device_batch(tensors, stream=None, outs=None, noalloc=False):
     _raise(fn(
         k, (ctypes.c_void_p * k)(*[w.data_ptr() if w.numel() else None for w in ws]),
         (ctypes.c_uint64 * k)(*[w.numel() for w in ws]), (ctypes.c_int * k)(*[w.dim() for w in ws]), dims,
-        (ctypes.c_void_p * k)(*[o.data_ptr() for o in outs]), (ctypes.c_uint64 * k)(*[o.numel() for o in outs]),
+        (ctypes.c_void_p * k)(*[o.data_ptr() for o in outs]),
+        (ctypes.c_uint64 * k)(*[o.numel() * o.element_size() for o in outs]),
         nbytes, dev.index or 0, _stream_handle(stream)))
-    return [o[: nbytes[t]] for t, o in enumerate(outs)]
+    return [o.view(torch.uint8)[: nbytes[t]] for t, o in enumerate(outs)]
 
 
 def sha256(data) -> bytes:
@@ -363,6 +385,8 @@ def decode_batch(plan: Plan, containers: List, outs: List, stream=None):
 def bw_control(src, dst, device: int = 0, stream=None):
     """Enqueue the bandwidth-control kernel: read all of `src`, write all of
     `dst` (device tensors, sizes multiples of 16 bytes), no decoding."""
+    _check_device_tensor(src, "src", 0, device)
+    _check_device_tensor(dst, "dst", 0, device)
     _raise(lib().df11_bw_control(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),
                                  dst.numel() * dst.element_size(), device, _stream_handle(stream)))
 

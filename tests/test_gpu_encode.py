@@ -154,3 +154,27 @@ def test_containers_into_dirty_buffers_match_oracle_bytes(fill):
         want = oracle.encode(w)
         got = c.cpu().numpy()
         assert got.size == want.size and (got == want).all(), w.size
+
+
+def test_binding_rejects_host_and_mistyped_tensors():
+    """The GPU encoder reads its words on the GPU: the binding refuses host
+    tensors, tensors that are not 16-bit, more than 8 dimensions and a
+    wrong number of output buffers before anything reaches the library."""
+    import torch
+    w = torch.zeros(1000, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        df11.encode_device(w)                                    # a host tensor
+    with pytest.raises(ValueError):
+        df11.encode_device(w.to(torch.int32).cuda())             # not 16-bit
+    with pytest.raises(ValueError):
+        df11.encode_device_batch([w.cuda(), w])                  # one on the host
+    with pytest.raises(ValueError):
+        df11.encode_device_batch([torch.zeros((1,) * 9, dtype=torch.int16, device="cuda")])
+    with pytest.raises(ValueError):
+        df11.encode_device_batch([w.cuda()], outs=[])
+    with pytest.raises(ValueError):
+        df11.bw_control(torch.zeros(64, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8, device="cuda"))
+    # outputs of another dtype are taken as bytes
+    outs = [torch.zeros((df11.container_bound(1000) + 1) // 2, dtype=torch.int16, device="cuda")]
+    got = df11.encode_device_batch([w.cuda()], outs=outs)[0]
+    assert (got.cpu().numpy() == oracle.encode(w.numpy().view(np.uint16))).all()
