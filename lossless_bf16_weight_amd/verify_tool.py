@@ -115,50 +115,52 @@ def verify_containers(containers: Sequence[np.ndarray], sources: Optional[Sequen
         return CANNOT, msgs + [f"{level} level: torch is not available"]
     dev = torch.device("cuda", device)
     plan = L.Plan(list(containers), device=device)
-    d_conts = [torch.from_numpy(np.ascontiguousarray(c)).to(dev) for c in containers]
-    outs = [torch.empty(i["n_elems"], dtype=torch.int16, device=dev) for i in infos]
-    stream = torch.cuda.current_stream(dev)
-    L.decode_batch(plan, d_conts, outs, stream=stream)
     try:
-        L.check(plan, stream=stream)
-    except L.DF11Error as e:
-        msgs.append(f"decode: {e}")
-        worst = FAIL
-
-    if level == "sampled":
-        chunks = [(t, c) for t, i in enumerate(infos) for c in range(i["n_chunks"])]
-        rng = np.random.default_rng(seed)
-        pick = chunks if samples >= len(chunks) else [chunks[k] for k in
-                                                      sorted(rng.choice(len(chunks), samples, replace=False))]
-        bad = 0
-        for t, c in pick:
-            lo, hi = c * 32768, min((c + 1) * 32768, infos[t]["n_elems"])
-            want = torch.from_numpy(np.array(sources[t][lo:hi], dtype=np.uint16).view(np.int16)).to(dev)
-            if not torch.equal(outs[t][lo:hi], want):
-                bad += 1
-                if bad <= 5:
-                    msgs.append(f"{names[t]}: chunk {c} decodes to words that differ from the source")
-        msgs.append(f"sampled: {len(pick)} chunk(s) compared, {bad} differ")
-        if bad:
+        d_conts = [torch.from_numpy(np.ascontiguousarray(c)).to(dev) for c in containers]
+        outs = [torch.empty(i["n_elems"], dtype=torch.int16, device=dev) for i in infos]
+        stream = torch.cuda.current_stream(dev)
+        L.decode_batch(plan, d_conts, outs, stream=stream)
+        try:
+            L.check(plan, stream=stream)
+        except L.DF11Error as e:
+            msgs.append(f"decode: {e}")
             worst = FAIL
-    else:
-        for t, info in enumerate(infos):
-            got = outs[t].cpu().numpy().view(np.uint16)
-            if sources is not None:
-                diff = int(np.count_nonzero(got != np.asarray(sources[t])))
-                if diff:
-                    msgs.append(f"{names[t]}: {diff} decoded word(s) differ from the source")
-                    worst = FAIL
-            if _has_hash(info):
-                st = L.verify_status(containers[t], got)
-                if st == L.E_CORRUPT:
-                    msgs.append(f"{names[t]}: the decoded words' SHA-256 differs from the header's")
-                    worst = FAIL
-                elif st != L.OK:
-                    msgs.append(f"{names[t]}: could not check the hash ({L.lib().df11_status_str(st).decode()})")
-                    worst = max(worst, CANNOT)
-        msgs.append(f"full: {len(infos)} tensor(s) decoded and compared")
-    plan.close()
+
+        if level == "sampled":
+            chunks = [(t, c) for t, i in enumerate(infos) for c in range(i["n_chunks"])]
+            rng = np.random.default_rng(seed)
+            pick = chunks if samples >= len(chunks) else [chunks[k] for k in
+                                                          sorted(rng.choice(len(chunks), samples, replace=False))]
+            bad = 0
+            for t, c in pick:
+                lo, hi = c * 32768, min((c + 1) * 32768, infos[t]["n_elems"])
+                want = torch.from_numpy(np.array(sources[t][lo:hi], dtype=np.uint16).view(np.int16)).to(dev)
+                if not torch.equal(outs[t][lo:hi], want):
+                    bad += 1
+                    if bad <= 5:
+                        msgs.append(f"{names[t]}: chunk {c} decodes to words that differ from the source")
+            msgs.append(f"sampled: {len(pick)} chunk(s) compared, {bad} differ")
+            if bad:
+                worst = FAIL
+        else:
+            for t, info in enumerate(infos):
+                got = outs[t].cpu().numpy().view(np.uint16)
+                if sources is not None:
+                    diff = int(np.count_nonzero(got != np.asarray(sources[t])))
+                    if diff:
+                        msgs.append(f"{names[t]}: {diff} decoded word(s) differ from the source")
+                        worst = FAIL
+                if _has_hash(info):
+                    st = L.verify_status(containers[t], got)
+                    if st == L.E_CORRUPT:
+                        msgs.append(f"{names[t]}: the decoded words' SHA-256 differs from the header's")
+                        worst = FAIL
+                    elif st != L.OK:
+                        msgs.append(f"{names[t]}: could not check the hash ({L.lib().df11_status_str(st).decode()})")
+                        worst = max(worst, CANNOT)
+            msgs.append(f"full: {len(infos)} tensor(s) decoded and compared")
+    finally:
+        plan.close()
     return worst, msgs
 
 
