@@ -370,7 +370,7 @@ def workload_table(rounds: int = 3, names=None):
     two events, per round (after 400 warm-up reps, as the part runs slower
     for its first few hundred back-to-back launches); "flushed": each rep
     alone between its own events, after a pass that reads 1 GiB of other
-    data (the bandwidth control with a 16-byte output), so that the
+    data (a sum over it into one 64-bit word), so that the
     containers come from HBM and the last-level cache holds only clean
     lines; "write_flushed": the same after 1 GiB of writes instead, whose
     dirty lines the decode's own traffic then writes back.  Medians over
@@ -385,7 +385,8 @@ def workload_table(rounds: int = 3, names=None):
     stream = torch.cuda.current_stream()
     flush = torch.empty(1 << 29, dtype=torch.int16, device=dev)
     flush.fill_(1)
-    sink = torch.empty(16, dtype=torch.uint8, device=dev)
+    # (a sum over the 1 GiB buffer reads all of it and writes 8 bytes)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
     threads = max(1, min(16, os.cpu_count() or 1))
     rows = []
     for name in names or ("single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"):
@@ -415,7 +416,7 @@ def workload_table(rounds: int = 3, names=None):
             warm.append(a.elapsed_time(b) / reps)
         cold, wcold = [], []
         for _ in range(5 * rounds):
-            df11.bw_control(flush, sink, stream=stream)
+            torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
             a.record(stream)
             run()
             b.record(stream)

@@ -297,8 +297,10 @@ df11_status df11_check(df11_plan_t plan, hipStream_t stream);
  * sizes, its rate is the HBM ceiling for that decode -- the analogue of the
  * control condition in the mlx-dfloat project page's overhead benchmark (the
  * same path without the decoding).  Sizes: multiples of 16, at least 16,
- * below 2^40 bytes; pointers 16-byte aligned, regions not overlapping.  The
- * output bytes are unspecified.  Never allocates or synchronizes.
+ * below 2^40 bytes, src_bytes <= dst_bytes (as in every decode: 2 bytes
+ * written per element, fewer read; output unit i reads source unit
+ * floor(i * src_bytes / dst_bytes)); pointers 16-byte aligned, regions not
+ * overlapping.  The output bytes are unspecified.  Never allocates or synchronizes.
  * Returns DF11_OK, DF11_E_ARG or DF11_E_HIP. */
 df11_status df11_bw_control(const void *d_src, uint64_t src_bytes, void *d_dst, uint64_t dst_bytes,
                             int hip_device, hipStream_t stream);

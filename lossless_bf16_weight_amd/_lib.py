@@ -384,7 +384,8 @@ def decode_batch(plan: Plan, containers: List, outs: List, stream=None):
 
 def bw_control(src, dst, device: int = 0, stream=None):
     """Enqueue the bandwidth-control kernel: read all of `src`, write all of
-    `dst` (device tensors, sizes multiples of 16 bytes), no decoding."""
+    `dst` (device tensors, sizes multiples of 16 bytes, `src` no larger than
+    `dst`), no decoding."""
     _check_device_tensor(src, "src", 0, device)
     _check_device_tensor(dst, "dst", 0, device)
     _raise(lib().df11_bw_control(src.data_ptr(), src.numel() * src.element_size(), dst.data_ptr(),

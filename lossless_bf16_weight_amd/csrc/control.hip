@@ -15,8 +15,9 @@ namespace df11 {
 typedef uint32_t c32x4 __attribute__((ext_vector_type(4)));
 
 // Output unit i (16 bytes) is source unit floor(i * ratio) xor-ed with i:
-// every source unit is read (consecutive outputs share or advance their
-// source unit), every output unit is written once.  Workgroups sweep the
+// with ratio <= 1 (the host refuses a source larger than the output) every
+// source unit is read, consecutive outputs sharing or advancing their source
+// unit, and every output unit is written once.  Workgroups sweep the
 // output in interleaved 32 KiB tiles (8 units per lane in flight), the order
 // that measured fastest for this mix of reads and writes.
 constexpr int kUnroll = 8;

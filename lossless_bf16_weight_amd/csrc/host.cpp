@@ -635,6 +635,10 @@ extern "C" df11_status df11_bw_control(const void *d_src, uint64_t src_bytes, vo
         return fail(DF11_E_ARG, "sizes must be positive multiples of 16");
     if (src_bytes >= (uint64_t(1) << 40) || dst_bytes >= (uint64_t(1) << 40))
         return fail(DF11_E_ARG, "sizes must be below 2^40 bytes");
+    // (output unit i reads source unit floor(i * src / dst): with a smaller
+    // output most of the source would go unread)
+    if (src_bytes > dst_bytes)
+        return fail(DF11_E_ARG, "src_bytes above dst_bytes: a decode writes more than it reads");
     const uintptr_t s0 = (uintptr_t)d_src, d0 = (uintptr_t)d_dst;
     if (s0 < d0 + dst_bytes && d0 < s0 + src_bytes) return fail(DF11_E_ARG, "regions overlap");
     DeviceGuard guard(hip_device);

@@ -559,6 +559,8 @@ def test_bw_control_moves_every_byte():
         df11.bw_control(src[:15], dst)                # size not a multiple of 16
     with pytest.raises(df11.DF11Error):
         df11.bw_control(src, src)                     # overlapping regions
+    with pytest.raises(df11.DF11Error):
+        df11.bw_control(dst, src)                     # source above the output: not all of it would be read
 
 
 def test_decode_batch_replays_from_a_hip_graph():
