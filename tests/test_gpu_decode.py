@@ -166,7 +166,7 @@ def test_more_tensors_than_one_launch():
     cs = oracle_encode_many(ws)
     plan = df11.Plan(cs)
     dcs = [to_device_u8(c) for c in cs]
-    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in ws]
+    outs = [torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda") for w in ws]
     df11.decode_batch(plan, dcs, outs)
     df11.check(plan)
     for w, o in zip(ws, outs):
@@ -184,7 +184,7 @@ def test_non_default_stream_and_repeats():
     outs = []
     with torch.cuda.stream(s):
         for _ in range(3):
-            o = torch.empty(w.size, dtype=torch.int16, device="cuda")
+            o = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
             df11.decode(plan, 0, dc, o, stream=s)
             outs.append(o)
     df11.check(plan, stream=s)
@@ -214,7 +214,7 @@ def test_one_plan_from_four_host_threads():
             outs = []
             with torch.cuda.stream(s):
                 for _ in range(20):
-                    o = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+                    o = [torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda") for n in sizes]
                     df11.decode_batch(plan, dcs, o, stream=s)
                     outs.append(o)
             s.synchronize()
@@ -249,8 +249,10 @@ def test_ticket_counters_across_many_launches_and_streams():
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     outs = []
     for r in range(40):
-        o = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
-        ob = [torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes]
+        o = [torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda") for n in sizes]
+        ob = [torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda") for n in sizes]
+        s1.wait_stream(torch.cuda.current_stream())   # (the fills come first)
+        s2.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s1):
             df11.decode(plan, 0, dcs[0], o[0], stream=s1)
             df11.decode(plan, 2, dcs[2], o[2], stream=s1)
@@ -284,7 +286,7 @@ def test_more_queued_launches_than_ticket_counters():
     held, s1, s2, cp = (torch.cuda.Stream() for _ in range(4))
     big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     big2 = torch.empty_like(big)
-    outs = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(3)]
+    outs = [torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda") for _ in range(3)]
     torch.cuda.synchronize()
     with torch.cuda.stream(cp):
         for _ in range(6):
@@ -317,7 +319,7 @@ def test_corrupted_stream_sets_the_flag():
     bad = c.copy()
     bad[h["off_stream"] + 4000] ^= 0x40
     dc = to_device_u8(bad)
-    o = torch.empty(w.size, dtype=torch.int16, device="cuda")
+    o = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
     df11.decode(plan, 0, dc, o)
     try:
         df11.check(plan)
@@ -450,7 +452,7 @@ def test_source_hash_verifies_decoded_output():
     ws = [W.normal_bf16((65536 + 77,), seed=21), W.heavy_tail_bf16((40000,), seed=22)]
     cs = [oracle.encode(w, sha256=True) for w in ws]
     plan = df11.Plan(cs)
-    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in ws]
+    outs = [torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda") for w in ws]
     df11.decode_batch(plan, [to_device_u8(c) for c in cs], outs)
     df11.check(plan)
     for w, c, o in zip(ws, cs, outs):
@@ -469,7 +471,7 @@ def test_bad_arguments_are_rejected():
     c = oracle.encode(w)
     plan = df11.Plan([c])
     dc = to_device_u8(c)
-    o = torch.empty(w.size + 8, dtype=torch.int16, device="cuda")
+    o = torch.full((w.size + 8,), 0x5A5A, dtype=torch.int16, device="cuda")
     with pytest.raises(df11.DF11Error) as e:
         df11.decode(plan, 0, dc, o[1:])      # misaligned output
     assert e.value.status == 1
@@ -510,7 +512,7 @@ def _full_workload(specs):
     plan = df11.Plan(cs)
     dcs = [to_device_u8(c) for c in cs]
     srcs = [to_device_words(w) for w in ws]
-    outs = [torch.empty(w.size, dtype=torch.int16, device="cuda") for w in ws]
+    outs = [torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda") for w in ws]
     df11.decode_batch(plan, dcs, outs)
     df11.check(plan)
     torch.cuda.synchronize()
@@ -575,8 +577,9 @@ def test_decode_batch_replays_from_a_hip_graph():
     cs = oracle_encode_many(ws)
     plan = df11.Plan(cs)
     dcs = [to_device_u8(c) for c in cs]
-    outs = [[torch.empty(n, dtype=torch.int16, device="cuda") for n in sizes] for _ in range(3)]
+    outs = [[torch.full((n,), 0x5A5A, dtype=torch.int16, device="cuda") for n in sizes] for _ in range(3)]
     s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())               # (the fills come first)
     with torch.cuda.stream(s):
         df11.decode_batch(plan, dcs, outs[0], stream=s)      # warm-up outside the capture
     torch.cuda.synchronize()

@@ -82,7 +82,7 @@ def test_workloads_match_host_encoder_and_round_trip(name):
         got = c.cpu().numpy()
         assert got.size == want.size and (got == want).all(), s.name
         plan = df11.Plan([got])
-        out = torch.empty(w.size, dtype=torch.int16, device="cuda")
+        out = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
         df11.decode(plan, 0, c, out)
         df11.check(plan)
         assert torch.equal(out, t.reshape(-1)), s.name

@@ -62,9 +62,10 @@ def test_every_word_and_all_outliers():
 def test_empty_tensor_enqueues_nothing():
     import torch
     c = df11.nf12_encode(np.zeros(0, np.uint16))
-    out = torch.empty(8, dtype=torch.int16, device="cuda")
+    out = torch.full((8,), 0x5A5A, dtype=torch.int16, device="cuda")
     df11.nf12_decode(c[:256], to_device_u8(np.pad(c, (0, 16))), out)
     torch.cuda.synchronize()
+    assert (out.cpu().numpy().view(np.uint16) == 0x5A5A).all()
 
 
 @pytest.mark.parametrize("name", ["single_2048", "llama8b_block", "heavy_tail_8192", "flux_dit_block"])
@@ -74,7 +75,7 @@ def test_workloads_bit_exact(name):
     for s in W.WORKLOADS[name]():
         w = s.make().reshape(-1)
         c = df11.nf12_encode(w, threads=16)
-        out = torch.empty(w.size, dtype=torch.int16, device="cuda")
+        out = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
         df11.nf12_decode(c[:256], to_device_u8(c), out)
         torch.cuda.synchronize()
         got = out.cpu().numpy().view(np.uint16)
@@ -95,7 +96,7 @@ def test_llama8b_stack_sample_bit_exact():
         for s in g:
             w = s.make().reshape(-1)
             c = df11.nf12_encode(w, threads=16)
-            out = torch.empty(w.size, dtype=torch.int16, device="cuda")
+            out = torch.full((w.size,), 0x5A5A, dtype=torch.int16, device="cuda")
             df11.nf12_decode(c[:256], to_device_u8(c), out)
             torch.cuda.synchronize()
             assert (out.cpu().numpy().view(np.uint16) == w).all(), s.name
@@ -127,7 +128,7 @@ def test_bad_arguments_are_rejected():
     w = W.normal_bf16((4096,), seed=1)
     c = df11.nf12_encode(w)
     dc = to_device_u8(c)
-    out = torch.empty(w.size + 8, dtype=torch.int16, device="cuda")
+    out = torch.full((w.size + 8,), 0x5A5A, dtype=torch.int16, device="cuda")
     with pytest.raises(df11.DF11Error):
         hdr = c[:256].copy()
         hdr[0] = ord("X")

@@ -76,7 +76,7 @@ def test_llama8b_stack_jit_layer_loop():
     assert n_total == 32 * 218103808 + 128256 * 4096
 
     # ---- one reused output buffer, large enough for the largest group
-    buf = torch.empty(max(sum(c) for c in counts), dtype=torch.int16, device="cuda")
+    buf = torch.full((max(sum(c) for c in counts),), 0x5A5A, dtype=torch.int16, device="cuda")
 
     def views(ci):
         out, off = [], 0
